@@ -1,0 +1,142 @@
+"""ctypes loader for the fp64 CPU oracle (oracle.c).
+
+Test infrastructure only: the tests, the smoke check and the CPU baseline leg
+of the benchmark use it.  The product path (barnes_hut_tree_amd) never
+imports it.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force=False):
+    """Compile oracle.c with gcc (-O2, OpenMP, no fast-math) into liboracle.so."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+           "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        L.orc_build.restype = P
+        L.orc_build.argtypes = [P, i64, ctypes.c_int, ctypes.c_int]
+        L.orc_free.argtypes = [P]
+        L.orc_bbox.argtypes = [P, P, P, P]
+        L.orc_keys.argtypes = [P, P]
+        L.orc_perm.argtypes = [P, P]
+        L.orc_ncells.restype = i64
+        L.orc_ncells.argtypes = [P]
+        L.orc_cells.argtypes = [P] + [P] * 8
+        L.orc_bh.argtypes = [P, P, P, i64, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                             ctypes.c_int, P, P, P]
+        L.orc_direct.argtypes = [P, i64, P, P, i64, ctypes.c_double, ctypes.c_double, P]
+        L.orc_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _f4(pos_mass):
+    a = np.ascontiguousarray(pos_mass, dtype=np.float32)
+    if a.ndim != 2 or a.shape[1] != 4:
+        raise ValueError("expected an (n, 4) float32 array of x, y, z, m")
+    return a
+
+
+class Tree:
+    """The oracle's octree over fp32 (x, y, z, m) sources, built in fp64."""
+
+    def __init__(self, pos_mass, key_bits=63, leaf_cap=16):
+        self.src = _f4(pos_mass)  # kept alive: the C side keeps a pointer to it
+        self.n = self.src.shape[0]
+        self.key_bits = key_bits
+        self.leaf_cap = leaf_cap
+        self._h = lib().orc_build(_ptr(self.src), self.n, key_bits, leaf_cap)
+        if not self._h:
+            raise ValueError("invalid oracle build arguments")
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            lib().orc_free(h)
+            self._h = None
+
+    def bbox(self):
+        lo = np.zeros(3)
+        hi = np.zeros(3)
+        L = np.zeros(1)
+        lib().orc_bbox(self._h, _ptr(lo), _ptr(hi), _ptr(L))
+        return lo, hi, float(L[0])
+
+    def keys(self):
+        k = np.zeros(self.n, dtype=np.uint64)
+        lib().orc_keys(self._h, _ptr(k))
+        return k
+
+    def perm(self):
+        p = np.zeros(self.n, dtype=np.int64)
+        lib().orc_perm(self._h, _ptr(p))
+        return p
+
+    def cells(self):
+        nc = lib().orc_ncells(self._h)
+        out = dict(
+            level=np.zeros(nc, np.int32), is_leaf=np.zeros(nc, np.int32),
+            prefix=np.zeros(nc, np.uint64), start=np.zeros(nc, np.int64),
+            count=np.zeros(nc, np.int64), n_children=np.zeros(nc, np.int32),
+            mass=np.zeros(nc), com=np.zeros((nc, 3)))
+        lib().orc_cells(self._h, *[_ptr(out[k]) for k in
+                                   ("level", "is_leaf", "prefix", "start", "count",
+                                    "n_children", "mass", "com")])
+        return out
+
+    def gravity(self, theta, G=1.0, eps=0.0, targets=None, which=None, tie_mode=0):
+        """(n_t, 4) fp64 (ax, ay, az, phi), interactions and near-ties per target.
+
+        targets=None: the sources are the targets, self excluded.  which selects
+        a subset of targets by index."""
+        t = None if targets is None else _f4(targets)
+        w = None if which is None else np.ascontiguousarray(which, dtype=np.int64)
+        nt = (self.n if t is None else t.shape[0]) if w is None else w.shape[0]
+        out = np.zeros((nt, 4))
+        ni = np.zeros(nt, np.int64)
+        nties = np.zeros(nt, np.int64)
+        lib().orc_bh(self._h, _ptr(t), _ptr(w), nt, float(theta), float(G), float(eps),
+                     int(tie_mode), _ptr(out), _ptr(ni), _ptr(nties))
+        return out, ni, nties
+
+
+def direct(pos_mass, G=1.0, eps=0.0, targets=None, which=None):
+    """The O(N^2) direct sum in fp64: (n_t, 4) (ax, ay, az, phi)."""
+    src = _f4(pos_mass)
+    t = None if targets is None else _f4(targets)
+    w = None if which is None else np.ascontiguousarray(which, dtype=np.int64)
+    nt = (src.shape[0] if t is None else t.shape[0]) if w is None else w.shape[0]
+    out = np.zeros((nt, 4))
+    lib().orc_direct(_ptr(src), src.shape[0], _ptr(t), _ptr(w), nt, float(G), float(eps),
+                     _ptr(out))
+    return out
+
+
+def threads():
+    return lib().orc_threads()
