@@ -1,0 +1,229 @@
+"""Barnes-Hut octree self-gravity for AMD MI355X (gfx950).
+
+A thin ctypes binding over libbh.so (include/bh.h): argument marshalling only,
+every step of the computation runs in the library's HIP kernels.  PyTorch is
+used for device memory and streams.
+
+    import torch, barnes_hut_tree_amd as bh
+    tree = bh.BarnesHut(max_sources=n, key_bits=63, leaf_cap=16)
+    tree.build(pos_mass)                  # (n, 4) float32 cuda tensor: x, y, z, m
+    out = tree.gravity(theta=0.5, G=1.0, eps=1e-3)   # (n, 4): ax, ay, az, phi
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbh.so")
+
+BH_OK = 0
+BH_ERR_INVALID = -1
+BH_ERR_OOM = -2
+BH_ERR_HIP = -3
+BH_ERR_CAPACITY = -4
+BH_ERR_NONFINITE = -5
+BH_ERR_NOT_BUILT = -6
+
+EXPORTS = ("bh_create", "bh_build", "bh_gravity", "bh_gravity_counted", "bh_sync", "bh_destroy",
+           "bh_status_string", "bh_get_keys", "bh_get_node_count", "bh_get_nodes", "bh_get_bbox",
+           "bh_set_profiling", "bh_get_profile")
+
+NODE_DTYPE_FIELDS = [("com_x", "f4"), ("com_y", "f4"), ("com_z", "f4"), ("mass", "f4"),
+                     ("start", "u4"), ("count", "u4"), ("skip", "u4"), ("meta", "u4")]
+
+
+class BHError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s: %s (%d)" % (where, status_string(status), status))
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [("key_bits", ctypes.c_int32), ("leaf_cap", ctypes.c_int32),
+                ("node_capacity", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load_library():
+    """Load libbh.so (built in-tree).  Fails loudly when it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libbh.so is not built: run `python -m barnes_hut_tree_amd.build` "
+                          "(or __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    sigs = {
+        "bh_create": [ctypes.POINTER(P), i64, i64, ctypes.POINTER(_Params)],
+        "bh_build": [P, P, i64, P],
+        "bh_gravity": [P, P, i64, f32, f32, f32, P, P],
+        "bh_gravity_counted": [P, P, i64, f32, f32, f32, P, P, P],
+        "bh_sync": [P],
+        "bh_destroy": [P],
+        "bh_get_keys": [P, P, P, P],
+        "bh_get_node_count": [P, ctypes.POINTER(i64), P],
+        "bh_get_nodes": [P, P, i64, P],
+        "bh_get_bbox": [P, P, P, P, P],
+        "bh_set_profiling": [P, i32],
+        "bh_get_profile": [P, P, i32],
+    }
+    for name, args in sigs.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    L.bh_status_string.argtypes = [ctypes.c_int]
+    L.bh_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def status_string(status):
+    return load_library().bh_status_string(int(status)).decode()
+
+
+def _check(status, where):
+    if status != BH_OK:
+        raise BHError(status, where)
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _rows(t, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != torch.float32:
+        raise TypeError("%s must be a float32 CUDA tensor" % name)
+    if t.dim() != 2 or t.shape[1] != 4 or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous (n, 4) tensor" % name)
+    return t
+
+
+class BarnesHut:
+    """One octree context (bh_ctx) on the current device."""
+
+    def __init__(self, max_sources, max_targets=0, key_bits=63, leaf_cap=16, node_capacity=0):
+        L = load_library()
+        self._h = ctypes.c_void_p()
+        p = _Params(int(key_bits), int(leaf_cap), int(node_capacity))
+        _check(L.bh_create(ctypes.byref(self._h), int(max_sources), int(max_targets),
+                           ctypes.byref(p)), "bh_create")
+        self.max_sources = int(max_sources)
+        self.max_targets = int(max_targets)
+        self.key_bits = int(key_bits)
+        self.leaf_cap = int(leaf_cap)
+        self.n = 0
+
+    def close(self):
+        if getattr(self, "_h", None) and self._h.value:
+            load_library().bh_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def build(self, pos_mass):
+        t = _rows(pos_mass, "pos_mass")
+        _check(load_library().bh_build(self._h, ctypes.c_void_p(t.data_ptr()), t.shape[0],
+                                       _stream()), "bh_build")
+        self.n = t.shape[0]
+
+    def gravity(self, theta, G=1.0, eps=0.0, targets=None, out=None, interactions=None):
+        """(n_targets, 4) float32: ax, ay, az, phi in the caller's order.
+
+        targets=None: the built sources, each excluding itself.
+        interactions: optional uint64 (int64) CUDA tensor of 1 element that the
+        interaction count is added to."""
+        import torch
+        if targets is not None:
+            targets = _rows(targets, "targets")
+            nt = targets.shape[0]
+            tp = ctypes.c_void_p(targets.data_ptr())
+        else:
+            nt = self.n
+            tp = ctypes.c_void_p()
+        if out is None:
+            out = torch.empty((nt, 4), dtype=torch.float32, device="cuda")
+        else:
+            _rows(out, "out")
+        L = load_library()
+        if interactions is None:
+            st = L.bh_gravity(self._h, tp, nt, float(theta), float(G), float(eps),
+                              ctypes.c_void_p(out.data_ptr()), _stream())
+        else:
+            st = L.bh_gravity_counted(self._h, tp, nt, float(theta), float(G), float(eps),
+                                      ctypes.c_void_p(out.data_ptr()),
+                                      ctypes.c_void_p(interactions.data_ptr()), _stream())
+        _check(st, "bh_gravity")
+        return out
+
+    def count_interactions(self, theta, eps=0.0, targets=None):
+        import torch
+        cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+        self.gravity(theta, 1.0, eps, targets=targets, interactions=cnt)
+        return int(cnt.item())
+
+    def sync(self):
+        _check(load_library().bh_sync(self._h), "bh_sync")
+
+    def status(self):
+        return load_library().bh_sync(self._h)
+
+    def keys(self):
+        """Sorted Morton keys (int64 view of uint64) and the sorted permutation."""
+        import torch
+        k = torch.empty(self.n, dtype=torch.int64, device="cuda")
+        p = torch.empty(self.n, dtype=torch.int32, device="cuda")
+        _check(load_library().bh_get_keys(self._h, ctypes.c_void_p(k.data_ptr()),
+                                          ctypes.c_void_p(p.data_ptr()), _stream()), "bh_get_keys")
+        return k, p
+
+    def node_count(self):
+        n = ctypes.c_int64()
+        _check(load_library().bh_get_node_count(self._h, ctypes.byref(n), _stream()),
+               "bh_get_node_count")
+        return n.value
+
+    def nodes(self):
+        """Node records as an (n_nodes, 8) int32 CUDA tensor (bh_node layout)."""
+        import torch
+        nn = self.node_count()
+        buf = torch.empty((max(nn, 1), 8), dtype=torch.int32, device="cuda")
+        _check(load_library().bh_get_nodes(self._h, ctypes.c_void_p(buf.data_ptr()), nn,
+                                           _stream()), "bh_get_nodes")
+        return buf[:nn]
+
+    def bbox(self):
+        lo = (ctypes.c_double * 3)()
+        hi = (ctypes.c_double * 3)()
+        L = ctypes.c_double()
+        _check(load_library().bh_get_bbox(self._h, lo, hi, ctypes.byref(L), _stream()),
+               "bh_get_bbox")
+        return list(lo), list(hi), L.value
+
+    def set_profiling(self, on=True):
+        _check(load_library().bh_set_profiling(self._h, int(bool(on))), "bh_set_profiling")
+
+    def profile(self):
+        """Device ms of [bbox+keys, sort, tree, centre of mass, walk]."""
+        ms = (ctypes.c_float * 5)()
+        _check(load_library().bh_get_profile(self._h, ms, 5), "bh_get_profile")
+        return list(ms)
+
+
+def nodes_numpy(node_tensor):
+    """Split an (n, 8) int32 node tensor (on any device) into named numpy fields."""
+    import numpy as np
+    a = node_tensor.cpu().numpy()
+    f = a[:, :4].view(np.float32)
+    u = a[:, 4:].view(np.uint32)
+    meta = u[:, 3]
+    return dict(com=f[:, :3].copy(), mass=f[:, 3].copy(), start=u[:, 0].copy(),
+                count=u[:, 1].copy(), skip=u[:, 2].copy(), level=(meta & 0xff).astype(np.int32),
+                is_leaf=((meta >> 8) & 1).astype(np.int32))

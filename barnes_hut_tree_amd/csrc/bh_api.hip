@@ -1,0 +1,375 @@
+// C ABI of libbh.so: context, argument checks, launch sequencing, status.
+//
+// bh_build runs the steps of [Tree] 实现步骤 in order on one stream with no
+// host synchronisation: bounding box -> Morton keys -> stable sort (with the
+// sorted copy of the sources gathered in its last pass) -> octree -> centre
+// of mass.  bh_gravity runs the walk.  Every scalar one step hands to the next
+// (the root cube, node counts, the status word) stays in device memory.
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "bh_internal.h"
+
+using namespace bh;
+
+struct bh_ctx {
+    int device = 0;
+    int64_t max_src = 0, max_tgt = 0;
+    int key_bits = 63, bits = 21, leaf_cap = 16;
+    uint64_t node_cap = 0;
+
+    DevParams *prm = nullptr;
+    DevParams *host_prm = nullptr;   // pinned, for synchronous read-back
+    float *bbox_part = nullptr;
+    uint64_t *keys = nullptr, *keys_alt = nullptr;
+    uint32_t *vals = nullptr, *vals_alt = nullptr;
+    uint32_t *spine = nullptr;
+    float4 *spos = nullptr;
+    uint64_t *keys_sorted = nullptr;  // aliases keys or keys_alt after a build
+    uint32_t *perm = nullptr;         // aliases vals or vals_alt after a build
+    uint16_t *dc = nullptr;
+    uint32_t *blk_counts = nullptr, *blk_scan = nullptr;
+    uint32_t *first_node = nullptr, *level_list = nullptr;
+    Node *nodes = nullptr;
+
+    uint64_t *tkeys = nullptr, *tkeys_alt = nullptr;
+    uint32_t *tvals = nullptr, *tvals_alt = nullptr;
+    uint32_t *tspine = nullptr;
+    float4 *tpos = nullptr;
+
+    uint32_t n_src = 0;
+    bool built = false;
+    hipStream_t last_stream = nullptr;
+
+    bool prof = false;
+    hipEvent_t ev[8] = {};
+};
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+template <typename T>
+hipError_t dalloc(T **p, size_t count)
+{
+    if (count == 0) count = 1;
+    return hipMalloc((void **)p, count * sizeof(T));
+}
+
+void free_all(bh_ctx *c)
+{
+    void *ptrs[] = {c->prm, c->bbox_part, c->keys, c->keys_alt, c->vals, c->vals_alt, c->spine,
+                    c->spos, c->dc, c->blk_counts, c->blk_scan, c->first_node, c->level_list,
+                    c->nodes, c->tkeys, c->tkeys_alt, c->tvals, c->tvals_alt, c->tspine, c->tpos};
+    for (void *p : ptrs)
+        if (p) (void)hipFree(p);
+    if (c->host_prm) (void)hipHostFree(c->host_prm);
+    for (hipEvent_t &e : c->ev)
+        if (e) (void)hipEventDestroy(e);
+}
+
+void record(bh_ctx *c, int k, hipStream_t s)
+{
+    if (c->prof) (void)hipEventRecord(c->ev[k], s);
+}
+
+bh_status launch_status()
+{
+    return hipGetLastError() == hipSuccess ? BH_OK : BH_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *bh_status_string(int status)
+{
+    switch (status) {
+    case BH_OK: return "ok";
+    case BH_ERR_INVALID: return "invalid argument";
+    case BH_ERR_OOM: return "device allocation failed";
+    case BH_ERR_HIP: return "HIP runtime error";
+    case BH_ERR_CAPACITY: return "tree node capacity exceeded";
+    case BH_ERR_NONFINITE: return "non-finite source coordinate or mass";
+    case BH_ERR_NOT_BUILT: return "no successful build";
+    default: return "unknown status";
+    }
+}
+
+bh_status bh_create(bh_ctx **out, int64_t max_sources, int64_t max_targets,
+                    const bh_build_params *params)
+{
+    if (!out) return BH_ERR_INVALID;
+    *out = nullptr;
+    if (max_sources < 0 || max_targets < 0 || max_sources >= (int64_t)1 << 31 ||
+        max_targets >= (int64_t)1 << 31)
+        return BH_ERR_INVALID;
+    bh_build_params p = {63, 16, 0};
+    if (params) p = *params;
+    if ((p.key_bits != 63 && p.key_bits != 30) || p.leaf_cap < 1 || p.leaf_cap > kMaxLeafCap ||
+        p.node_capacity < 0)
+        return BH_ERR_INVALID;
+
+    bh_ctx *c = new (std::nothrow) bh_ctx();
+    if (!c) return BH_ERR_OOM;
+    if (hipGetDevice(&c->device) != hipSuccess) {
+        delete c;
+        return BH_ERR_HIP;
+    }
+    c->max_src = max_sources;
+    c->max_tgt = max_targets;
+    c->key_bits = p.key_bits;
+    c->bits = p.key_bits / 3;
+    c->leaf_cap = p.leaf_cap;
+    const uint64_t worst = (uint64_t)max_sources * (uint64_t)(c->bits + 1) + 1;
+    c->node_cap = p.node_capacity ? (uint64_t)p.node_capacity : worst;
+    if (c->node_cap > 0xfffffff0ull) c->node_cap = 0xfffffff0ull;
+
+    const size_t ns = (size_t)max_sources, nt = (size_t)max_targets;
+    const size_t tiles = build_blocks((uint32_t)ns);
+    bool ok = true;
+    ok &= dalloc(&c->prm, 1) == hipSuccess;
+    ok &= hipHostMalloc((void **)&c->host_prm, sizeof(DevParams), hipHostMallocDefault) == hipSuccess;
+    ok &= dalloc(&c->bbox_part, 8 * 1024) == hipSuccess;
+    ok &= dalloc(&c->keys, ns) == hipSuccess;
+    ok &= dalloc(&c->keys_alt, ns) == hipSuccess;
+    ok &= dalloc(&c->vals, ns) == hipSuccess;
+    ok &= dalloc(&c->vals_alt, ns) == hipSuccess;
+    ok &= dalloc(&c->spine, sort_spine_entries((uint32_t)ns)) == hipSuccess;
+    ok &= dalloc(&c->spos, ns) == hipSuccess;
+    ok &= dalloc(&c->dc, ns) == hipSuccess;
+    ok &= dalloc(&c->blk_counts, kBuildCols * tiles) == hipSuccess;
+    ok &= dalloc(&c->blk_scan, kBuildCols * tiles + 1) == hipSuccess;
+    ok &= dalloc(&c->first_node, ns + 1) == hipSuccess;
+    ok &= dalloc(&c->level_list, (size_t)c->node_cap) == hipSuccess;
+    ok &= dalloc(&c->nodes, (size_t)c->node_cap) == hipSuccess;
+    if (nt) {
+        ok &= dalloc(&c->tkeys, nt) == hipSuccess;
+        ok &= dalloc(&c->tkeys_alt, nt) == hipSuccess;
+        ok &= dalloc(&c->tvals, nt) == hipSuccess;
+        ok &= dalloc(&c->tvals_alt, nt) == hipSuccess;
+        ok &= dalloc(&c->tspine, sort_spine_entries((uint32_t)nt)) == hipSuccess;
+        ok &= dalloc(&c->tpos, nt) == hipSuccess;
+    }
+    for (hipEvent_t &e : c->ev) ok &= hipEventCreate(&e) == hipSuccess;
+    if (!ok) {
+        (void)hipGetLastError();
+        free_all(c);
+        delete c;
+        return BH_ERR_OOM;
+    }
+    *out = c;
+    return BH_OK;
+}
+
+bh_status bh_destroy(bh_ctx *c)
+{
+    if (!c) return BH_OK;
+    (void)hipDeviceSynchronize();
+    free_all(c);
+    delete c;
+    return BH_OK;
+}
+
+bh_status bh_build(bh_ctx *c, const float *src_pos_mass, int64_t n, void *stream)
+{
+    if (!c || n < 0 || n > c->max_src) return BH_ERR_INVALID;
+    if (n > 0 && (!src_pos_mass || !aligned16(src_pos_mass))) return BH_ERR_INVALID;
+    hipStream_t s = (hipStream_t)stream;
+    c->last_stream = s;
+    c->built = false;
+    const uint32_t un = (uint32_t)n;
+    const float4 *src = (const float4 *)src_pos_mass;
+
+    record(c, 0, s);
+    launch_bbox(src, un, c->bbox_part, bbox_partials(un), c->prm, c->bits, s);
+    if (un > 0) {
+        launch_morton(src, un, c->prm, c->bits, c->keys, c->vals, s);
+        record(c, 1, s);
+        radix_sort(c->keys, c->vals, c->keys_alt, c->vals_alt, &c->keys_sorted, &c->perm, un,
+                   c->key_bits, c->spine, src, c->spos, s);
+        record(c, 2, s);
+        build_tree(c->keys_sorted, c->spos, un, c->bits, c->leaf_cap, c->node_cap, c->dc,
+                   c->blk_counts, c->blk_scan, c->first_node, c->level_list, c->nodes, c->prm, s);
+        record(c, 3, s);
+        com_levels(c->keys_sorted, c->nodes, c->level_list, un, c->node_cap, c->bits, c->prm, s);
+        record(c, 4, s);
+    } else {
+        for (int k = 1; k <= 4; ++k) record(c, k, s);
+    }
+    bh_status st = launch_status();
+    if (st != BH_OK) return st;
+    c->n_src = un;
+    c->built = true;
+    return BH_OK;
+}
+
+static bh_status gravity_impl(bh_ctx *c, const float *targets, int64_t n_targets, float theta,
+                              float G, float eps, float *out, uint64_t *count, void *stream)
+{
+    if (!c) return BH_ERR_INVALID;
+    if (!c->built) return BH_ERR_NOT_BUILT;
+    if (n_targets < 0 || !(theta >= 0.f) || !(eps >= 0.f) || !__builtin_isfinite(G)) return BH_ERR_INVALID;
+    if (n_targets > 0 && (!out || !aligned16(out))) return BH_ERR_INVALID;
+    if (targets) {
+        if (n_targets > c->max_tgt || !aligned16(targets)) return BH_ERR_INVALID;
+    } else if ((uint32_t)n_targets != c->n_src) {
+        return BH_ERR_INVALID;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    c->last_stream = s;
+    const uint32_t nt = (uint32_t)n_targets;
+    if (nt == 0) return BH_OK;
+    if (c->n_src == 0) {
+        launch_fill_zero((float4 *)out, nt, s);
+        return launch_status();
+    }
+    WalkArgs a;
+    a.nodes = c->nodes;
+    a.src = c->spos;
+    a.prm = c->prm;
+    a.n_targets = nt;
+    a.theta = theta;
+    a.G = G;
+    a.eps = eps;
+    a.out = (float4 *)out;
+    a.count = (unsigned long long *)count;
+    if (targets) {
+        uint64_t *ko;
+        uint32_t *vo;
+        launch_morton((const float4 *)targets, nt, c->prm, c->bits, c->tkeys, c->tvals, s);
+        radix_sort(c->tkeys, c->tvals, c->tkeys_alt, c->tvals_alt, &ko, &vo, nt, c->key_bits,
+                   c->tspine, (const float4 *)targets, c->tpos, s);
+        a.tpos = c->tpos;
+        a.tperm = vo;
+        a.self = 0;
+    } else {
+        a.tpos = c->spos;
+        a.tperm = c->perm;
+        a.self = 1;
+    }
+    record(c, 5, s);
+    launch_walk(a, s);
+    record(c, 6, s);
+    return launch_status();
+}
+
+bh_status bh_gravity(bh_ctx *c, const float *targets, int64_t n_targets, float theta, float G,
+                     float eps, float *out_acc_pot, void *stream)
+{
+    return gravity_impl(c, targets, n_targets, theta, G, eps, out_acc_pot, nullptr, stream);
+}
+
+bh_status bh_gravity_counted(bh_ctx *c, const float *targets, int64_t n_targets, float theta,
+                             float G, float eps, float *out_acc_pot, uint64_t *interactions,
+                             void *stream)
+{
+    if (!interactions) return BH_ERR_INVALID;
+    return gravity_impl(c, targets, n_targets, theta, G, eps, out_acc_pot, interactions, stream);
+}
+
+static bh_status read_params(bh_ctx *c, hipStream_t s)
+{
+    if (hipMemcpyAsync(c->host_prm, c->prm, sizeof(DevParams), hipMemcpyDeviceToHost, s) !=
+        hipSuccess)
+        return BH_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return BH_ERR_HIP;
+    return BH_OK;
+}
+
+bh_status bh_sync(bh_ctx *c)
+{
+    if (!c) return BH_ERR_INVALID;
+    bh_status st = read_params(c, c->last_stream);
+    if (st != BH_OK) return st;
+    const uint32_t w = c->host_prm->status;
+    if (w & kStatusNonFinite) {
+        c->built = false;
+        return BH_ERR_NONFINITE;
+    }
+    if (w & kStatusCapacity) {
+        c->built = false;
+        return BH_ERR_CAPACITY;
+    }
+    return BH_OK;
+}
+
+bh_status bh_get_keys(bh_ctx *c, uint64_t *keys_sorted, uint32_t *perm, void *stream)
+{
+    if (!c || !c->built) return c ? BH_ERR_NOT_BUILT : BH_ERR_INVALID;
+    hipStream_t s = (hipStream_t)stream;
+    const size_t n = c->n_src;
+    if (n == 0) return BH_OK;
+    if (keys_sorted &&
+        hipMemcpyAsync(keys_sorted, c->keys_sorted, n * 8, hipMemcpyDeviceToDevice, s) != hipSuccess)
+        return BH_ERR_HIP;
+    if (perm && hipMemcpyAsync(perm, c->perm, n * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+        return BH_ERR_HIP;
+    return BH_OK;
+}
+
+bh_status bh_get_node_count(bh_ctx *c, int64_t *n_nodes, void *stream)
+{
+    if (!c || !n_nodes) return BH_ERR_INVALID;
+    if (!c->built) return BH_ERR_NOT_BUILT;
+    if (c->n_src == 0) {
+        *n_nodes = 0;
+        return BH_OK;
+    }
+    bh_status st = read_params(c, (hipStream_t)stream);
+    if (st != BH_OK) return st;
+    *n_nodes = c->host_prm->n_nodes;
+    return BH_OK;
+}
+
+bh_status bh_get_nodes(bh_ctx *c, bh_node *nodes, int64_t n_nodes, void *stream)
+{
+    if (!c || n_nodes < 0 || (uint64_t)n_nodes > c->node_cap || (n_nodes && !nodes))
+        return BH_ERR_INVALID;
+    if (!c->built) return BH_ERR_NOT_BUILT;
+    if (n_nodes == 0) return BH_OK;
+    if (hipMemcpyAsync(nodes, c->nodes, (size_t)n_nodes * sizeof(Node), hipMemcpyDeviceToDevice,
+                       (hipStream_t)stream) != hipSuccess)
+        return BH_ERR_HIP;
+    return BH_OK;
+}
+
+bh_status bh_get_bbox(bh_ctx *c, double *lo, double *hi, double *L, void *stream)
+{
+    if (!c || !lo || !hi || !L) return BH_ERR_INVALID;
+    if (!c->built) return BH_ERR_NOT_BUILT;
+    bh_status st = read_params(c, (hipStream_t)stream);
+    if (st != BH_OK) return st;
+    for (int a = 0; a < 3; ++a) {
+        lo[a] = c->host_prm->lo[a];
+        hi[a] = c->host_prm->hi[a];
+    }
+    *L = c->host_prm->L;
+    return BH_OK;
+}
+
+bh_status bh_set_profiling(bh_ctx *c, int enable)
+{
+    if (!c) return BH_ERR_INVALID;
+    c->prof = enable != 0;
+    return BH_OK;
+}
+
+bh_status bh_get_profile(bh_ctx *c, float *ms, int n)
+{
+    if (!c || !ms || n < 0) return BH_ERR_INVALID;
+    if (!c->prof) return BH_ERR_INVALID;
+    const int pairs[5][2] = {{0, 1}, {1, 2}, {2, 3}, {3, 4}, {5, 6}};
+    for (int k = 0; k < n && k < 5; ++k) {
+        if (hipEventSynchronize(c->ev[pairs[k][1]]) != hipSuccess) return BH_ERR_HIP;
+        float t = 0.f;
+        if (hipEventElapsedTime(&t, c->ev[pairs[k][0]], c->ev[pairs[k][1]]) != hipSuccess)
+            return BH_ERR_HIP;
+        ms[k] = t;
+    }
+    return BH_OK;
+}
+
+}  // extern "C"

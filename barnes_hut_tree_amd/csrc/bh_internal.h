@@ -1,0 +1,101 @@
+// Internal declarations shared by the HIP translation units of libbh.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/bh.h"
+
+namespace bh {
+
+constexpr int kMaxLevels = 22;      // levels 0..21 for 63-bit keys
+constexpr int kMaxLeafCap = 256;
+
+// Device status bits (a word in DevParams; 0 = fine).
+constexpr uint32_t kStatusNonFinite = 1u;
+constexpr uint32_t kStatusCapacity = 2u;
+
+// Per-build scalars kept in device memory, so that no step needs the host to
+// read back an intermediate value.
+struct DevParams {
+    double lo[3];        // min corner of the sources
+    double hi[3];        // max corner
+    double L;            // root cube side = largest extent
+    double scale;        // 2^bits / L, or 0 when L == 0
+    uint32_t status;     // kStatus* bits
+    uint32_t n_nodes;    // nodes emitted by the build
+    uint32_t n_src;      // sources of this build
+    uint32_t pad;
+    uint32_t level_count[kMaxLevels];
+    uint32_t level_offset[kMaxLevels + 1];
+};
+
+// Pre-order node record; the public bh_node has the same layout.
+struct alignas(16) Node {
+    float cx, cy, cz, m;
+    uint32_t start, count, skip, meta;
+};
+static_assert(sizeof(Node) == 32, "node is 32 bytes");
+static_assert(sizeof(Node) == sizeof(bh_node), "node matches the public record");
+
+constexpr uint32_t kLeafBit = 1u << 8;
+__host__ __device__ inline uint32_t node_level(uint32_t meta) { return meta & 0xffu; }
+
+// Radix sort geometry: a tile of 4096 keys per workgroup of 256 threads.
+constexpr int kSortThreads = 256;
+constexpr int kSortItems = 16;
+constexpr int kSortTile = kSortThreads * kSortItems;
+constexpr int kRadix = 256;
+
+// Tree build geometry: 1024 key positions per workgroup of 256 threads.
+constexpr int kBuildThreads = 256;
+constexpr int kBuildTile = 1024;
+constexpr int kBuildCols = 1 + kMaxLevels;   // node count + one count per level
+
+// ---- launchers (each defined in its own .hip file) ------------------------
+
+// bbox.hip
+void launch_bbox(const float4 *src, uint32_t n, float *partials, uint32_t n_partials,
+                 DevParams *prm, int bits, hipStream_t s);
+uint32_t bbox_partials(uint32_t n);
+void launch_morton(const float4 *pts, uint32_t n, const DevParams *prm, int bits,
+                   uint64_t *keys, uint32_t *idx, hipStream_t s);
+
+// radix_sort.hip
+size_t sort_spine_entries(uint32_t n);
+// Stable LSD sort of (keys, vals) over the low `key_bits` bits.  Ping-pongs
+// between the two buffer pairs; the result ends in (keys_out, vals_out).  With
+// gather_src != NULL the last pass also writes gather_dst[i] = gather_src[vals[i]].
+void radix_sort(uint64_t *keys, uint32_t *vals, uint64_t *keys_alt, uint32_t *vals_alt,
+                uint64_t **keys_out, uint32_t **vals_out, uint32_t n, int key_bits,
+                uint32_t *spine, const float4 *gather_src, float4 *gather_dst, hipStream_t s);
+
+// generic single-workgroup exclusive scan: out[i] = sum(in[0..i)), out[n] = total
+void launch_scan_u32(const uint32_t *in, uint32_t *out, uint32_t n, hipStream_t s);
+
+// build.hip
+uint32_t build_blocks(uint32_t n);
+void build_tree(const uint64_t *keys_sorted, const float4 *spos, uint32_t n, int bits,
+                int leaf_cap, uint64_t node_capacity, uint16_t *dc, uint32_t *block_counts,
+                uint32_t *block_scan, uint32_t *first_node, uint32_t *level_list, Node *nodes,
+                DevParams *prm, hipStream_t s);
+void com_levels(const uint64_t *keys_sorted, Node *nodes, const uint32_t *level_list,
+                uint32_t n, uint64_t node_capacity, int bits, DevParams *prm, hipStream_t s);
+
+// traverse.hip
+struct WalkArgs {
+    const Node *nodes;
+    const float4 *src;          // sources in Morton order
+    const float4 *tpos;         // targets in Morton order
+    const uint32_t *tperm;      // caller index of each sorted target
+    const DevParams *prm;
+    uint32_t n_targets;
+    int self;                   // targets are the sources (exclude i == j)
+    float theta, G, eps;
+    float4 *out;
+    unsigned long long *count;  // optional interaction counter
+};
+void launch_walk(const WalkArgs &a, hipStream_t s);
+void launch_fill_zero(float4 *out, uint32_t n, hipStream_t s);
+
+}  // namespace bh

@@ -1,0 +1,242 @@
+// Stable LSD radix sort of (Morton key, index) pairs, 8-bit digits.
+//
+// The pages order particles by Morton key before the walk ([Tree] 实现步骤,
+// 粒子空间排序) and keep the particle data in place behind a gather index
+// ([GASPHiA] 排序算法: sort indices, not data).  Here the sort carries the
+// index as payload and its last pass also gathers a sorted copy of the
+// float4 rows, so the walk reads contiguous memory.
+//
+// Per pass three kernels: a per-tile digit histogram, one exclusive scan over
+// the digit-major [digit][tile] table (global offsets), and a scatter in
+// which each workgroup ranks its tile stably in LDS (64-lane ballots give the
+// rank among equal digits within a wave row) and writes the tile out
+// digit-group by digit-group, so writes of one digit are contiguous.
+#include "bh_internal.h"
+
+namespace bh {
+namespace {
+
+constexpr int kWaves = kSortThreads / 64;
+
+__device__ inline uint32_t lane_id() { return threadIdx.x & 63; }
+
+__device__ inline uint32_t wave_incl_scan(uint32_t v)
+{
+    const uint32_t lane = lane_id();
+    for (int o = 1; o < 64; o <<= 1) {
+        uint32_t t = __shfl_up(v, o, 64);
+        if (lane >= (uint32_t)o) v += t;
+    }
+    return v;
+}
+
+// Exclusive scan of v over a 256-thread workgroup; *total receives the sum.
+__device__ inline uint32_t block_excl_scan_256(uint32_t v, uint32_t *tmp, uint32_t *total)
+{
+    const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
+    uint32_t incl = wave_incl_scan(v);
+    if (lane == 63) tmp[wave] = incl;
+    __syncthreads();
+    uint32_t off = 0, sum = 0;
+    for (int w = 0; w < kWaves; ++w) {
+        uint32_t t = tmp[w];
+        if ((uint32_t)w < wave) off += t;
+        sum += t;
+    }
+    *total = sum;
+    __syncthreads();
+    return off + incl - v;
+}
+
+__global__ __launch_bounds__(kSortThreads) void k_hist(const uint64_t *__restrict__ keys, uint32_t n,
+                                                       int shift, uint32_t *__restrict__ hist,
+                                                       uint32_t n_tiles)
+{
+    __shared__ uint32_t h[kWaves][kRadix];
+    const uint32_t wave = threadIdx.x >> 6;
+    for (int d = threadIdx.x; d < kWaves * kRadix; d += kSortThreads) (&h[0][0])[d] = 0;
+    __syncthreads();
+    const uint32_t base = blockIdx.x * kSortTile;
+#pragma unroll 4
+    for (int k = 0; k < kSortItems; ++k) {
+        uint32_t i = base + k * kSortThreads + threadIdx.x;
+        if (i < n) atomicAdd(&h[wave][(keys[i] >> shift) & 0xff], 1u);
+    }
+    __syncthreads();
+    const uint32_t d = threadIdx.x;
+    uint32_t c = 0;
+    for (int w = 0; w < kWaves; ++w) c += h[w][d];
+    hist[d * n_tiles + blockIdx.x] = c;
+}
+
+template <bool GATHER>
+__global__ __launch_bounds__(kSortThreads) void k_scatter(
+    const uint64_t *__restrict__ kin, const uint32_t *__restrict__ vin,
+    uint64_t *__restrict__ kout, uint32_t *__restrict__ vout, uint32_t n, int shift,
+    const uint32_t *__restrict__ offsets, uint32_t n_tiles, const float4 *__restrict__ gsrc,
+    float4 *__restrict__ gdst)
+{
+    __shared__ uint64_t skey[kSortTile];
+    __shared__ uint32_t sval[kSortTile];
+    __shared__ uint32_t wcnt[kWaves][kRadix];
+    __shared__ uint32_t bstart[kRadix];
+    __shared__ uint32_t tmp[kWaves];
+
+    const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+    for (int d = threadIdx.x; d < kWaves * kRadix; d += kSortThreads) (&wcnt[0][0])[d] = 0;
+    __syncthreads();
+
+    // Each wave owns 1024 consecutive keys of the tile; row k holds keys
+    // [k*64, k*64+64) of that range, so (wave, row, lane) is input order.
+    const uint32_t base = blockIdx.x * kSortTile + wave * (kSortItems * 64);
+    uint64_t key[kSortItems];
+    uint32_t val[kSortItems];
+    uint32_t rank[kSortItems];
+#pragma unroll
+    for (int k = 0; k < kSortItems; ++k) {
+        const uint32_t i = base + k * 64 + lane;
+        const bool valid = i < n;
+        key[k] = valid ? kin[i] : 0;
+        val[k] = valid ? vin[i] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kSortItems; ++k) {
+        const uint32_t i = base + k * 64 + lane;
+        const bool valid = i < n;
+        const uint32_t digit = (uint32_t)(key[k] >> shift) & 0xffu;
+        uint64_t peers = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const bool bit = (digit >> b) & 1u;
+            const uint64_t m = __ballot(bit);
+            peers &= bit ? m : ~m;
+        }
+        const uint32_t before = wcnt[wave][digit];
+        const uint32_t r = (uint32_t)__popcll(peers & lt_mask);
+        if (valid && r == 0) wcnt[wave][digit] = before + (uint32_t)__popcll(peers);
+        rank[k] = before + r;
+    }
+    __syncthreads();
+
+    // Per digit: the exclusive prefix over waves, and the tile-local start.
+    {
+        const uint32_t d = threadIdx.x;
+        uint32_t run = 0;
+        for (int w = 0; w < kWaves; ++w) {
+            uint32_t c = wcnt[w][d];
+            wcnt[w][d] = run;
+            run += c;
+        }
+        uint32_t total;
+        const uint32_t start = block_excl_scan_256(run, tmp, &total);
+        bstart[d] = start;
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int k = 0; k < kSortItems; ++k) {
+        const uint32_t i = base + k * 64 + lane;
+        if (i < n) {
+            const uint32_t digit = (uint32_t)(key[k] >> shift) & 0xffu;
+            const uint32_t pos = bstart[digit] + wcnt[wave][digit] + rank[k];
+            skey[pos] = key[k];
+            sval[pos] = val[k];
+        }
+    }
+    __syncthreads();
+
+    const uint32_t tile_base = blockIdx.x * kSortTile;
+    const uint32_t tile_n = min((uint32_t)kSortTile, n - tile_base);
+#pragma unroll 4
+    for (int k = 0; k < kSortItems; ++k) {
+        const uint32_t j = k * kSortThreads + threadIdx.x;
+        if (j < tile_n) {
+            const uint64_t kk = skey[j];
+            const uint32_t vv = sval[j];
+            const uint32_t digit = (uint32_t)(kk >> shift) & 0xffu;
+            const uint32_t g = offsets[digit * n_tiles + blockIdx.x] + (j - bstart[digit]);
+            kout[g] = kk;
+            vout[g] = vv;
+            if (GATHER) gdst[g] = gsrc[vv];
+        }
+    }
+}
+
+constexpr int kScanThreads = 1024;
+
+// Exclusive scan of n entries by one workgroup: each thread sums a contiguous
+// chunk, the 1024 sums are scanned, then each chunk is rescanned and written.
+__global__ __launch_bounds__(kScanThreads) void k_scan(const uint32_t *__restrict__ in,
+                                                       uint32_t *__restrict__ out, uint32_t n)
+{
+    __shared__ uint32_t tmp[kScanThreads / 64];
+    const uint32_t chunk = (n + kScanThreads - 1) / kScanThreads;
+    const uint32_t b = min(n, threadIdx.x * chunk), e = min(n, b + chunk);
+    uint32_t s = 0;
+    for (uint32_t i = b; i < e; ++i) s += in[i];
+    const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
+    const uint32_t incl = wave_incl_scan(s);
+    if (lane == 63) tmp[wave] = incl;
+    __syncthreads();
+    uint32_t off = 0, total = 0;
+    for (int w = 0; w < kScanThreads / 64; ++w) {
+        uint32_t t = tmp[w];
+        if ((uint32_t)w < wave) off += t;
+        total += t;
+    }
+    uint32_t run = off + incl - s;
+    for (uint32_t i = b; i < e; ++i) {
+        uint32_t v = in[i];
+        out[i] = run;
+        run += v;
+    }
+    if (threadIdx.x == 0) out[n] = total;
+}
+
+}  // namespace
+
+size_t sort_spine_entries(uint32_t n)
+{
+    size_t tiles = (n + kSortTile - 1) / kSortTile;
+    if (tiles == 0) tiles = 1;
+    return 2 * (size_t)kRadix * tiles + 1;
+}
+
+void launch_scan_u32(const uint32_t *in, uint32_t *out, uint32_t n, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, s, in, out, n);
+}
+
+void radix_sort(uint64_t *keys, uint32_t *vals, uint64_t *keys_alt, uint32_t *vals_alt,
+                uint64_t **keys_out, uint32_t **vals_out, uint32_t n, int key_bits,
+                uint32_t *spine, const float4 *gather_src, float4 *gather_dst, hipStream_t s)
+{
+    uint64_t *ka = keys, *kb = keys_alt;
+    uint32_t *va = vals, *vb = vals_alt;
+    const uint32_t tiles = (n + kSortTile - 1) / kSortTile;
+    const uint32_t entries = kRadix * tiles;
+    uint32_t *hist = spine, *offs = spine + entries;
+    const int passes = (key_bits + 7) / 8;
+    for (int p = 0; p < passes && n > 0; ++p) {
+        const int shift = 8 * p;
+        const bool last = (p == passes - 1);
+        hipLaunchKernelGGL(k_hist, dim3(tiles), dim3(kSortThreads), 0, s, ka, n, shift, hist,
+                           tiles);
+        launch_scan_u32(hist, offs, entries, s);
+        if (last && gather_src) {
+            hipLaunchKernelGGL(k_scatter<true>, dim3(tiles), dim3(kSortThreads), 0, s, ka, va, kb,
+                               vb, n, shift, offs, tiles, gather_src, gather_dst);
+        } else {
+            hipLaunchKernelGGL(k_scatter<false>, dim3(tiles), dim3(kSortThreads), 0, s, ka, va,
+                               kb, vb, n, shift, offs, tiles, (const float4 *)nullptr,
+                               (float4 *)nullptr);
+        }
+        uint64_t *tk = ka; ka = kb; kb = tk;
+        uint32_t *tv = va; va = vb; vb = tv;
+    }
+    *keys_out = ka;
+    *vals_out = va;
+}
+
+}  // namespace bh

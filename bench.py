@@ -1,0 +1,197 @@
+"""Benchmark: one gravity step = tree build + tree walk over all particles.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload plummer]
+
+Default workload: an equal-mass Plummer sphere of N = 2^20 particles (scale
+radius 1, truncated at 20), fp32 float4, theta = 0.5, G = 1, Plummer
+softening eps = 0.01, leaf capacity 16, 63-bit Morton keys, fed in random
+(generation) order.  Inputs are synthetic (workloads.py) and resident in
+device memory before timing starts.  One step = bh_build + bh_gravity (keys,
+sort, tree, centre of mass, walk), from caller-order input to caller-order
+output.  Prints one JSON line.
+
+value = interactions per second of the whole step (interactions = accepted
+nodes + particle pairs of the walk, counted by the library in an untimed
+pass).  The roofline object describes the walk kernel (the dominant one),
+counted at 20 flops per interaction against the fp32 vector peak.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms per gravity step + interactions/s at N=2^20, θ=0.5, fp32 (1 GPU)"
+FLOPS_PER_INTERACTION = 20
+FP32_PEAK_TFLOPS = 157.3
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def make_workload(name):
+    import workloads as W
+    if name == "plummer":
+        return W.plummer(1 << 20, seed=3), dict(theta=0.5, G=1.0, eps=0.01), \
+            "plummer_n1048576_random_order"
+    if name == "lattice":
+        return W.lattice(100, shuffled=True, seed=2), dict(theta=0.5, G=1.0, eps=1e-3), \
+            "lattice_n1000000_shuffled"
+    if name == "galaxy":
+        return W.galaxy_pair()[0], dict(theta=0.5, G=1.0, eps=0.02), "galaxy_pair_n5000000"
+    if name == "uniform":
+        return W.uniform_cube(4096, seed=1), dict(theta=0.5, G=1.0, eps=1e-3), "uniform_n4096"
+    raise SystemExit("unknown workload " + name)
+
+
+def walk_source_hash():
+    """Hash of the walk kernel source: counter summaries taken for another
+    version of the kernel are not reported."""
+    path = os.path.join(ROOT, "barnes_hut_tree_amd", "csrc", "traverse.hip")
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(workload):
+    """HBM bytes per walk launch from the committed rocprofv3 counter summary,
+    or None when absent or taken for a different walk kernel source."""
+    path = os.path.join(PROFILES, "walk_%s_traffic.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("walk_source_sha256_16") != walk_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(p, prm, key_bits, leaf_cap, budget_s=8.0):
+    """The oracle (fp64, OpenMP) on the host: full tree build plus the walk
+    for a random sample of targets sized to about budget_s seconds, scaled to
+    the whole step."""
+    import numpy as np
+
+    import oracle
+    n = p.shape[0]
+    t0 = time.perf_counter()
+    tree = oracle.Tree(p, key_bits, leaf_cap)
+    t_build = time.perf_counter() - t0
+    rng = np.random.default_rng(99)
+    m = min(n, 1 << 13)
+    which = np.sort(rng.choice(n, m, replace=False))
+    t0 = time.perf_counter()
+    _, ni, _ = tree.gravity(prm["theta"], prm["G"], prm["eps"], which=which)
+    t_walk = time.perf_counter() - t0
+    if t_walk < budget_s and m < n:
+        m = int(min(n, m * budget_s / max(t_walk, 1e-3)))
+        which = np.sort(rng.choice(n, m, replace=False))
+        t0 = time.perf_counter()
+        _, ni, _ = tree.gravity(prm["theta"], prm["G"], prm["eps"], which=which)
+        t_walk = time.perf_counter() - t0
+    per_target = t_walk / m
+    t_step = t_build + per_target * n
+    inter = float(ni.sum()) * n / m
+    return {
+        "value": inter / t_step, "unit": "interactions/s", "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": "full fp64 tree build (%.2f s) + walk of %d random targets of %d (%.2f s), "
+                  "scaled to all targets: %.2f s per step" % (t_build, m, n, t_walk, t_step),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="plummer")
+    ap.add_argument("--leaf-cap", type=int, default=16)
+    ap.add_argument("--key-bits", type=int, default=63)
+    ap.add_argument("--theta", type=float, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the walk has no multi-GPU path in this build "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import barnes_hut_tree_amd as bh
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    p, prm, wname = make_workload(args.workload)
+    if args.theta is not None:
+        prm["theta"] = args.theta
+    n = p.shape[0]
+    src = torch.from_numpy(p).cuda()
+    out = torch.empty((n, 4), dtype=torch.float32, device="cuda")
+    tree = bh.BarnesHut(n, 0, args.key_bits, args.leaf_cap)
+
+    def step():
+        tree.build(src)
+        tree.gravity(prm["theta"], prm["G"], prm["eps"], out=out)
+
+    for _ in range(args.warmup):
+        step()
+    tree.sync()
+    interactions = tree.count_interactions(prm["theta"], prm["eps"])
+
+    # per-phase device times, from one profiled step outside the timed region
+    tree.set_profiling(True)
+    step()
+    phases = tree.profile()
+    tree.set_profiling(False)
+    tree.sync()
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        tree.build(src)
+        ev[k][0].record(stream)
+        tree.gravity(prm["theta"], prm["G"], prm["eps"], out=out)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    tree.sync()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    walk_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    value = interactions / (ms_step * 1e-3)
+
+    achieved = FLOPS_PER_INTERACTION * interactions / (walk_ms * 1e-3) / 1e12
+    roofline = {"bound": "alu", "achieved": round(achieved, 3), "peak": FP32_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK_TFLOPS, 4),
+                "traffic": read_traffic(wname)}
+
+    rec = {
+        "metric": METRIC, "value": value, "unit": "interactions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wname, "n": n, "theta": prm["theta"], "G": prm["G"],
+                   "eps": prm["eps"], "leaf_cap": args.leaf_cap, "key_bits": args.key_bits,
+                   "interactions_per_step": interactions,
+                   "walk_ms": round(walk_ms, 4),
+                   "phase_ms": {k: round(v, 4) for k, v in zip(
+                       ("bbox_keys", "sort", "tree", "com", "walk"), phases)}},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(p, prm, args.key_bits, args.leaf_cap)
+    tree.close()
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

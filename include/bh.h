@@ -1,0 +1,151 @@
+/*
+ * bh.h — Barnes-Hut octree self-gravity on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libbh.so.  Plain pointers and sizes only.  All device pointers are
+ * HIP device memory on the current device; every `stream` argument is a
+ * hipStream_t passed as void* (NULL = the default stream).
+ *
+ * The operations follow these pages (cited by title and section):
+ *   [GASPHiA]  "GASPHiA中的自引力树代码效率与优化分析"
+ *   [Tree]     "树结构（基于根据 Burtscher 和 Pingali 的研究）" and its embedded
+ *              article "基于稠密存储的并行树构建实现方案"
+ *   [SBH]      notes on "Stochastic Barnes-Hut Approximation for Fast Summation
+ *              on the GPU"
+ *
+ * Conventions
+ *   Particles are float4 rows (x, y, z, m), 16 bytes each, 16-byte aligned
+ *   ([Tree] 构建树结构: the w component carries the mass).
+ *   Every call is stream-ordered and asynchronous unless stated otherwise;
+ *   pointers must stay valid until the stream reaches the call.
+ *   Argument errors are returned synchronously.  Conditions found on the
+ *   device (non-finite coordinates, node-capacity overflow) are recorded in a
+ *   device status word and returned by bh_sync; a build that failed on the
+ *   device leaves the context unbuilt for the next bh_gravity.
+ *   A context is not thread-safe: use one per host thread / stream.
+ *   Limits: n < 2^31 particles.
+ */
+#ifndef BH_H
+#define BH_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct bh_ctx bh_ctx;
+
+typedef enum bh_status {
+    BH_OK = 0,
+    BH_ERR_INVALID = -1,    /* bad argument: NULL, negative or too-large size, misaligned pointer, bad parameter */
+    BH_ERR_OOM = -2,        /* device allocation failed in bh_create */
+    BH_ERR_HIP = -3,        /* a HIP runtime call or kernel launch failed */
+    BH_ERR_CAPACITY = -4,   /* the tree needed more nodes than node_capacity */
+    BH_ERR_NONFINITE = -5,  /* a source coordinate or mass is NaN or infinite */
+    BH_ERR_NOT_BUILT = -6   /* bh_gravity before a successful bh_build */
+} bh_status;
+
+/* Build parameters, fixed for the life of a context.
+ *   key_bits      63 (21 bits per axis) or 30 (10 bits per axis): the depth of
+ *                 the Morton key of [Tree] 实现步骤 and the deepest tree level.
+ *   leaf_cap      B >= 1: a cell holding more than B particles is split into its
+ *                 octants unless it is at the deepest level ([Tree] 实现步骤: a
+ *                 leaf holds a few particles).  At most 256.
+ *   node_capacity maximum number of tree nodes; 0 selects the worst case
+ *                 max_sources * (key_bits/3 + 1) + 1, which can never overflow. */
+typedef struct bh_build_params {
+    int32_t key_bits;
+    int32_t leaf_cap;
+    int64_t node_capacity;
+} bh_build_params;
+
+/* One tree node as stored on the device (32 bytes), in pre-order: a node's
+ * subtree is the index range [self, skip).  Children follow their parent in
+ * octant order 0..7, the octant numbering of [Tree] 构建树结构 (x upper half
+ * = 1, y = 2, z = 4).  com_x..mass follow [GASPHiA] 计算节点质心. */
+typedef struct bh_node {
+    float com_x, com_y, com_z;  /* centre of mass (cell centre when mass is 0) */
+    float mass;                 /* total mass of the cell */
+    uint32_t start;             /* first particle, as an index into the Morton-sorted order */
+    uint32_t count;             /* number of particles in the cell */
+    uint32_t skip;              /* pre-order index just past this subtree */
+    uint32_t meta;              /* bits 0-7: level (root = 0); bit 8: leaf */
+} bh_node;
+
+/* Create a context owning all device scratch for up to max_sources sources
+ * and max_targets separate targets (0 if only self-gravity is needed).
+ * Allocates device memory (synchronous).  *out is NULL on failure. */
+bh_status bh_create(bh_ctx **out, int64_t max_sources, int64_t max_targets,
+                    const bh_build_params *params);
+
+/* Build the tree over n sources, steps of [Tree] 实现步骤 in order:
+ * bounding box (确定粒子空间范围), Morton keys and their stable sort (粒子空间
+ * 排序, the gather index of [GASPHiA] 排序算法), the octree (构建树结构) and the
+ * centre of mass of every node ([GASPHiA] 计算节点质心).
+ *   src_pos_mass  device, n float4 rows (x, y, z, m), read only, 16-byte aligned.
+ * The sources are copied in sorted order; src_pos_mass is not needed after
+ * the stream passes this call.  n = 0 builds an empty tree. */
+bh_status bh_build(bh_ctx *ctx, const float *src_pos_mass, int64_t n, void *stream);
+
+/* Accelerations and potentials by the tree walk of [GASPHiA] 计算自引力 /
+ * 性能瓶颈分析: a node is used whole when (w/theta)^2 < r^2 (w the node's cell
+ * edge, r the distance from the target to its centre of mass), otherwise its
+ * children are visited; an opened leaf is summed particle by particle.
+ * Every interaction uses Plummer softening:
+ *   a += G m d / (|d|^2 + eps^2)^(3/2),  phi -= G m / (|d|^2 + eps^2)^(1/2),
+ * with d = x_source - x_target; a pair with |d|^2 + eps^2 = 0 adds nothing.
+ *   targets       NULL: the built sources are the targets and each excludes
+ *                 itself; else device, n_targets float4 rows (w ignored), at
+ *                 most max_targets ([SBH] 实验结果 evaluates separate queries).
+ *   out_acc_pot   device, n_targets float4 rows (ax, ay, az, phi) in the
+ *                 caller's order of the targets (for targets == NULL,
+ *                 n_targets must equal the n given to bh_build).
+ *   theta >= 0 (0 = exact direct sum), eps >= 0, G any finite value. */
+bh_status bh_gravity(bh_ctx *ctx, const float *targets, int64_t n_targets, float theta,
+                     float G, float eps, float *out_acc_pot, void *stream);
+
+/* Same as bh_gravity, and adds the number of interactions (accepted nodes plus
+ * particle pairs, self excluded) to *interactions (device, uint64) — slower,
+ * for measurement and tests. */
+bh_status bh_gravity_counted(bh_ctx *ctx, const float *targets, int64_t n_targets,
+                             float theta, float G, float eps, float *out_acc_pot,
+                             uint64_t *interactions, void *stream);
+
+/* Wait for the context's last stream and return the device status word
+ * (BH_OK, BH_ERR_NONFINITE or BH_ERR_CAPACITY).  Synchronous. */
+bh_status bh_sync(bh_ctx *ctx);
+
+/* Free the context (synchronous).  NULL is accepted. */
+bh_status bh_destroy(bh_ctx *ctx);
+
+/* Static text for a status code. */
+const char *bh_status_string(int status);
+
+/* ---- introspection, used by the parity tests ---------------------------- */
+
+/* Copy the Morton keys in sorted order and the sorted permutation (perm[i] =
+ * the caller's index of the i-th sorted source) of the last build into
+ * device buffers of n entries.  Either pointer may be NULL. */
+bh_status bh_get_keys(bh_ctx *ctx, uint64_t *keys_sorted, uint32_t *perm, void *stream);
+
+/* Number of nodes of the last build (synchronous: waits for the stream). */
+bh_status bh_get_node_count(bh_ctx *ctx, int64_t *n_nodes, void *stream);
+
+/* Copy the first n_nodes nodes (bh_node records) into a device buffer. */
+bh_status bh_get_nodes(bh_ctx *ctx, bh_node *nodes, int64_t n_nodes, void *stream);
+
+/* Root cube of the last build (synchronous): lo[3] = min corner, hi[3] = max
+ * corner of the sources, *L = the cube side (largest extent), all fp64. */
+bh_status bh_get_bbox(bh_ctx *ctx, double *lo, double *hi, double *L, void *stream);
+
+/* Per-phase device times of the last bh_build and bh_gravity in ms, when
+ * enabled with bh_set_profiling (events add a little overhead).
+ * ms[0] bbox + keys, ms[1] sort, ms[2] tree, ms[3] centre of mass,
+ * ms[4] walk (the last bh_gravity).  Synchronous. */
+bh_status bh_set_profiling(bh_ctx *ctx, int enable);
+bh_status bh_get_profile(bh_ctx *ctx, float *ms, int n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BH_H */
