@@ -30,7 +30,7 @@ struct bh_ctx {
     uint64_t *keys_sorted = nullptr;  // aliases keys or keys_alt after a build
     uint32_t *perm = nullptr;         // aliases vals or vals_alt after a build
     uint16_t *dc = nullptr;
-    uint32_t *blk_counts = nullptr, *blk_scan = nullptr;
+    uint32_t *blk_counts = nullptr, *blk_pref = nullptr, *blk_tot = nullptr;
     uint32_t *first_node = nullptr, *level_list = nullptr;
     Node *nodes = nullptr;
 
@@ -61,7 +61,8 @@ hipError_t dalloc(T **p, size_t count)
 void free_all(bh_ctx *c)
 {
     void *ptrs[] = {c->prm, c->bbox_part, c->keys, c->keys_alt, c->vals, c->vals_alt, c->spine,
-                    c->spos, c->dc, c->blk_counts, c->blk_scan, c->first_node, c->level_list,
+                    c->spos, c->dc, c->blk_counts, c->blk_pref, c->blk_tot, c->first_node,
+                    c->level_list,
                     c->nodes, c->tkeys, c->tkeys_alt, c->tvals, c->tvals_alt, c->tspine, c->tpos};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
@@ -138,13 +139,15 @@ bh_status bh_create(bh_ctx **out, int64_t max_sources, int64_t max_targets,
     ok &= dalloc(&c->vals, ns) == hipSuccess;
     ok &= dalloc(&c->vals_alt, ns) == hipSuccess;
     ok &= dalloc(&c->spine, sort_spine_entries((uint32_t)ns)) == hipSuccess;
-    ok &= dalloc(&c->spos, ns) == hipSuccess;
+    // the walk reads up to 7 sources past a leaf and one node record past the last
+    ok &= dalloc(&c->spos, ns + kSourcePad) == hipSuccess;
     ok &= dalloc(&c->dc, ns) == hipSuccess;
     ok &= dalloc(&c->blk_counts, kBuildCols * tiles) == hipSuccess;
-    ok &= dalloc(&c->blk_scan, kBuildCols * tiles + 1) == hipSuccess;
+    ok &= dalloc(&c->blk_pref, kBuildCols * tiles) == hipSuccess;
+    ok &= dalloc(&c->blk_tot, kBuildCols) == hipSuccess;
     ok &= dalloc(&c->first_node, ns + 1) == hipSuccess;
     ok &= dalloc(&c->level_list, (size_t)c->node_cap) == hipSuccess;
-    ok &= dalloc(&c->nodes, (size_t)c->node_cap) == hipSuccess;
+    ok &= dalloc(&c->nodes, (size_t)c->node_cap + 1) == hipSuccess;
     if (nt) {
         ok &= dalloc(&c->tkeys, nt) == hipSuccess;
         ok &= dalloc(&c->tkeys_alt, nt) == hipSuccess;
@@ -192,7 +195,8 @@ bh_status bh_build(bh_ctx *c, const float *src_pos_mass, int64_t n, void *stream
                    c->key_bits, c->spine, src, c->spos, s);
         record(c, 2, s);
         build_tree(c->keys_sorted, c->spos, un, c->bits, c->leaf_cap, c->node_cap, c->dc,
-                   c->blk_counts, c->blk_scan, c->first_node, c->level_list, c->nodes, c->prm, s);
+                   c->blk_counts, c->blk_pref, c->blk_tot, c->first_node, c->level_list,
+                   c->nodes, c->prm, s);
         record(c, 3, s);
         com_levels(c->keys_sorted, c->nodes, c->level_list, un, c->node_cap, c->bits, c->prm, s);
         record(c, 4, s);

@@ -10,6 +10,7 @@ namespace bh {
 
 constexpr int kMaxLevels = 22;      // levels 0..21 for 63-bit keys
 constexpr int kMaxLeafCap = 256;
+constexpr int kSourcePad = 8;       // readable slack after the sorted sources
 
 // Device status bits (a word in DevParams; 0 = fine).
 constexpr uint32_t kStatusNonFinite = 1u;
@@ -70,15 +71,17 @@ void radix_sort(uint64_t *keys, uint32_t *vals, uint64_t *keys_alt, uint32_t *va
                 uint64_t **keys_out, uint32_t **vals_out, uint32_t n, int key_bits,
                 uint32_t *spine, const float4 *gather_src, float4 *gather_dst, hipStream_t s);
 
-// generic single-workgroup exclusive scan: out[i] = sum(in[0..i)), out[n] = total
-void launch_scan_u32(const uint32_t *in, uint32_t *out, uint32_t n, hipStream_t s);
+// Exclusive scan of each row of a [rows][len] table, one workgroup per row:
+// pref[r][t] = sum(in[r][0..t)), tot[r] = row total.
+void launch_scan_rows(const uint32_t *in, uint32_t *pref, uint32_t *tot, uint32_t rows,
+                      uint32_t len, hipStream_t s);
 
 // build.hip
 uint32_t build_blocks(uint32_t n);
 void build_tree(const uint64_t *keys_sorted, const float4 *spos, uint32_t n, int bits,
                 int leaf_cap, uint64_t node_capacity, uint16_t *dc, uint32_t *block_counts,
-                uint32_t *block_scan, uint32_t *first_node, uint32_t *level_list, Node *nodes,
-                DevParams *prm, hipStream_t s);
+                uint32_t *block_pref, uint32_t *block_tot, uint32_t *first_node,
+                uint32_t *level_list, Node *nodes, DevParams *prm, hipStream_t s);
 void com_levels(const uint64_t *keys_sorted, Node *nodes, const uint32_t *level_list,
                 uint32_t n, uint64_t node_capacity, int bits, DevParams *prm, hipStream_t s);
 

@@ -20,8 +20,8 @@
 // of them, ancestors first.  So the pre-order index of node (a, l) is
 // sum_{a'<a} c(a') + l - d(a) - 1, one prefix sum over positions.
 //
-// Kernels: count (d, c, per-tile totals per column) -> one exclusive scan over
-// the [column][tile] table -> emit (node start/level, level lists, index of
+// Kernels: count (d, c, per-tile totals per column) -> a scan of each column
+// over the tiles -> emit (node start/level, level lists, index of
 // the first node at each position) -> ranges (cell end by galloping search,
 // skip = first node at the end, leaf centres of mass).  The centre of mass of
 // internal nodes ([GASPHiA] 计算节点质心) is then combined level by level from
@@ -109,8 +109,11 @@ __device__ inline uint32_t wave_incl_scan(uint32_t v)
     return v;
 }
 
+// pref[c][t] / tot[c]: per-column scan over tiles of the k_count table
+// (column 0: nodes, column 1 + l: nodes of level l).
 __global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restrict__ dc, uint32_t n,
-                                                        const uint32_t *__restrict__ scan,
+                                                        const uint32_t *__restrict__ pref,
+                                                        const uint32_t *__restrict__ tot,
                                                         uint32_t n_tiles, uint64_t cap,
                                                         uint32_t *__restrict__ first_node,
                                                         uint32_t *__restrict__ level_list,
@@ -120,9 +123,17 @@ __global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restri
     constexpr int per = kBuildTile / kBuildThreads;  // consecutive positions per thread
     __shared__ uint32_t wtot[kBuildThreads / 64];
     __shared__ uint32_t lrank[kBuildCols];
+    __shared__ uint32_t lbase[kBuildCols];   // this tile's first slot in each level list
     const uint32_t blk = blockIdx.x;
-    const uint32_t total = scan[n_tiles];            // all nodes
+    const uint32_t total = tot[0];           // all nodes
     if (threadIdx.x < kBuildCols) lrank[threadIdx.x] = 0;
+    if (threadIdx.x == 0) {
+        uint32_t off = 0;
+        for (int l = 0; l < kMaxLevels; ++l) {
+            lbase[1 + l] = off + pref[(1 + l) * n_tiles + blk];
+            off += tot[1 + l];
+        }
+    }
 
     const int64_t a0 = (int64_t)blk * kBuildTile + per * threadIdx.x;
     int dd[per], cc[per];
@@ -138,7 +149,7 @@ __global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restri
     const uint32_t incl = wave_incl_scan(s);
     if (lane == 63) wtot[wave] = incl;
     __syncthreads();
-    uint32_t run = scan[blk];
+    uint32_t run = pref[blk];
     for (uint32_t w = 0; w < wave; ++w) run += wtot[w];
     run += incl - s;
 
@@ -150,7 +161,7 @@ __global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restri
             const int l = dd[k] + 1 + j;
             const uint32_t X = run + j;
             const uint32_t r = atomicAdd(&lrank[1 + l], 1u);
-            const uint32_t pos = scan[(1 + l) * n_tiles + blk] - total + r;
+            const uint32_t pos = lbase[1 + l] + r;
             if (X < cap) {
                 nodes[X].start = (uint32_t)a;
                 nodes[X].meta = (uint32_t)l | (j == cc[k] - 1 ? kLeafBit : 0u);
@@ -163,11 +174,13 @@ __global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restri
     if (blk == 0 && threadIdx.x == 0) {
         prm->n_nodes = total;
         if (total > cap) prm->status |= kStatusCapacity;
+        uint32_t off = 0;
         for (int l = 0; l < kMaxLevels; ++l) {
-            prm->level_offset[l] = scan[(1 + l) * n_tiles] - total;
-            prm->level_count[l] = scan[(2 + l) * n_tiles] - scan[(1 + l) * n_tiles];
+            prm->level_offset[l] = off;
+            prm->level_count[l] = tot[1 + l];
+            off += tot[1 + l];
         }
-        prm->level_offset[kMaxLevels] = scan[(1 + kMaxLevels) * n_tiles] - total;
+        prm->level_offset[kMaxLevels] = off;
     }
 }
 
@@ -298,14 +311,15 @@ uint32_t build_blocks(uint32_t n)
 
 void build_tree(const uint64_t *keys_sorted, const float4 *spos, uint32_t n, int bits,
                 int leaf_cap, uint64_t node_capacity, uint16_t *dc, uint32_t *block_counts,
-                uint32_t *block_scan, uint32_t *first_node, uint32_t *level_list, Node *nodes,
-                DevParams *prm, hipStream_t s)
+                uint32_t *block_pref, uint32_t *block_tot, uint32_t *first_node,
+                uint32_t *level_list, Node *nodes, DevParams *prm, hipStream_t s)
 {
     const uint32_t tiles = build_blocks(n);
     hipLaunchKernelGGL(k_count, dim3(tiles), dim3(kBuildThreads), 0, s, keys_sorted, n, bits,
                        leaf_cap, dc, block_counts, tiles);
-    launch_scan_u32(block_counts, block_scan, kBuildCols * tiles, s);
-    hipLaunchKernelGGL(k_emit, dim3(tiles), dim3(kBuildThreads), 0, s, dc, n, block_scan, tiles,
+    launch_scan_rows(block_counts, block_pref, block_tot, kBuildCols, tiles, s);
+    hipLaunchKernelGGL(k_emit, dim3(tiles), dim3(kBuildThreads), 0, s, dc, n,
+                       (const uint32_t *)block_pref, (const uint32_t *)block_tot, tiles,
                        node_capacity, first_node, level_list, nodes, prm);
     hipLaunchKernelGGL(k_ranges, dim3(grid_for(n, 2048)), dim3(256), 0, s, keys_sorted, spos, n,
                        bits, node_capacity, first_node, nodes, (const DevParams *)prm);

@@ -6,11 +6,12 @@
 // index as payload and its last pass also gathers a sorted copy of the
 // float4 rows, so the walk reads contiguous memory.
 //
-// Per pass three kernels: a per-tile digit histogram, one exclusive scan over
-// the digit-major [digit][tile] table (global offsets), and a scatter in
-// which each workgroup ranks its tile stably in LDS (64-lane ballots give the
-// rank among equal digits within a wave row) and writes the tile out
-// digit-group by digit-group, so writes of one digit are contiguous.
+// Per pass three kernels: a per-tile digit histogram, a scan of each digit's
+// row of tile counts (one workgroup per digit), and a scatter in which each
+// workgroup ranks its tile stably in LDS (64-lane ballots give the rank among
+// equal digits within a wave row), adds the digit bases (a scan of the 256
+// digit totals) and writes the tile out digit-group by digit-group, so
+// writes of one digit are contiguous.
 #include "bh_internal.h"
 
 namespace bh {
@@ -73,13 +74,14 @@ template <bool GATHER>
 __global__ __launch_bounds__(kSortThreads) void k_scatter(
     const uint64_t *__restrict__ kin, const uint32_t *__restrict__ vin,
     uint64_t *__restrict__ kout, uint32_t *__restrict__ vout, uint32_t n, int shift,
-    const uint32_t *__restrict__ offsets, uint32_t n_tiles, const float4 *__restrict__ gsrc,
-    float4 *__restrict__ gdst)
+    const uint32_t *__restrict__ row_pref, const uint32_t *__restrict__ row_tot,
+    uint32_t n_tiles, const float4 *__restrict__ gsrc, float4 *__restrict__ gdst)
 {
     __shared__ uint64_t skey[kSortTile];
     __shared__ uint32_t sval[kSortTile];
     __shared__ uint32_t wcnt[kWaves][kRadix];
     __shared__ uint32_t bstart[kRadix];
+    __shared__ uint32_t gbase[kRadix];
     __shared__ uint32_t tmp[kWaves];
 
     const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
@@ -131,6 +133,10 @@ __global__ __launch_bounds__(kSortThreads) void k_scatter(
         uint32_t total;
         const uint32_t start = block_excl_scan_256(run, tmp, &total);
         bstart[d] = start;
+        // global start of digit d for this tile: all smaller digits, plus
+        // digit d in earlier tiles
+        const uint32_t digit_base = block_excl_scan_256(row_tot[d], tmp, &total);
+        gbase[d] = digit_base + row_pref[d * n_tiles + blockIdx.x];
     }
     __syncthreads();
 
@@ -155,7 +161,7 @@ __global__ __launch_bounds__(kSortThreads) void k_scatter(
             const uint64_t kk = skey[j];
             const uint32_t vv = sval[j];
             const uint32_t digit = (uint32_t)(kk >> shift) & 0xffu;
-            const uint32_t g = offsets[digit * n_tiles + blockIdx.x] + (j - bstart[digit]);
+            const uint32_t g = gbase[digit] + (j - bstart[digit]);
             kout[g] = kk;
             vout[g] = vv;
             if (GATHER) gdst[g] = gsrc[vv];
@@ -163,35 +169,28 @@ __global__ __launch_bounds__(kSortThreads) void k_scatter(
     }
 }
 
-constexpr int kScanThreads = 1024;
+constexpr int kScanThreads = 256;
 
-// Exclusive scan of n entries by one workgroup: each thread sums a contiguous
-// chunk, the 1024 sums are scanned, then each chunk is rescanned and written.
-__global__ __launch_bounds__(kScanThreads) void k_scan(const uint32_t *__restrict__ in,
-                                                       uint32_t *__restrict__ out, uint32_t n)
+// Exclusive scan of each row of a [rows][len] table, one workgroup per row:
+// pref[r][t] = sum(in[r][0..t)), tot[r] = sum(in[r][0..len)).  Coalesced
+// rounds of 256 entries carry the running sum.
+__global__ __launch_bounds__(kScanThreads) void k_scan_rows(const uint32_t *__restrict__ in,
+                                                            uint32_t *__restrict__ pref,
+                                                            uint32_t *__restrict__ tot,
+                                                            uint32_t len)
 {
     __shared__ uint32_t tmp[kScanThreads / 64];
-    const uint32_t chunk = (n + kScanThreads - 1) / kScanThreads;
-    const uint32_t b = min(n, threadIdx.x * chunk), e = min(n, b + chunk);
-    uint32_t s = 0;
-    for (uint32_t i = b; i < e; ++i) s += in[i];
-    const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
-    const uint32_t incl = wave_incl_scan(s);
-    if (lane == 63) tmp[wave] = incl;
-    __syncthreads();
-    uint32_t off = 0, total = 0;
-    for (int w = 0; w < kScanThreads / 64; ++w) {
-        uint32_t t = tmp[w];
-        if ((uint32_t)w < wave) off += t;
-        total += t;
+    const size_t row = (size_t)blockIdx.x * len;
+    uint32_t carry = 0;
+    for (uint32_t b = 0; b < len; b += kScanThreads) {
+        const uint32_t t = b + threadIdx.x;
+        const uint32_t v = t < len ? in[row + t] : 0u;
+        uint32_t total;
+        const uint32_t ex = block_excl_scan_256(v, tmp, &total);
+        if (t < len) pref[row + t] = carry + ex;
+        carry += total;
     }
-    uint32_t run = off + incl - s;
-    for (uint32_t i = b; i < e; ++i) {
-        uint32_t v = in[i];
-        out[i] = run;
-        run += v;
-    }
-    if (threadIdx.x == 0) out[n] = total;
+    if (threadIdx.x == 0) tot[blockIdx.x] = carry;
 }
 
 }  // namespace
@@ -200,12 +199,13 @@ size_t sort_spine_entries(uint32_t n)
 {
     size_t tiles = (n + kSortTile - 1) / kSortTile;
     if (tiles == 0) tiles = 1;
-    return 2 * (size_t)kRadix * tiles + 1;
+    return 2 * (size_t)kRadix * tiles + kRadix;
 }
 
-void launch_scan_u32(const uint32_t *in, uint32_t *out, uint32_t n, hipStream_t s)
+void launch_scan_rows(const uint32_t *in, uint32_t *pref, uint32_t *tot, uint32_t rows,
+                      uint32_t len, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, s, in, out, n);
+    hipLaunchKernelGGL(k_scan_rows, dim3(rows), dim3(kScanThreads), 0, s, in, pref, tot, len);
 }
 
 void radix_sort(uint64_t *keys, uint32_t *vals, uint64_t *keys_alt, uint32_t *vals_alt,
@@ -216,20 +216,20 @@ void radix_sort(uint64_t *keys, uint32_t *vals, uint64_t *keys_alt, uint32_t *va
     uint32_t *va = vals, *vb = vals_alt;
     const uint32_t tiles = (n + kSortTile - 1) / kSortTile;
     const uint32_t entries = kRadix * tiles;
-    uint32_t *hist = spine, *offs = spine + entries;
+    uint32_t *hist = spine, *pref = spine + entries, *tot = spine + 2 * entries;
     const int passes = (key_bits + 7) / 8;
     for (int p = 0; p < passes && n > 0; ++p) {
         const int shift = 8 * p;
         const bool last = (p == passes - 1);
         hipLaunchKernelGGL(k_hist, dim3(tiles), dim3(kSortThreads), 0, s, ka, n, shift, hist,
                            tiles);
-        launch_scan_u32(hist, offs, entries, s);
+        launch_scan_rows(hist, pref, tot, kRadix, tiles, s);
         if (last && gather_src) {
             hipLaunchKernelGGL(k_scatter<true>, dim3(tiles), dim3(kSortThreads), 0, s, ka, va, kb,
-                               vb, n, shift, offs, tiles, gather_src, gather_dst);
+                               vb, n, shift, pref, tot, tiles, gather_src, gather_dst);
         } else {
             hipLaunchKernelGGL(k_scatter<false>, dim3(tiles), dim3(kSortThreads), 0, s, ka, va,
-                               kb, vb, n, shift, offs, tiles, (const float4 *)nullptr,
+                               kb, vb, n, shift, pref, tot, tiles, (const float4 *)nullptr,
                                (float4 *)nullptr);
         }
         uint64_t *tk = ka; ka = kb; kb = tk;

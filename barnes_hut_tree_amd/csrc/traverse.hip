@@ -51,6 +51,105 @@ __device__ inline void pair(float4 s, float px, float py, float pz, float eps2, 
     pot -= mi;
 }
 
+// Direct sum over the sources [b, e) of an opened leaf, eight at a time (one
+// batch of scalar loads per eight).  MINE: the leaf may hold this lane's own
+// particle i, whose mass is masked out.
+template <bool SOFT, bool MINE>
+__device__ __attribute__((always_inline)) inline void leaf_tile(
+    const float4 *__restrict__ src, uint32_t b, uint32_t e, uint32_t i, float4 p, float eps2,
+    float &ax, float &ay, float &az, float &pot)
+{
+    for (uint32_t j = b; j < e; j += 8) {
+        const float4 *q = src + j;
+        float4 s[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) s[k] = q[k];
+        asm volatile("" ::: "memory");   // issue all eight loads first
+        const uint32_t left = e - j;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if ((uint32_t)k < left) {
+                if (MINE) s[k].w = (j + k == i) ? 0.f : s[k].w;
+                pair<SOFT>(s[k], p.x, p.y, p.z, eps2, ax, ay, az, pot);
+            }
+        }
+    }
+}
+
+__device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Walk of one wave (see the file comment).  EXACT_T selects ldexp for the
+// level thresholds (w_l / theta)^2 = T0 * 4^-l; otherwise 4^-l is an exponent
+// decrement on the scalar unit (exact whenever T0 * 4^-21 stays normal, and
+// for T0 = 0, inf or NaN with a zero step).
+//
+// The loop is bound by instruction issue (vector and scalar units both issue
+// about one wave instruction per cycle per CU), so it is written to keep both
+// streams short: node fields stay in scalar registers and feed the vector
+// ops directly, the node address is a 32-bit byte offset, and the lane masks
+// come straight from the comparisons.  The one scalar load per node is not
+// prefetched; the other waves on the SIMD cover its latency.
+template <bool SOFT, bool SELF, bool COUNT, bool EXACT_T>
+__device__ __attribute__((always_inline)) inline void walk_wave(
+    const Node *__restrict__ nodes, const float4 *__restrict__ src, uint32_t nn, float4 p,
+    uint32_t i, uint32_t wave_base, bool valid, float T0, uint32_t T0_bits, uint32_t T_step,
+    float eps2, float &ax, float &ay, float &az, float &pot, uint32_t &n_int)
+{
+    const char *node_bytes = reinterpret_cast<const char *>(nodes);
+    uint32_t cur = valid ? 0u : 0xffffffffu;
+    uint32_t X = 0;
+    while (X < nn) {
+        const uint4 *rec = reinterpret_cast<const uint4 *>(node_bytes + X * (uint32_t)sizeof(Node));
+        const uint4 lo = rec[0], hi = rec[1];
+        const float cx = __uint_as_float(lo.x), cy = __uint_as_float(lo.y);
+        uint32_t mbits = lo.w;
+        asm volatile("" : "+s"(mbits));   // keep the mass in a register, not reloaded
+        const float cz = __uint_as_float(lo.z), m = __uint_as_float(mbits);
+        const uint32_t skip = hi.z, meta = hi.w;
+        const uint32_t level = node_level(meta);
+        const float T = EXACT_T ? ldexpf(T0, -2 * (int)level)
+                                : __uint_as_float(sgpr(T0_bits - level * T_step));
+        const float dx = cx - p.x, dy = cy - p.y, dz = cz - p.z;
+        const float r2 = fmaf(dz, dz, fmaf(dy, dy, dx * dx));
+        const bool active = cur == X;
+        const bool far = T < r2;
+        const uint64_t act_m = __ballot(active);
+        const uint64_t far_m = __ballot(far);
+        const uint64_t open_m = act_m & ~far_m;
+        // Cursor: lanes that use X whole move to skip(X), lanes that open it
+        // to X + 1 (its first child; for a leaf skip == X + 1 as well).
+        // Written as increments so both stay single vector ops.
+        if (active && far) {
+            const float inv = __builtin_amdgcn_rsqf(r2 + eps2);
+            const float mi = m * inv;
+            const float f = mi * inv * inv;
+            ax = fmaf(f, dx, ax);
+            ay = fmaf(f, dy, ay);
+            az = fmaf(f, dz, az);
+            pot -= mi;
+            cur += skip - X - 1;
+            if (COUNT) ++n_int;
+        }
+        cur += (uint32_t)active;
+        const uint64_t leaf_open_m = (meta & kLeafBit) ? open_m : 0ull;
+        if (leaf_open_m != 0) {
+            const uint32_t b = hi.x, e = hi.x + hi.y;
+            // a leaf holding some of this wave's own targets needs the self
+            // pair removed; others take the plain loop
+            const bool mine = SELF && b < wave_base + 64 && e > wave_base;
+            if (active && !far) {
+                if (mine)
+                    leaf_tile<SOFT, true>(src, b, e, i, p, eps2, ax, ay, az, pot);
+                else
+                    leaf_tile<SOFT, false>(src, b, e, i, p, eps2, ax, ay, az, pot);
+                if (COUNT) n_int += (e - b) - ((SELF && i >= b && i < e) ? 1u : 0u);
+            }
+        }
+        // the wave descends if any lane opened X (for a leaf, skip == X + 1)
+        X = open_m != 0 ? X + 1 : skip;
+    }
+}
+
 template <bool SOFT, bool SELF, bool COUNT>
 __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ nodes,
                                                        const float4 *__restrict__ src,
@@ -76,63 +175,24 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
     const float4 p = valid ? tpos[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     const double L = prm->L;
     const float T0 = (float)(L * L / ((double)theta * (double)theta));
+    const uint32_t T0_bits = sgpr(__float_as_uint(T0));
+    const uint32_t T0_exp = (T0_bits >> 23) & 0xffu;
+    // zero, inf and NaN thresholds are the same at every level (step 0); a
+    // normal T0 with T0 * 4^-21 normal steps the exponent by 2 per level;
+    // anything else takes ldexp
+    const bool fixed = (T0_bits & 0x7fffffffu) == 0u || T0_exp == 255u;
+    const bool exact = !fixed && T0_exp <= 44u;
+    const uint32_t T_step = fixed ? 0u : (1u << 24);
 
-    uint32_t cur = valid ? 0u : 0xffffffffu;
     float ax = 0.f, ay = 0.f, az = 0.f, pot = 0.f;
     uint32_t n_int = 0;
+    if (exact)
+        walk_wave<SOFT, SELF, COUNT, true>(nodes, src, nn, p, i, wave_base, valid, T0, T0_bits,
+                                           T_step, eps2, ax, ay, az, pot, n_int);
+    else
+        walk_wave<SOFT, SELF, COUNT, false>(nodes, src, nn, p, i, wave_base, valid, T0, T0_bits,
+                                            T_step, eps2, ax, ay, az, pot, n_int);
 
-    uint32_t X = 0;
-    while (X < nn) {
-        X = __builtin_amdgcn_readfirstlane(X);
-        const Node nd = nodes[X];
-        const uint32_t level = node_level(nd.meta);
-        const bool leaf = (nd.meta & kLeafBit) != 0;
-        const float T = ldexpf(T0, -2 * (int)level);
-        const float dx = nd.cx - p.x, dy = nd.cy - p.y, dz = nd.cz - p.z;
-        const float r2 = fmaf(dz, dz, fmaf(dy, dy, dx * dx));
-        const bool active = cur == X;
-        const bool acc = active && (T < r2);
-        const bool open = active && !acc;
-        if (acc) {
-            const float r2s = r2 + eps2;
-            const float inv = __builtin_amdgcn_rsqf(r2s);
-            const float mi = nd.m * inv;
-            const float f = mi * inv * inv;
-            ax = fmaf(f, dx, ax);
-            ay = fmaf(f, dy, ay);
-            az = fmaf(f, dz, az);
-            pot -= mi;
-            if (COUNT) ++n_int;
-        }
-        const uint64_t omask = __ballot(open);
-        if (leaf) {
-            if (omask != 0) {
-                const uint32_t b = nd.start, e = nd.start + nd.count;
-                // a leaf holding some of this wave's own targets needs the
-                // self pair removed; others take the plain loop
-                const bool mine = SELF && b < wave_base + 64 && e > wave_base;
-                if (open) {
-                    if (mine) {
-                        for (uint32_t j = b; j < e; ++j) {
-                            float4 s = src[j];
-                            s.w = (j == i) ? 0.f : s.w;
-                            pair<SOFT>(s, p.x, p.y, p.z, eps2, ax, ay, az, pot);
-                        }
-                    } else {
-                        for (uint32_t j = b; j < e; ++j)
-                            pair<SOFT>(src[j], p.x, p.y, p.z, eps2, ax, ay, az, pot);
-                    }
-                    if (COUNT) n_int += (e - b) - ((SELF && i >= b && i < e) ? 1u : 0u);
-                }
-            }
-            if (active) cur = nd.skip;
-            X = nd.skip;
-        } else {
-            if (acc) cur = nd.skip;
-            if (open) cur = X + 1;
-            X = omask ? X + 1 : nd.skip;
-        }
-    }
     if (valid) out[tperm[i]] = make_float4(G * ax, G * ay, G * az, G * pot);
     if (COUNT) {
         unsigned long long c = n_int;
