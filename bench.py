@@ -116,6 +116,9 @@ def main():
     ap.add_argument("--key-bits", type=int, default=63)
     ap.add_argument("--theta", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device-to-device copy of this many MiB (3 times), "
+                         "the reference kernel for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the walk has no multi-GPU path in this build "
@@ -127,6 +130,18 @@ def main():
     import barnes_hut_tree_amd as bh
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+
+    if args.copy_calibration_mib:
+        nbytes = args.copy_calibration_mib << 20
+        a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": nbytes, "copy_calibration_bytes_written":
+                          nbytes, "copies": 3}), file=sys.stderr, flush=True)
+        del a, b
 
     p, prm, wname = make_workload(args.workload)
     if args.theta is not None:
