@@ -4,21 +4,22 @@
 // One wavefront walks the tree for 64 consecutive sorted targets.  The node it
 // visits is wave-uniform, so node records come through scalar loads and are
 // broadcast to all lanes for free.  The walk is stackless: nodes sit in
-// pre-order, a subtree spans [node, skip), and each lane keeps a cursor, the
-// next node it must see (initially the root).  At node X the lanes whose
-// cursor equals X apply the opening test of the pages, (w/theta)^2 < r^2 with
-// w the cell edge and r the distance to the centre of mass.  Lanes that pass
-// add one monopole term and move their cursor to skip(X).  The others open X;
+// pre-order, a subtree spans [node, skip), and each lane keeps a rejoin index,
+// the next node it must see (initially the root).  At node X the lanes with
+// rejoin <= X apply the opening test of the pages, (w/theta)^2 < r^2 with w
+// the cell edge and r the distance to the centre of mass.  Lanes that pass
+// add one monopole term and set rejoin = skip(X).  The others open X;
 // a 64-lane ballot of them decides the wave's next node: X + 1 (the first
 // child) if any lane opened an internal node, else skip(X).  An opened leaf
 // is summed particle by particle by the lanes that opened it.
 //
-// A lane that accepted an ancestor of the current node holds a cursor at that
+// A lane that accepted an ancestor of the current node waits for that
 // ancestor's skip, which is at or beyond skip(X); the wave reaches it exactly
 // when it leaves that subtree.  So every lane sees exactly the nodes its own
 // particle-by-particle walk would visit (the pages' warp vote instead makes
 // all lanes descend when any lane must; here the ballot only decides where
-// the wave goes, and the per-lane cursor keeps each lane's result its own).
+// the wave goes, and the per-lane rejoin index keeps each lane's result its
+// own).
 #include "bh_internal.h"
 
 namespace bh {
@@ -96,14 +97,18 @@ __device__ __attribute__((always_inline)) inline void walk_wave(
     float eps2, float &ax, float &ay, float &az, float &pot, uint32_t &n_int)
 {
     const char *node_bytes = reinterpret_cast<const char *>(nodes);
-    uint32_t cur = valid ? 0u : 0xffffffffu;
+    // Lane state: a lane takes part at node X when rejoin <= X.  A lane that
+    // uses a node whole sets rejoin = skip(node) and so sits out the node's
+    // subtree; lanes that open a node keep theirs.  (The wave lands on every
+    // such skip on its way out, so `<=` and `==` select the same lanes.)
+    uint32_t rejoin = valid ? 0u : 0xffffffffu;
     uint32_t X = 0;
     while (X < nn) {
         const uint4 *rec = reinterpret_cast<const uint4 *>(node_bytes + X * (uint32_t)sizeof(Node));
         const uint4 lo = rec[0], hi = rec[1];
-        const float cx = __uint_as_float(lo.x), cy = __uint_as_float(lo.y);
         uint32_t mbits = lo.w;
         asm volatile("" : "+s"(mbits));   // keep the mass in a register, not reloaded
+        const float cx = __uint_as_float(lo.x), cy = __uint_as_float(lo.y);
         const float cz = __uint_as_float(lo.z), m = __uint_as_float(mbits);
         const uint32_t skip = hi.z, meta = hi.w;
         const uint32_t level = node_level(meta);
@@ -111,15 +116,12 @@ __device__ __attribute__((always_inline)) inline void walk_wave(
                                 : __uint_as_float(sgpr(T0_bits - level * T_step));
         const float dx = cx - p.x, dy = cy - p.y, dz = cz - p.z;
         const float r2 = fmaf(dz, dz, fmaf(dy, dy, dx * dx));
-        const bool active = cur == X;
-        const bool far = T < r2;
-        const uint64_t act_m = __ballot(active);
-        const uint64_t far_m = __ballot(far);
+        // lane masks straight from the two compares
+        const uint64_t act_m = __ballot(rejoin <= X);
+        const uint64_t far_m = __ballot(T < r2);
         const uint64_t open_m = act_m & ~far_m;
-        // Cursor: lanes that use X whole move to skip(X), lanes that open it
-        // to X + 1 (its first child; for a leaf skip == X + 1 as well).
-        // Written as increments so both stay single vector ops.
-        if (active && far) {
+        const uint32_t rejoin_before = rejoin;
+        if (rejoin <= X && T < r2) {
             const float inv = __builtin_amdgcn_rsqf(r2 + eps2);
             const float mi = m * inv;
             const float f = mi * inv * inv;
@@ -127,26 +129,27 @@ __device__ __attribute__((always_inline)) inline void walk_wave(
             ay = fmaf(f, dy, ay);
             az = fmaf(f, dz, az);
             pot -= mi;
-            cur += skip - X - 1;
+            rejoin = skip;
             if (COUNT) ++n_int;
         }
-        cur += (uint32_t)active;
-        const uint64_t leaf_open_m = (meta & kLeafBit) ? open_m : 0ull;
-        if (leaf_open_m != 0) {
-            const uint32_t b = hi.x, e = hi.x + hi.y;
-            // a leaf holding some of this wave's own targets needs the self
-            // pair removed; others take the plain loop
-            const bool mine = SELF && b < wave_base + 64 && e > wave_base;
-            if (active && !far) {
-                if (mine)
-                    leaf_tile<SOFT, true>(src, b, e, i, p, eps2, ax, ay, az, pot);
-                else
-                    leaf_tile<SOFT, false>(src, b, e, i, p, eps2, ax, ay, az, pot);
-                if (COUNT) n_int += (e - b) - ((SELF && i >= b && i < e) ? 1u : 0u);
-            }
+        if (open_m == 0) {   // every active lane used X whole
+            X = skip;
+            continue;
         }
-        // the wave descends if any lane opened X (for a leaf, skip == X + 1)
-        X = open_m != 0 ? X + 1 : skip;
+        const bool leaf = (meta & kLeafBit) != 0;
+        if (leaf && rejoin_before <= X && !(T < r2)) {
+            // lanes that opened a leaf sum its particles; a leaf holding some
+            // of this wave's own targets needs the self pair removed
+            const uint32_t b = hi.x, e = hi.x + hi.y;
+            if (SELF && b < wave_base + 64 && e > wave_base)
+                leaf_tile<SOFT, true>(src, b, e, i, p, eps2, ax, ay, az, pot);
+            else
+                leaf_tile<SOFT, false>(src, b, e, i, p, eps2, ax, ay, az, pot);
+            if (COUNT) n_int += (e - b) - ((SELF && i >= b && i < e) ? 1u : 0u);
+        }
+        // descend into an opened internal node; leave an opened leaf
+        // (for a leaf, skip == X + 1)
+        X = leaf ? skip : X + 1;
     }
 }
 
