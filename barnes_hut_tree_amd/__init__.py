@@ -211,9 +211,9 @@ class BarnesHut:
         _check(load_library().bh_set_profiling(self._h, int(bool(on))), "bh_set_profiling")
 
     def profile(self):
-        """Device ms of [bbox+keys, sort, tree, centre of mass, walk]."""
-        ms = (ctypes.c_float * 5)()
-        _check(load_library().bh_get_profile(self._h, ms, 5), "bh_get_profile")
+        """Device ms of [bbox+keys, sort, tree with centres of mass, walk]."""
+        ms = (ctypes.c_float * 4)()
+        _check(load_library().bh_get_profile(self._h, ms, 4), "bh_get_profile")
         return list(ms)
 
 

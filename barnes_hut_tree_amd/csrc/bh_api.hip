@@ -29,9 +29,7 @@ struct bh_ctx {
     float4 *spos = nullptr;
     uint64_t *keys_sorted = nullptr;  // aliases keys or keys_alt after a build
     uint32_t *perm = nullptr;         // aliases vals or vals_alt after a build
-    uint16_t *dc = nullptr;
-    uint32_t *blk_counts = nullptr, *blk_pref = nullptr, *blk_tot = nullptr;
-    uint32_t *first_node = nullptr, *level_list = nullptr;
+    BuildScratch bw = {};
     Node *nodes = nullptr;
 
     uint64_t *tkeys = nullptr, *tkeys_alt = nullptr;
@@ -61,9 +59,9 @@ hipError_t dalloc(T **p, size_t count)
 void free_all(bh_ctx *c)
 {
     void *ptrs[] = {c->prm, c->bbox_part, c->keys, c->keys_alt, c->vals, c->vals_alt, c->spine,
-                    c->spos, c->dc, c->blk_counts, c->blk_pref, c->blk_tot, c->first_node,
-                    c->level_list,
-                    c->nodes, c->tkeys, c->tkeys_alt, c->tvals, c->tvals_alt, c->tspine, c->tpos};
+                    c->spos, c->bw.dc, c->bw.tile_counts, c->bw.tile_sums, c->bw.tile_scan,
+                    c->bw.first_node, c->bw.P, c->nodes, c->tkeys, c->tkeys_alt, c->tvals,
+                    c->tvals_alt, c->tspine, c->tpos};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
     if (c->host_prm) (void)hipHostFree(c->host_prm);
@@ -141,12 +139,12 @@ bh_status bh_create(bh_ctx **out, int64_t max_sources, int64_t max_targets,
     ok &= dalloc(&c->spine, sort_spine_entries((uint32_t)ns)) == hipSuccess;
     // the walk reads up to 7 sources past a leaf and one node record past the last
     ok &= dalloc(&c->spos, ns + kSourcePad) == hipSuccess;
-    ok &= dalloc(&c->dc, ns) == hipSuccess;
-    ok &= dalloc(&c->blk_counts, kBuildCols * tiles) == hipSuccess;
-    ok &= dalloc(&c->blk_pref, kBuildCols * tiles) == hipSuccess;
-    ok &= dalloc(&c->blk_tot, kBuildCols) == hipSuccess;
-    ok &= dalloc(&c->first_node, ns + 1) == hipSuccess;
-    ok &= dalloc(&c->level_list, (size_t)c->node_cap) == hipSuccess;
+    ok &= dalloc(&c->bw.dc, ns) == hipSuccess;
+    ok &= dalloc(&c->bw.tile_counts, tiles) == hipSuccess;
+    ok &= dalloc(&c->bw.tile_sums, tiles) == hipSuccess;
+    ok &= dalloc(&c->bw.tile_scan, tiles + 1) == hipSuccess;
+    ok &= dalloc(&c->bw.first_node, ns + 1) == hipSuccess;
+    ok &= dalloc(&c->bw.P, ns + 1) == hipSuccess;
     ok &= dalloc(&c->nodes, (size_t)c->node_cap + 1) == hipSuccess;
     if (nt) {
         ok &= dalloc(&c->tkeys, nt) == hipSuccess;
@@ -194,14 +192,11 @@ bh_status bh_build(bh_ctx *c, const float *src_pos_mass, int64_t n, void *stream
         radix_sort(c->keys, c->vals, c->keys_alt, c->vals_alt, &c->keys_sorted, &c->perm, un,
                    c->key_bits, c->spine, src, c->spos, s);
         record(c, 2, s);
-        build_tree(c->keys_sorted, c->spos, un, c->bits, c->leaf_cap, c->node_cap, c->dc,
-                   c->blk_counts, c->blk_pref, c->blk_tot, c->first_node, c->level_list,
+        build_tree(c->keys_sorted, c->spos, un, c->bits, c->leaf_cap, c->node_cap, c->bw,
                    c->nodes, c->prm, s);
         record(c, 3, s);
-        com_levels(c->keys_sorted, c->nodes, c->level_list, un, c->node_cap, c->bits, c->prm, s);
-        record(c, 4, s);
     } else {
-        for (int k = 1; k <= 4; ++k) record(c, k, s);
+        for (int k = 1; k <= 3; ++k) record(c, k, s);
     }
     bh_status st = launch_status();
     if (st != BH_OK) return st;
@@ -365,8 +360,8 @@ bh_status bh_get_profile(bh_ctx *c, float *ms, int n)
 {
     if (!c || !ms || n < 0) return BH_ERR_INVALID;
     if (!c->prof) return BH_ERR_INVALID;
-    const int pairs[5][2] = {{0, 1}, {1, 2}, {2, 3}, {3, 4}, {5, 6}};
-    for (int k = 0; k < n && k < 5; ++k) {
+    const int pairs[4][2] = {{0, 1}, {1, 2}, {2, 3}, {5, 6}};
+    for (int k = 0; k < n && k < 4; ++k) {
         if (hipEventSynchronize(c->ev[pairs[k][1]]) != hipSuccess) return BH_ERR_HIP;
         float t = 0.f;
         if (hipEventElapsedTime(&t, c->ev[pairs[k][0]], c->ev[pairs[k][1]]) != hipSuccess)

@@ -27,8 +27,19 @@ struct DevParams {
     uint32_t n_nodes;    // nodes emitted by the build
     uint32_t n_src;      // sources of this build
     uint32_t pad;
-    uint32_t level_count[kMaxLevels];
-    uint32_t level_offset[kMaxLevels + 1];
+};
+
+// fp64 (mass, mass-weighted offsets) used for centre-of-mass prefix sums.
+struct alignas(16) D4 {
+    double m, x, y, z;
+};
+__host__ __device__ inline D4 operator+(D4 a, D4 b) { return D4{a.m + b.m, a.x + b.x, a.y + b.y, a.z + b.z}; }
+__host__ __device__ inline D4 operator-(D4 a, D4 b) { return D4{a.m - b.m, a.x - b.x, a.y - b.y, a.z - b.z}; }
+
+// Exclusive per-tile prefix of node counts and particle sums.
+struct alignas(16) TileScan {
+    D4 sums;
+    uint32_t nodes, pad[3];
 };
 
 // Pre-order node record; the public bh_node has the same layout.
@@ -42,16 +53,16 @@ static_assert(sizeof(Node) == sizeof(bh_node), "node matches the public record")
 constexpr uint32_t kLeafBit = 1u << 8;
 __host__ __device__ inline uint32_t node_level(uint32_t meta) { return meta & 0xffu; }
 
-// Radix sort geometry: a tile of 4096 keys per workgroup of 256 threads.
+// Radix sort geometry: a tile of 2048 keys per workgroup of 256 threads.
 constexpr int kSortThreads = 256;
-constexpr int kSortItems = 16;
+constexpr int kSortItems = 8;
 constexpr int kSortTile = kSortThreads * kSortItems;
 constexpr int kRadix = 256;
 
 // Tree build geometry: 1024 key positions per workgroup of 256 threads.
 constexpr int kBuildThreads = 256;
 constexpr int kBuildTile = 1024;
-constexpr int kBuildCols = 1 + kMaxLevels;   // node count + one count per level
+constexpr int kTileScanThreads = 256;
 
 // ---- launchers (each defined in its own .hip file) ------------------------
 
@@ -78,12 +89,18 @@ void launch_scan_rows(const uint32_t *in, uint32_t *pref, uint32_t *tot, uint32_
 
 // build.hip
 uint32_t build_blocks(uint32_t n);
+// Device scratch of the tree build (owned by the context).
+struct BuildScratch {
+    uint16_t *dc;           // per position: d + 1 (low byte), nodes starting there (high byte)
+    uint32_t *tile_counts;  // per tile: nodes starting in the tile
+    D4 *tile_sums;          // per tile: particle sums
+    TileScan *tile_scan;    // per tile: exclusive prefix; [n_tiles] = totals
+    uint32_t *first_node;   // per position (and n): pre-order index of the first node there
+    D4 *P;                  // per position (and n): prefix sums of (m, m (x - lo))
+};
 void build_tree(const uint64_t *keys_sorted, const float4 *spos, uint32_t n, int bits,
-                int leaf_cap, uint64_t node_capacity, uint16_t *dc, uint32_t *block_counts,
-                uint32_t *block_pref, uint32_t *block_tot, uint32_t *first_node,
-                uint32_t *level_list, Node *nodes, DevParams *prm, hipStream_t s);
-void com_levels(const uint64_t *keys_sorted, Node *nodes, const uint32_t *level_list,
-                uint32_t n, uint64_t node_capacity, int bits, DevParams *prm, hipStream_t s);
+                int leaf_cap, uint64_t node_capacity, BuildScratch &w, Node *nodes,
+                DevParams *prm, hipStream_t s);
 
 // traverse.hip
 struct WalkArgs {

@@ -1,4 +1,4 @@
-// Octree from Morton-sorted keys, and the bottom-up centre-of-mass pass.
+// Octree from Morton-sorted keys, and the centre of mass of every node.
 //
 // The pages build the tree top-down by inserting particles one at a time
 // under atomic child-slot locks ([Tree] 构建树结构 / 基于稠密存储的并行树构建实现方案,
@@ -20,12 +20,17 @@
 // of them, ancestors first.  So the pre-order index of node (a, l) is
 // sum_{a'<a} c(a') + l - d(a) - 1, one prefix sum over positions.
 //
-// Kernels: count (d, c, per-tile totals per column) -> a scan of each column
-// over the tiles -> emit (node start/level, level lists, index of
-// the first node at each position) -> ranges (cell end by galloping search,
-// skip = first node at the end, leaf centres of mass).  The centre of mass of
-// internal nodes ([GASPHiA] 计算节点质心) is then combined level by level from
-// the deepest level up, each node summing its children.
+// Centre of mass ([GASPHiA] 计算节点质心): M = sum m and X = sum(m x) / M over
+// the cell's particles, which are the contiguous sorted range [start, end).
+// The same tile pass keeps fp64 prefix sums P of (m, m (x - lo)) over the
+// sorted particles, so every node, leaf or internal, takes
+// (P[end] - P[start]) in one step; with fp64 sums the difference keeps about
+// 1e-10 relative accuracy even at N = 2^26, far below the fp32 result.
+//
+// Kernels: count (d, c, per-tile node totals and particle sums) -> one scan
+// over the tiles -> emit (node start/level, the index of the first node at
+// each position, the prefix sums P) -> ranges (cell end by galloping search,
+// skip = first node at the end, mass and centre of mass from P).
 #include "bh_internal.h"
 
 namespace bh {
@@ -46,20 +51,46 @@ __device__ inline int d_at(const uint64_t *keys, int64_t j, uint32_t n, int bits
     return lcp_digits(keys[j - 1], keys[j], bits);
 }
 
+// Per-particle summand of the centre-of-mass prefix: (m, m (x - lo)).
+__device__ inline D4 mass_moment(float4 q, const DevParams *prm)
+{
+    const double m = (double)q.w;
+    return D4{m, m * ((double)q.x - prm->lo[0]), m * ((double)q.y - prm->lo[1]),
+              m * ((double)q.z - prm->lo[2])};
+}
+
+__device__ inline D4 shfl_up_d4(D4 v, int o)
+{
+    return D4{__shfl_up(v.m, o, 64), __shfl_up(v.x, o, 64), __shfl_up(v.y, o, 64),
+              __shfl_up(v.z, o, 64)};
+}
+
+__device__ inline D4 wave_incl_scan_d4(D4 v)
+{
+    const uint32_t lane = threadIdx.x & 63;
+    for (int o = 1; o < 64; o <<= 1) {
+        const D4 t = shfl_up_d4(v, o);
+        if (lane >= (uint32_t)o) v = v + t;
+    }
+    return v;
+}
+
 __global__ __launch_bounds__(kBuildThreads) void k_count(const uint64_t *__restrict__ keys,
+                                                         const float4 *__restrict__ spos,
                                                          uint32_t n, int bits, int B,
                                                          uint16_t *__restrict__ dc,
                                                          uint32_t *__restrict__ block_counts,
-                                                         uint32_t n_tiles)
+                                                         D4 *__restrict__ block_sums,
+                                                         const DevParams *__restrict__ prm)
 {
     __shared__ int8_t sd[kBuildTile + 2 * kMaxLeafCap + 2];
-    __shared__ uint32_t lc[kBuildCols];
+    __shared__ uint32_t lc;
     const int64_t t0 = (int64_t)blockIdx.x * kBuildTile;
     const int64_t w0 = t0 - B;   // window covers positions [t0 - B, t0 + tile + B]
     const int wlen = kBuildTile + 2 * B + 1;
     for (int k = threadIdx.x; k < wlen; k += kBuildThreads)
         sd[k] = (int8_t)d_at(keys, w0 + k, n, bits);
-    if (threadIdx.x < kBuildCols) lc[threadIdx.x] = 0;
+    if (threadIdx.x == 0) lc = 0;
     __syncthreads();
 
     for (int k = 0; k < kBuildTile / kBuildThreads; ++k) {
@@ -90,13 +121,30 @@ __global__ __launch_bounds__(kBuildThreads) void k_count(const uint64_t *__restr
             for (int t = 1; t <= B; ++t) rm = min(rm, (int)sd[ia + t]);
             const int ell = min(bits, 1 + max(da, rm));
             c = ell - da;
-            for (int l = da + 1; l <= ell; ++l) atomicAdd(&lc[1 + l], 1u);
-            atomicAdd(&lc[0], (uint32_t)c);
+            atomicAdd(&lc, (uint32_t)c);
         }
         dc[a] = (uint16_t)((da + 1) | (c << 8));
     }
-    __syncthreads();
-    if (threadIdx.x < kBuildCols) block_counts[threadIdx.x * n_tiles + blockIdx.x] = lc[threadIdx.x];
+    // the tile's particle sums, each thread over 4 consecutive positions in
+    // the order the emit kernel scans them
+    {
+        constexpr int per = kBuildTile / kBuildThreads;
+        __shared__ D4 wsum[kBuildThreads / 64];
+        D4 acc = {0.0, 0.0, 0.0, 0.0};
+        for (int k = 0; k < per; ++k) {
+            const int64_t a = t0 + per * threadIdx.x + k;
+            if (a < (int64_t)n) acc = acc + mass_moment(spos[a], prm);
+        }
+        const D4 incl = wave_incl_scan_d4(acc);
+        if ((threadIdx.x & 63) == 63) wsum[threadIdx.x >> 6] = incl;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            D4 tot = wsum[0];
+            for (int w = 1; w < kBuildThreads / 64; ++w) tot = tot + wsum[w];
+            block_sums[blockIdx.x] = tot;
+            block_counts[blockIdx.x] = lc;
+        }
+    }
 }
 
 __device__ inline uint32_t wave_incl_scan(uint32_t v)
@@ -109,78 +157,134 @@ __device__ inline uint32_t wave_incl_scan(uint32_t v)
     return v;
 }
 
-// pref[c][t] / tot[c]: per-column scan over tiles of the k_count table
-// (column 0: nodes, column 1 + l: nodes of level l).
-__global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restrict__ dc, uint32_t n,
-                                                        const uint32_t *__restrict__ pref,
-                                                        const uint32_t *__restrict__ tot,
+// tiles: the exclusive scan over tiles of the node counts and particle sums.
+__global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restrict__ dc,
+                                                        const float4 *__restrict__ spos, uint32_t n,
+                                                        const TileScan *__restrict__ tiles,
                                                         uint32_t n_tiles, uint64_t cap,
                                                         uint32_t *__restrict__ first_node,
-                                                        uint32_t *__restrict__ level_list,
+                                                        D4 *__restrict__ P,
                                                         Node *__restrict__ nodes,
                                                         DevParams *__restrict__ prm)
 {
     constexpr int per = kBuildTile / kBuildThreads;  // consecutive positions per thread
     __shared__ uint32_t wtot[kBuildThreads / 64];
-    __shared__ uint32_t lrank[kBuildCols];
-    __shared__ uint32_t lbase[kBuildCols];   // this tile's first slot in each level list
+    __shared__ D4 wsum[kBuildThreads / 64];
     const uint32_t blk = blockIdx.x;
-    const uint32_t total = tot[0];           // all nodes
-    if (threadIdx.x < kBuildCols) lrank[threadIdx.x] = 0;
-    if (threadIdx.x == 0) {
-        uint32_t off = 0;
-        for (int l = 0; l < kMaxLevels; ++l) {
-            lbase[1 + l] = off + pref[(1 + l) * n_tiles + blk];
-            off += tot[1 + l];
-        }
-    }
+    const uint32_t total = tiles[n_tiles].nodes;   // all nodes
 
     const int64_t a0 = (int64_t)blk * kBuildTile + per * threadIdx.x;
     int dd[per], cc[per];
+    D4 mm[per];
     uint32_t s = 0;
+    D4 ms = {0.0, 0.0, 0.0, 0.0};
     for (int k = 0; k < per; ++k) {
         const int64_t a = a0 + k;
         uint16_t v = a < (int64_t)n ? dc[a] : (uint16_t)0;
         dd[k] = (int)(v & 0xffu) - 1;
         cc[k] = v >> 8;
         s += cc[k];
+        mm[k] = a < (int64_t)n ? mass_moment(spos[a], prm) : D4{0.0, 0.0, 0.0, 0.0};
+        ms = ms + mm[k];
     }
     const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t incl = wave_incl_scan(s);
-    if (lane == 63) wtot[wave] = incl;
+    const D4 mincl = wave_incl_scan_d4(ms);
+    if (lane == 63) {
+        wtot[wave] = incl;
+        wsum[wave] = mincl;
+    }
     __syncthreads();
-    uint32_t run = pref[blk];
-    for (uint32_t w = 0; w < wave; ++w) run += wtot[w];
+    uint32_t run = tiles[blk].nodes;
+    D4 mrun = tiles[blk].sums;
+    for (uint32_t w = 0; w < wave; ++w) {
+        run += wtot[w];
+        mrun = mrun + wsum[w];
+    }
     run += incl - s;
+    mrun = mrun + (mincl - ms);
 
     for (int k = 0; k < per; ++k) {
         const int64_t a = a0 + k;
         if (a >= (int64_t)n) break;
         first_node[a] = run;
+        P[a] = mrun;
+        mrun = mrun + mm[k];
         for (int j = 0; j < cc[k]; ++j) {
             const int l = dd[k] + 1 + j;
             const uint32_t X = run + j;
-            const uint32_t r = atomicAdd(&lrank[1 + l], 1u);
-            const uint32_t pos = lbase[1 + l] + r;
             if (X < cap) {
                 nodes[X].start = (uint32_t)a;
                 nodes[X].meta = (uint32_t)l | (j == cc[k] - 1 ? kLeafBit : 0u);
             }
-            if (pos < cap) level_list[pos] = X;
         }
         run += cc[k];
     }
-    if (blk == n_tiles - 1 && threadIdx.x == 0) first_node[n] = total;
+    if (blk == n_tiles - 1 && threadIdx.x == 0) {
+        first_node[n] = total;
+        P[n] = tiles[n_tiles].sums;
+    }
     if (blk == 0 && threadIdx.x == 0) {
         prm->n_nodes = total;
         if (total > cap) prm->status |= kStatusCapacity;
-        uint32_t off = 0;
-        for (int l = 0; l < kMaxLevels; ++l) {
-            prm->level_offset[l] = off;
-            prm->level_count[l] = tot[1 + l];
-            off += tot[1 + l];
+    }
+}
+
+// Exclusive scan over the tiles of (node count, particle sums), one
+// workgroup; tiles[n_tiles] receives the totals.  Each thread sums a
+// contiguous run of tiles, the first wave scans the per-thread totals, and
+// each thread rescans its run.
+__global__ __launch_bounds__(kTileScanThreads) void k_scan_tiles(
+    const uint32_t *__restrict__ counts, const D4 *__restrict__ sums, uint32_t n_tiles,
+    TileScan *__restrict__ out)
+{
+    __shared__ D4 tsum[kTileScanThreads];
+    __shared__ uint32_t tcnt[kTileScanThreads];
+    const uint32_t chunk = (n_tiles + kTileScanThreads - 1) / kTileScanThreads;
+    const uint32_t b = min(n_tiles, threadIdx.x * chunk), e = min(n_tiles, b + chunk);
+    uint32_t c = 0;
+    D4 m = {0.0, 0.0, 0.0, 0.0};
+    for (uint32_t t = b; t < e; ++t) {
+        c += counts[t];
+        m = m + sums[t];
+    }
+    tcnt[threadIdx.x] = c;
+    tsum[threadIdx.x] = m;
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        // lane k owns per-thread totals [k*R, k*R + R)
+        constexpr int R = kTileScanThreads / 64;
+        uint32_t lc = 0;
+        D4 lm = {0.0, 0.0, 0.0, 0.0};
+        for (int r = 0; r < R; ++r) {
+            lc += tcnt[threadIdx.x * R + r];
+            lm = lm + tsum[threadIdx.x * R + r];
         }
-        prm->level_offset[kMaxLevels] = off;
+        const uint32_t ic = wave_incl_scan(lc);
+        const D4 im = wave_incl_scan_d4(lm);
+        uint32_t rc = ic - lc;
+        D4 rm = im - lm;
+        for (int r = 0; r < R; ++r) {
+            const uint32_t vc = tcnt[threadIdx.x * R + r];
+            const D4 vm = tsum[threadIdx.x * R + r];
+            tcnt[threadIdx.x * R + r] = rc;
+            tsum[threadIdx.x * R + r] = rm;
+            rc += vc;
+            rm = rm + vm;
+        }
+        if (threadIdx.x == 63) {
+            out[n_tiles].nodes = rc;
+            out[n_tiles].sums = rm;
+        }
+    }
+    __syncthreads();
+    c = tcnt[threadIdx.x];
+    m = tsum[threadIdx.x];
+    for (uint32_t t = b; t < e; ++t) {
+        out[t].nodes = c;
+        out[t].sums = m;
+        c += counts[t];
+        m = m + sums[t];
     }
 }
 
@@ -209,7 +313,7 @@ __device__ inline float3 cell_centre(uint64_t key, int level, int bits, const De
 }
 
 __global__ __launch_bounds__(256) void k_ranges(const uint64_t *__restrict__ keys,
-                                                const float4 *__restrict__ spos, uint32_t n,
+                                                const D4 *__restrict__ P, uint32_t n,
                                                 int bits, uint64_t cap,
                                                 const uint32_t *__restrict__ first_node,
                                                 Node *__restrict__ nodes,
@@ -237,57 +341,14 @@ __global__ __launch_bounds__(256) void k_ranges(const uint64_t *__restrict__ key
         const uint32_t e = hi;
         nodes[X].count = e - a;
         nodes[X].skip = first_node[e];
-        if (meta & kLeafBit) {
-            const float4 r = spos[a];
-            float m = 0.f, sx = 0.f, sy = 0.f, sz = 0.f;
-            for (uint32_t j = a; j < e; ++j) {
-                const float4 q = spos[j];
-                m += q.w;
-                sx = fmaf(q.w, q.x - r.x, sx);
-                sy = fmaf(q.w, q.y - r.y, sy);
-                sz = fmaf(q.w, q.z - r.z, sz);
-            }
-            float4 com;
-            if (m != 0.f) {
-                com = make_float4(r.x + sx / m, r.y + sy / m, r.z + sz / m, m);
-            } else {
-                const float3 c = cell_centre(keys[a], l, bits, prm);
-                com = make_float4(c.x, c.y, c.z, 0.f);
-            }
-            *reinterpret_cast<float4 *>(&nodes[X]) = com;
-        }
-    }
-}
-
-// Internal nodes of one level: mass and centre of mass from their children,
-// which follow the node in pre-order (first child = node + 1, next = skip).
-__global__ __launch_bounds__(256) void k_com_level(const uint64_t *__restrict__ keys,
-                                                   Node *__restrict__ nodes,
-                                                   const uint32_t *__restrict__ level_list,
-                                                   int level, int bits, uint64_t cap,
-                                                   const DevParams *__restrict__ prm)
-{
-    if (prm->n_nodes > cap) return;
-    const uint32_t cnt = prm->level_count[level];
-    const uint32_t off = prm->level_offset[level];
-    for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < cnt; i += gridDim.x * blockDim.x) {
-        const uint32_t X = level_list[off + i];
-        const Node nd = nodes[X];
-        if (nd.meta & kLeafBit) continue;
-        const float4 r = *reinterpret_cast<const float4 *>(&nodes[X + 1]);
-        float m = 0.f, sx = 0.f, sy = 0.f, sz = 0.f;
-        for (uint32_t c = X + 1; c < nd.skip; c = nodes[c].skip) {
-            const float4 q = *reinterpret_cast<const float4 *>(&nodes[c]);
-            m += q.w;
-            sx = fmaf(q.w, q.x - r.x, sx);
-            sy = fmaf(q.w, q.y - r.y, sy);
-            sz = fmaf(q.w, q.z - r.z, sz);
-        }
+        const D4 sum = P[e] - P[a];
         float4 com;
-        if (m != 0.f) {
-            com = make_float4(r.x + sx / m, r.y + sy / m, r.z + sz / m, m);
+        if (sum.m != 0.0) {
+            com = make_float4((float)(prm->lo[0] + sum.x / sum.m),
+                              (float)(prm->lo[1] + sum.y / sum.m),
+                              (float)(prm->lo[2] + sum.z / sum.m), (float)sum.m);
         } else {
-            const float3 c = cell_centre(keys[nd.start], level, bits, prm);
+            const float3 c = cell_centre(keys[a], l, bits, prm);
             com = make_float4(c.x, c.y, c.z, 0.f);
         }
         *reinterpret_cast<float4 *>(&nodes[X]) = com;
@@ -310,28 +371,20 @@ uint32_t build_blocks(uint32_t n)
 }
 
 void build_tree(const uint64_t *keys_sorted, const float4 *spos, uint32_t n, int bits,
-                int leaf_cap, uint64_t node_capacity, uint16_t *dc, uint32_t *block_counts,
-                uint32_t *block_pref, uint32_t *block_tot, uint32_t *first_node,
-                uint32_t *level_list, Node *nodes, DevParams *prm, hipStream_t s)
+                int leaf_cap, uint64_t node_capacity, BuildScratch &w, Node *nodes,
+                DevParams *prm, hipStream_t s)
 {
     const uint32_t tiles = build_blocks(n);
-    hipLaunchKernelGGL(k_count, dim3(tiles), dim3(kBuildThreads), 0, s, keys_sorted, n, bits,
-                       leaf_cap, dc, block_counts, tiles);
-    launch_scan_rows(block_counts, block_pref, block_tot, kBuildCols, tiles, s);
-    hipLaunchKernelGGL(k_emit, dim3(tiles), dim3(kBuildThreads), 0, s, dc, n,
-                       (const uint32_t *)block_pref, (const uint32_t *)block_tot, tiles,
-                       node_capacity, first_node, level_list, nodes, prm);
-    hipLaunchKernelGGL(k_ranges, dim3(grid_for(n, 2048)), dim3(256), 0, s, keys_sorted, spos, n,
-                       bits, node_capacity, first_node, nodes, (const DevParams *)prm);
-}
-
-void com_levels(const uint64_t *keys_sorted, Node *nodes, const uint32_t *level_list, uint32_t n,
-                uint64_t node_capacity, int bits, DevParams *prm, hipStream_t s)
-{
-    const uint32_t grid = grid_for(n / 2 + 1, 1024);
-    for (int l = bits - 1; l >= 0; --l)
-        hipLaunchKernelGGL(k_com_level, dim3(grid), dim3(256), 0, s, keys_sorted, nodes,
-                           level_list, l, bits, node_capacity, (const DevParams *)prm);
+    hipLaunchKernelGGL(k_count, dim3(tiles), dim3(kBuildThreads), 0, s, keys_sorted, spos, n, bits,
+                       leaf_cap, w.dc, w.tile_counts, w.tile_sums, (const DevParams *)prm);
+    hipLaunchKernelGGL(k_scan_tiles, dim3(1), dim3(kTileScanThreads), 0, s,
+                       (const uint32_t *)w.tile_counts, (const D4 *)w.tile_sums, tiles, w.tile_scan);
+    hipLaunchKernelGGL(k_emit, dim3(tiles), dim3(kBuildThreads), 0, s, (const uint16_t *)w.dc, spos,
+                       n, (const TileScan *)w.tile_scan, tiles, node_capacity, w.first_node, w.P,
+                       nodes, prm);
+    hipLaunchKernelGGL(k_ranges, dim3(grid_for(n, 2048)), dim3(256), 0, s, keys_sorted,
+                       (const D4 *)w.P, n, bits, node_capacity, (const uint32_t *)w.first_node,
+                       nodes, (const DevParams *)prm);
 }
 
 }  // namespace bh

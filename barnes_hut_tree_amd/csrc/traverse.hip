@@ -25,7 +25,7 @@
 namespace bh {
 namespace {
 
-constexpr int kWalkThreads = 256;
+constexpr int kWalkThreads = 64;
 
 // Blocks are dispatched to the 8 XCDs round-robin; give each XCD a contiguous
 // run of the Morton order so the nodes and particles its waves share stay in

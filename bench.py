@@ -199,7 +199,7 @@ def main():
                    "interactions_per_step": interactions,
                    "walk_ms": round(walk_ms, 4),
                    "phase_ms": {k: round(v, 4) for k, v in zip(
-                       ("bbox_keys", "sort", "tree", "com", "walk"), phases)}},
+                       ("bbox_keys", "sort", "tree_com", "walk"), phases)}},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

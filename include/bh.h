@@ -140,8 +140,8 @@ bh_status bh_get_bbox(bh_ctx *ctx, double *lo, double *hi, double *L, void *stre
 
 /* Per-phase device times of the last bh_build and bh_gravity in ms, when
  * enabled with bh_set_profiling (events add a little overhead).
- * ms[0] bbox + keys, ms[1] sort, ms[2] tree, ms[3] centre of mass,
- * ms[4] walk (the last bh_gravity).  Synchronous. */
+ * ms[0] bbox + keys, ms[1] sort, ms[2] tree with centres of mass,
+ * ms[3] walk (the last bh_gravity).  Up to n (<= 4) entries.  Synchronous. */
 bh_status bh_set_profiling(bh_ctx *ctx, int enable);
 bh_status bh_get_profile(bh_ctx *ctx, float *ms, int n);
 
