@@ -43,6 +43,9 @@ def make_workload(name):
         return W.galaxy_pair()[0], dict(theta=0.5, G=1.0, eps=0.02), "galaxy_pair_n5000000"
     if name == "uniform":
         return W.uniform_cube(4096, seed=1), dict(theta=0.5, G=1.0, eps=1e-3), "uniform_n4096"
+    if name.startswith("uniform_2p"):
+        n = 1 << int(name[len("uniform_2p"):])
+        return W.uniform_box(n, seed=5), dict(theta=0.5, G=1.0, eps=1e-3), "uniform_n%d" % n
     raise SystemExit("unknown workload " + name)
 
 
