@@ -1,0 +1,117 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case plants one mistake in a copy of oracle.c (a text substitution; the
+oracle itself is untouched), compiles it on the CPU, and runs the pin tests of
+test_oracle.py against it: at least one pin must fail.  CPU only."""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+import test_oracle as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, original text in oracle.c, planted mistake)
+MUTANTS = [
+    ("pair_sign", "d[a] = xs[a] - w->x[a];", "d[a] = w->x[a] - xs[a];"),
+    ("potential_sign", "w->phi -= w->G * m * inv_r;", "w->phi += w->G * m * inv_r;"),
+    ("dropped_softening", "double d[3], r2 = w->eps_sq;", "double d[3], r2 = 0.0;"),
+    ("inverse_square_power", "double inv_r3 = inv_r * inv_r * inv_r;\n    for (int a = 0; a < 3; ++a) w->acc",
+     "double inv_r3 = inv_r * inv_r;\n    for (int a = 0; a < 3; ++a) w->acc"),
+    ("half_edge_w", "double width = ldexp(t->L, -cell->level);",
+     "double width = ldexp(t->L, -cell->level - 1);"),
+    ("mac_non_strict", "int accept = threshold < r_sq;", "int accept = threshold <= r_sq;"),
+    ("mac_to_cell_centre", "double d = cell->com[a] - w->x[a];",
+     "double d = t->lo[a] + ldexp(t->L, -cell->level) * ((double)cell->corner[a] + 0.5) - w->x[a];"),
+    ("self_not_excluded", "if (p == w->self) continue;", "if (p == -7) continue;"),
+    ("octant_bit_order", "return ox + 2 * oy + 4 * oz;", "return oz + 2 * oy + 4 * ox;"),
+    ("key_axis_order", "key |= ((qa >> k) & 1u) << (3 * k + a);",
+     "key |= ((qa >> k) & 1u) << (3 * k + (2 - a));"),
+    ("leaf_rule_le", "if (count <= t->leaf_cap || level == t->bits) {",
+     "if (count < t->leaf_cap || level == t->bits) {"),
+    ("no_max_depth", "if (count <= t->leaf_cap || level == t->bits) {",
+     "if (count <= t->leaf_cap || level == t->bits + 1) {"),
+    ("com_unweighted", "s[a] += mp * (double)t->src[4 * p + a];", "s[a] += (double)t->src[4 * p + a];"),
+    ("bbox_extent_min", "if (ext > t->L) t->L = ext;", "if (ext < t->L || t->L == 0.0) t->L = ext;"),
+    ("key_no_clamp", "uint64_t qa = (f >= (double)top) ? top : (uint64_t)f;",
+     "uint64_t qa = (uint64_t)f & top;"),
+    ("unstable_order", "return (a > b) - (a < b);", "return (a < b) - (a > b);"),
+    ("direct_self_pair", "if (j == self) continue;", "if (j == -7) continue;"),
+    ("direct_sign", "d[a] = (double)src[4 * j + a] - x[a];", "d[a] = x[a] - (double)src[4 * j + a];"),
+]
+
+PIN_TESTS = [name for name in dir(pins) if name.startswith("test_")]
+
+
+def _build_mutant(name, old, new, workdir):
+    text = open(SRC).read()
+    assert old in text, "mutation site not found in oracle.c: %s" % name
+    path = os.path.join(workdir, "oracle_%s.c" % name)
+    with open(path, "w") as fh:
+        fh.write(text.replace(old, new, 1))
+    lib = os.path.join(workdir, "liboracle_%s.so" % name)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+                    "-o", lib, path, "-lm"], check=True)
+    return lib
+
+
+def _run_pins_against(lib_path):
+    """Run every pin with the oracle module pointed at lib_path; return the
+    names of the pins that failed."""
+    saved = oracle._lib
+    failed = []
+    try:
+        oracle._lib = None
+        real_lib = oracle._LIB
+        oracle._LIB = lib_path
+        # load through the module's own loader (it checks mtimes: skip building)
+        orig_build = oracle.build
+        oracle.build = lambda force=False: lib_path
+        try:
+            oracle.lib()
+            for name in PIN_TESTS:
+                fn = getattr(pins, name)
+                params = getattr(fn, "pytestmark", [])
+                cases = [()]
+                for mark in params:
+                    if mark.name == "parametrize":
+                        argnames, values = mark.args[0], mark.args[1]
+                        argnames = [a.strip() for a in argnames.split(",")] if isinstance(
+                            argnames, str) else list(argnames)
+                        new = []
+                        for c in cases:
+                            for v in values:
+                                v = v if isinstance(v, tuple) else (v,)
+                                new.append(c + tuple(zip(argnames, v)))
+                        cases = new
+                for case in cases:
+                    try:
+                        fn(oracle, **dict(case))
+                    except Exception:  # an assertion, or a crash the mistake causes
+                        failed.append(name)
+                        break
+        finally:
+            oracle.build = orig_build
+            oracle._LIB = real_lib
+    finally:
+        oracle._lib = saved
+    return failed
+
+
+def test_unmutated_copy_passes_every_pin(orc):
+    """Control: the harness itself makes no pin fail."""
+    with tempfile.TemporaryDirectory() as d:
+        lib = _build_mutant("control", "", "", d)
+        failed = _run_pins_against(lib)
+    assert not failed, failed
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(orc, name, old, new):
+    with tempfile.TemporaryDirectory() as d:
+        lib = _build_mutant(name, old, new, d)
+        failed = _run_pins_against(lib)
+    assert failed, "no pin caught the planted mistake %r" % name
