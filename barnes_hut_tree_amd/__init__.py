@@ -23,7 +23,7 @@ BH_ERR_CAPACITY = -4
 BH_ERR_NONFINITE = -5
 BH_ERR_NOT_BUILT = -6
 
-EXPORTS = ("bh_create", "bh_build", "bh_gravity", "bh_gravity_counted", "bh_sync", "bh_destroy",
+EXPORTS = ("bh_create", "bh_build", "bh_gravity", "bh_gravity_counted", "bh_direct", "bh_sync", "bh_destroy",
            "bh_status_string", "bh_get_keys", "bh_get_node_count", "bh_get_nodes", "bh_get_bbox",
            "bh_set_profiling", "bh_get_profile")
 
@@ -60,6 +60,7 @@ def load_library():
         "bh_build": [P, P, i64, P],
         "bh_gravity": [P, P, i64, f32, f32, f32, P, P],
         "bh_gravity_counted": [P, P, i64, f32, f32, f32, P, P, P],
+        "bh_direct": [P, i64, P, i64, f32, f32, P, P],
         "bh_sync": [P],
         "bh_destroy": [P],
         "bh_get_keys": [P, P, P, P],
@@ -215,6 +216,28 @@ class BarnesHut:
         ms = (ctypes.c_float * 4)()
         _check(load_library().bh_get_profile(self._h, ms, 4), "bh_get_profile")
         return list(ms)
+
+
+def direct(src, G=1.0, eps=0.0, targets=None, out=None):
+    """All-pairs direct sum (bh_direct): (n_targets, 4) float32 ax, ay, az, phi.
+    targets=None: the sources themselves, each excluding itself."""
+    import torch
+    src = _rows(src, "src")
+    if targets is not None:
+        targets = _rows(targets, "targets")
+        nt, tp = targets.shape[0], ctypes.c_void_p(targets.data_ptr())
+    else:
+        nt, tp = src.shape[0], ctypes.c_void_p()
+    if out is None:
+        out = torch.empty((nt, 4), dtype=torch.float32, device="cuda")
+    else:
+        _rows(out, "out")
+    if nt == 0:   # an empty tensor's data pointer is NULL, which would mean "self"
+        return out
+    _check(load_library().bh_direct(ctypes.c_void_p(src.data_ptr()), src.shape[0], tp, nt,
+                                    float(G), float(eps), ctypes.c_void_p(out.data_ptr()),
+                                    _stream()), "bh_direct")
+    return out
 
 
 def nodes_numpy(node_tensor):

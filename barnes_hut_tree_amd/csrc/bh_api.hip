@@ -47,6 +47,9 @@ struct bh_ctx {
 
 namespace {
 
+// particle and target counts must fit 31 bits
+constexpr int64_t kMaxCount = ((int64_t)1 << 31) - 1;
+
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 template <typename T>
@@ -102,8 +105,7 @@ bh_status bh_create(bh_ctx **out, int64_t max_sources, int64_t max_targets,
 {
     if (!out) return BH_ERR_INVALID;
     *out = nullptr;
-    if (max_sources < 0 || max_targets < 0 || max_sources >= (int64_t)1 << 31 ||
-        max_targets >= (int64_t)1 << 31)
+    if (max_sources < 0 || max_targets < 0 || max_sources > kMaxCount || max_targets > kMaxCount)
         return BH_ERR_INVALID;
     bh_build_params p = {63, 16, 0};
     if (params) p = *params;
@@ -267,6 +269,30 @@ bh_status bh_gravity_counted(bh_ctx *c, const float *targets, int64_t n_targets,
 {
     if (!interactions) return BH_ERR_INVALID;
     return gravity_impl(c, targets, n_targets, theta, G, eps, out_acc_pot, interactions, stream);
+}
+
+bh_status bh_direct(const float *src_pos_mass, int64_t n_src, const float *targets,
+                    int64_t n_targets, float G, float eps, float *out_acc_pot, void *stream)
+{
+    if (n_src < 0 || n_targets < 0 || n_src > kMaxCount || n_targets > kMaxCount)
+        return BH_ERR_INVALID;
+    if (!(eps >= 0.f) || !__builtin_isfinite(G)) return BH_ERR_INVALID;
+    if (n_src > 0 && (!src_pos_mass || !aligned16(src_pos_mass))) return BH_ERR_INVALID;
+    if (n_targets > 0 && (!out_acc_pot || !aligned16(out_acc_pot))) return BH_ERR_INVALID;
+    if (targets) {
+        if (!aligned16(targets)) return BH_ERR_INVALID;
+    } else if (n_targets != n_src) {
+        return BH_ERR_INVALID;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    const uint32_t nt = (uint32_t)n_targets;
+    if (nt == 0) return BH_OK;
+    if (n_src == 0)
+        launch_fill_zero((float4 *)out_acc_pot, nt, s);
+    else
+        launch_direct((const float4 *)src_pos_mass, (uint32_t)n_src, (const float4 *)targets, nt,
+                      targets == nullptr, G, eps, (float4 *)out_acc_pot, s);
+    return launch_status();
 }
 
 static bh_status read_params(bh_ctx *c, hipStream_t s)

@@ -118,4 +118,9 @@ struct WalkArgs {
 void launch_walk(const WalkArgs &a, hipStream_t s);
 void launch_fill_zero(float4 *out, uint32_t n, hipStream_t s);
 
+// direct.hip: all-pairs sum over the caller's sources (self: tgt is ignored,
+// the sources are the targets and each excludes itself)
+void launch_direct(const float4 *src, uint32_t n, const float4 *tgt, uint32_t nt, bool self,
+                   float G, float eps, float4 *out, hipStream_t s);
+
 }  // namespace bh

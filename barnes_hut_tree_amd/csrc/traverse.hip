@@ -21,6 +21,7 @@
 // the wave goes, and the per-lane rejoin index keeps each lane's result its
 // own).
 #include "bh_internal.h"
+#include "interaction.h"
 
 namespace bh {
 namespace {
@@ -34,22 +35,6 @@ __device__ inline uint32_t xcd_block(uint32_t b, uint32_t nb)
 {
     const uint32_t x = b & 7u, k = b >> 3, q = nb >> 3, r = nb & 7u;
     return x * q + min(x, r) + k;
-}
-
-template <bool SOFT>
-__device__ inline void pair(float4 s, float px, float py, float pz, float eps2, float &ax,
-                            float &ay, float &az, float &pot)
-{
-    const float dx = s.x - px, dy = s.y - py, dz = s.z - pz;
-    const float r2 = fmaf(dz, dz, fmaf(dy, dy, fmaf(dx, dx, eps2)));
-    float inv = __builtin_amdgcn_rsqf(r2);
-    if (!SOFT) inv = r2 > 0.f ? inv : 0.f;
-    const float mi = s.w * inv;
-    const float f = mi * inv * inv;
-    ax = fmaf(f, dx, ax);
-    ay = fmaf(f, dy, ay);
-    az = fmaf(f, dz, az);
-    pot -= mi;
 }
 
 // Direct sum over the sources [b, e) of an opened leaf, eight at a time (one

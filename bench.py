@@ -50,10 +50,13 @@ def make_workload(name):
 
 
 def walk_source_hash():
-    """Hash of the walk kernel source: counter summaries taken for another
-    version of the kernel are not reported."""
-    path = os.path.join(ROOT, "barnes_hut_tree_amd", "csrc", "traverse.hip")
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """Hash of the walk kernel's sources (the walk and its pair interaction):
+    counter summaries taken for another version of the kernel are not
+    reported."""
+    h = hashlib.sha256()
+    for f in ("traverse.hip", "interaction.h"):
+        h.update(open(os.path.join(ROOT, "barnes_hut_tree_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(workload):
@@ -109,6 +112,64 @@ def cpu_baseline(p, prm, key_bits, leaf_cap, budget_s=8.0):
     }
 
 
+def theta_sweep(args):
+    """Accuracy and speed-up of the walk against the GPU direct sum over a
+    range of opening angles, in the layout of the pages' table ([GASPHiA]
+    精度与加速比验证): walk time, max and mean relative error of the
+    acceleration vector, speed-up over the direct sum.  One JSON line per
+    theta, then a summary line."""
+    import torch
+
+    import barnes_hut_tree_amd as bh
+    p, prm, wname = make_workload(args.workload)
+    n = p.shape[0]
+    src = torch.from_numpy(p).cuda()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    ref = torch.empty((n, 4), dtype=torch.float32, device="cuda")
+    direct_ms = timed(lambda: bh.direct(src, prm["G"], prm["eps"], out=ref), 2)
+    ref64 = ref.double()
+    ref_norm = ref64[:, :3].norm(dim=1)
+    pairs = n * (n - 1)
+    print(json.dumps({"kernel": "direct", "workload": wname, "n": n, "ms": round(direct_ms, 3),
+                      "pairs_per_s": pairs / (direct_ms * 1e-3),
+                      "tflops_at_20_per_pair": round(20 * pairs / (direct_ms * 1e-3) / 1e12, 2)}),
+          flush=True)
+
+    tree = bh.BarnesHut(n, 0, args.key_bits, args.leaf_cap)
+    build_ms = timed(lambda: tree.build(src), 5)
+    tree.sync()
+    out = torch.empty_like(ref)
+    rows = []
+    thetas = [0.1, 0.2, 0.3, 0.4, 0.5, 0.6, 0.7, 0.8] if args.theta is None else [args.theta]
+    for th in thetas:
+        walk_ms = timed(lambda: tree.gravity(th, prm["G"], prm["eps"], out=out), 3)
+        err = (out.double()[:, :3] - ref64[:, :3]).norm(dim=1) / ref_norm
+        perr = ((out.double()[:, 3] - ref64[:, 3]) / ref64[:, 3]).abs()
+        row = {"theta": th, "walk_ms": round(walk_ms, 3), "build_ms": round(build_ms, 3),
+               "max_rel_err": float(err.max()), "mean_rel_err": float(err.mean()),
+               "pot_max_rel_err": float(perr.max()), "pot_mean_rel_err": float(perr.mean()),
+               "interactions": tree.count_interactions(th, prm["eps"]),
+               "speedup_walk": round(direct_ms / walk_ms, 1),
+               "speedup_step": round(direct_ms / (walk_ms + build_ms), 1)}
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+    tree.close()
+    print(json.dumps({"sweep": wname, "n": n, "eps": prm["eps"], "leaf_cap": args.leaf_cap,
+                      "direct_ms": round(direct_ms, 3), "rows": len(rows)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +180,8 @@ def main():
     ap.add_argument("--key-bits", type=int, default=63)
     ap.add_argument("--theta", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="theta sweep against the GPU direct sum instead of the step benchmark")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB (3 times), "
                          "the reference kernel for scaling HBM byte counters")
@@ -133,6 +196,9 @@ def main():
     import barnes_hut_tree_amd as bh
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.sweep:
+        theta_sweep(args)
+        return
 
     if args.copy_calibration_mib:
         nbytes = args.copy_calibration_mib << 20

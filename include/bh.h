@@ -111,6 +111,23 @@ bh_status bh_gravity_counted(bh_ctx *ctx, const float *targets, int64_t n_target
                              float theta, float G, float eps, float *out_acc_pot,
                              uint64_t *interactions, void *stream);
 
+/* All-pairs direct sum, no tree and no context: every target against every
+ * source with the interaction of bh_gravity.  This is the brute-force
+ * reference that [GASPHiA] 精度与加速比验证 measures the walk's speed-up and
+ * relative error against, and the theta = 0 limit of the walk.
+ *   src_pos_mass  device, n_src float4 rows (x, y, z, m), 16-byte aligned.
+ *   targets       NULL: the sources are the targets and each excludes itself
+ *                 (n_targets must equal n_src); else device, n_targets float4
+ *                 rows (w ignored), 16-byte aligned.
+ *   out_acc_pot   device, n_targets float4 rows (ax, ay, az, phi), in the
+ *                 order of the targets; must not overlap the inputs.
+ *   eps >= 0, G finite; n_src, n_targets < 2^31.
+ * fp32 pair terms summed in fp32 over runs of 512 sources, the runs summed in
+ * fp64.  Non-finite inputs give non-finite outputs (no status word).
+ * Asynchronous on `stream`; allocates nothing. */
+bh_status bh_direct(const float *src_pos_mass, int64_t n_src, const float *targets,
+                    int64_t n_targets, float G, float eps, float *out_acc_pot, void *stream);
+
 /* Wait for the context's last stream and return the device status word
  * (BH_OK, BH_ERR_NONFINITE or BH_ERR_CAPACITY).  Synchronous. */
 bh_status bh_sync(bh_ctx *ctx);

@@ -58,6 +58,10 @@ def test_create_rejects_bad_arguments_before_touching_the_device(lib):
     assert lib.bh_build(None, None, 0, None) == bh.BH_ERR_INVALID
     assert lib.bh_gravity(None, None, 0, 0.5, 1.0, 0.0, None, None) == bh.BH_ERR_INVALID
     assert lib.bh_destroy(None) == bh.BH_OK
+    assert lib.bh_direct(None, -1, None, -1, 1.0, 0.0, None, None) == bh.BH_ERR_INVALID
+    assert lib.bh_direct(None, 4, None, 4, 1.0, 0.0, None, None) == bh.BH_ERR_INVALID
+    assert lib.bh_direct(None, 0, None, 0, 1.0, -1.0, None, None) == bh.BH_ERR_INVALID
+    assert lib.bh_direct(None, 0, None, 0, 1.0, 0.0, None, None) == bh.BH_OK
 
 
 def test_product_path_has_no_cpu_fallback():
