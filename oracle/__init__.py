@@ -47,6 +47,9 @@ def lib():
         L.orc_bh.argtypes = [P, P, P, i64, ctypes.c_double, ctypes.c_double, ctypes.c_double,
                              ctypes.c_int, P, P, P]
         L.orc_direct.argtypes = [P, i64, P, P, i64, ctypes.c_double, ctypes.c_double, P]
+        L.orc_bh_vote.restype = ctypes.c_int
+        L.orc_bh_vote.argtypes = [P, i64, P, i64, ctypes.c_double, ctypes.c_double,
+                                  ctypes.c_double, ctypes.c_int, P, P, P]
         L.orc_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -124,6 +127,27 @@ class Tree:
         lib().orc_bh(self._h, _ptr(t), _ptr(w), nt, float(theta), float(G), float(eps),
                      int(tie_mode), _ptr(out), _ptr(ni), _ptr(nties))
         return out, ni, nties
+
+    def gravity_vote(self, theta, G=1.0, eps=0.0, group=64, groups=None, tie_mode=0):
+        """Self-gravity by the warp vote over groups of `group` consecutive sorted
+        sources: (n, 4) fp64 in the caller's order, interactions and near-ties
+        per source, and the caller indices of the evaluated groups' members
+        (all sources when groups is None)."""
+        g = None if groups is None else np.ascontiguousarray(groups, dtype=np.int64)
+        ng = 0 if g is None else g.shape[0]
+        out = np.zeros((self.n, 4))
+        ni = np.zeros(self.n, np.int64)
+        nties = np.zeros(self.n, np.int64)
+        rc = lib().orc_bh_vote(self._h, int(group), _ptr(g), ng, float(theta), float(G),
+                               float(eps), int(tie_mode), _ptr(out), _ptr(ni), _ptr(nties))
+        if rc != 0:
+            raise ValueError("orc_bh_vote failed (%d)" % rc)
+        perm = self.perm()
+        if g is None:
+            members = perm
+        else:
+            members = np.concatenate([perm[k * group:(k + 1) * group] for k in g])
+        return out, ni, nties, members
 
 
 def direct(pos_mass, G=1.0, eps=0.0, targets=None, which=None):

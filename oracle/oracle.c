@@ -430,6 +430,133 @@ void orc_bh(const orc_tree *t, const float *targets, const int64_t *which, int64
 }
 
 /* ------------------------------------------------------------------------ */
+/* The warp vote of [GASPHiA] 性能瓶颈分析: the threads of one warp walk the   */
+/* tree together, and when the opening test fails for any of them, all of    */
+/* them descend.  Here a group is `group` consecutive targets in the order    */
+/* of the stable Morton-key sort (not the tree's partition order, which      */
+/* keeps input order inside a leaf); the targets are the sources, self       */
+/* excluded.  At a cell, each member applies the test of walk(); if no       */
+/* member fails, every member uses the cell whole; otherwise every member    */
+/* uses its children, or, for a leaf, its particles.  A member therefore     */
+/* never uses a cell that the per-particle walk would open, and may use the  */
+/* children of one it would accept.  Near-ties (as in walk()) are counted    */
+/* for every member of the group.                                            */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    const orc_tree *t;
+    int64_t m;               /* members */
+    walker *w;               /* one walker (position, self, sums) per member */
+    int *accept;             /* scratch, per member */
+} group_walker;
+
+static void walk_group(group_walker *g, int64_t c)
+{
+    const orc_tree *t = g->t;
+    const orc_cell *cell = &t->cells[c];
+    const double width = ldexp(t->L, -cell->level);
+    const double threshold = width * width / g->w[0].theta_sq;
+    int any_open = 0, tie = 0;
+    for (int64_t k = 0; k < g->m; ++k) {
+        walker *w = &g->w[k];
+        double r_sq = 0.0;
+        for (int a = 0; a < 3; ++a) {
+            double d = cell->com[a] - w->x[a];
+            r_sq += d * d;
+        }
+        int accept = threshold < r_sq;
+        if (isfinite(threshold) && fabs(r_sq - threshold) <= ldexp(threshold, -20)) {
+            tie = 1;
+            if (w->tie_mode == 1) accept = 0;
+            if (w->tie_mode == 2) accept = 1;
+        }
+        g->accept[k] = accept;
+        if (!accept) any_open = 1;
+    }
+    if (tie)
+        for (int64_t k = 0; k < g->m; ++k) g->w[k].n_ties++;
+    if (!any_open) {
+        for (int64_t k = 0; k < g->m; ++k) {
+            interact(&g->w[k], cell->mass, cell->com);
+            g->w[k].n_inter++;
+        }
+        return;
+    }
+    if (!cell->is_leaf) {
+        for (int o = 0; o < 8; ++o)
+            if (cell->child[o] >= 0) walk_group(g, cell->child[o]);
+        return;
+    }
+    for (int64_t k = 0; k < g->m; ++k) {
+        walker *w = &g->w[k];
+        for (int64_t q = 0; q < cell->count; ++q) {
+            int64_t p = t->idx[cell->off + q];
+            if (p == w->self) continue;
+            double xs[3] = {(double)t->src[4 * p + 0], (double)t->src[4 * p + 1],
+                            (double)t->src[4 * p + 2]};
+            interact(w, (double)t->src[4 * p + 3], xs);
+            w->n_inter++;
+        }
+    }
+}
+
+/* Self-gravity by the warp vote, groups of `group` >= 1 consecutive sorted
+   sources.  groups[k] (or k when groups == NULL) names the k-th group to
+   evaluate, n_groups of them; out (n x 4, the caller's order of the sources)
+   and the per-source n_inter / n_ties (may be NULL) are written for the
+   members of those groups only. */
+int orc_bh_vote(const orc_tree *t, int64_t group, const int64_t *groups, int64_t n_groups,
+                double theta, double G, double eps, int tie_mode, double *out,
+                int64_t *n_inter, int64_t *n_ties)
+{
+    if (group < 1 || n_groups < 0) return -1;
+    const int64_t total = (t->n + group - 1) / group;
+    if (!groups) n_groups = total;
+    for (int64_t k = 0; k < n_groups; ++k)
+        if (groups && (groups[k] < 0 || groups[k] >= total)) return -1;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 4) reduction(| : failed)
+    for (int64_t k = 0; k < n_groups; ++k) {
+        const int64_t gi = groups ? groups[k] : k;
+        const int64_t first = gi * group;
+        const int64_t m = (t->n - first < group) ? t->n - first : group;
+        group_walker g;
+        g.t = t;
+        g.m = m;
+        g.w = (walker *)calloc((size_t)m, sizeof(walker));
+        g.accept = (int *)calloc((size_t)m, sizeof(int));
+        if (!g.w || !g.accept) {
+            free(g.w);
+            free(g.accept);
+            failed = 1;
+            continue;
+        }
+        for (int64_t q = 0; q < m; ++q) {
+            walker *w = &g.w[q];
+            const int64_t i = t->perm[first + q];
+            w->t = t;
+            for (int a = 0; a < 3; ++a) w->x[a] = (double)t->src[4 * i + a];
+            w->self = i;
+            w->theta_sq = theta * theta;
+            w->G = G;
+            w->eps_sq = eps * eps;
+            w->tie_mode = tie_mode;
+        }
+        if (t->n_cells > 0) walk_group(&g, 0);
+        for (int64_t q = 0; q < m; ++q) {
+            const walker *w = &g.w[q];
+            const int64_t i = w->self;
+            for (int a = 0; a < 3; ++a) out[4 * i + a] = w->acc[a];
+            out[4 * i + 3] = w->phi;
+            if (n_inter) n_inter[i] = w->n_inter;
+            if (n_ties) n_ties[i] = w->n_ties;
+        }
+        free(g.w);
+        free(g.accept);
+    }
+    return failed ? -2 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Direct sum, the plain definition the tree approximates ([GASPHiA]          */
 /* 如何计算自引力: every pair of particles attracts; O(N^2)):                   */
 /*   a_i = G sum_{j != i} m_j d_ij / (|d_ij|^2 + eps^2)^(3/2),                */

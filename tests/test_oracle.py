@@ -410,3 +410,65 @@ def test_near_tie_bracket_modes(orc):
     assert np.any(op[:3] != ac[:3])
     untied = ties == 0
     assert np.array_equal(base[untied], op[untied]) and np.array_equal(base[untied], ac[untied])
+
+
+# ---------------------------------------------------------------------------
+# the warp vote ([GASPHiA] 性能瓶颈分析): groups of consecutive sorted targets
+# ---------------------------------------------------------------------------
+def test_vote_group_of_one_is_the_per_particle_walk(orc):
+    p = W.plummer(3000, seed=12)
+    t = orc.Tree(p, leaf_cap=8)
+    ref, n_ref, _ = t.gravity(0.6, 1.0, 0.01)
+    out, n_v, _, members = t.gravity_vote(0.6, 1.0, 0.01, group=1)
+    assert np.array_equal(out, ref) and np.array_equal(n_v, n_ref)
+    assert np.array_equal(np.sort(members), np.arange(3000))
+
+
+def test_vote_never_uses_a_cell_the_member_would_open(orc):
+    # every member sees at least the per-particle walk's interactions, and a
+    # member of a group whose other members open more sees strictly more
+    p = W.uniform_cube(4096, seed=1)
+    t = orc.Tree(p, leaf_cap=16)
+    _, n_ref, _ = t.gravity(0.5, 1.0, 1e-3)
+    for group in (2, 64, 4096):
+        _, n_v, _, _ = t.gravity_vote(0.5, 1.0, 1e-3, group=group)
+        assert np.all(n_v >= n_ref)
+        assert n_v.sum() > n_ref.sum()
+    # one group of everything: every member uses the same cells, so all
+    # counts are equal except for the self pair
+    _, n_all, _, _ = t.gravity_vote(0.5, 1.0, 1e-3, group=4096)
+    assert n_all.max() - n_all.min() <= 1
+
+
+def test_vote_theta_limits(orc):
+    p = W.plummer(2000, seed=13)
+    t = orc.Tree(p, leaf_cap=4)
+    d = orc.direct(p, 1.0, 0.02)
+    out, n_v, _, _ = t.gravity_vote(0.0, 1.0, 0.02, group=64)
+    assert np.all(n_v == 1999)
+    assert np.allclose(out, d, rtol=1e-10, atol=1e-12)
+    ref, _, _ = t.gravity(float("inf"), 1.0, 0.02)
+    out, n_v, _, _ = t.gravity_vote(float("inf"), 1.0, 0.02, group=64)
+    assert np.array_equal(out, ref) and np.all(n_v == 1)
+
+
+def test_vote_groups_are_independent(orc):
+    p = W.plummer(5000, seed=14)
+    t = orc.Tree(p, leaf_cap=16)
+    full, n_full, _, _ = t.gravity_vote(0.5, 1.0, 0.01, group=64)
+    out, n_sub, _, members = t.gravity_vote(0.5, 1.0, 0.01, group=64, groups=[3, 40, 78])
+    assert members.shape == (64 * 2 + 5000 - 78 * 64,)
+    assert np.array_equal(out[members], full[members])
+    assert np.array_equal(n_sub[members], n_full[members])
+
+
+def test_vote_is_more_accurate_than_the_per_particle_walk(orc):
+    p = W.uniform_cube(4096, seed=1)
+    t = orc.Tree(p, leaf_cap=16)
+    d = orc.direct(p, 1.0, 1e-3)
+    dn = np.linalg.norm(d[:, :3], axis=1)
+    ref, _, _ = t.gravity(0.5, 1.0, 1e-3)
+    out, _, _, _ = t.gravity_vote(0.5, 1.0, 1e-3, group=64)
+    e_ref = np.linalg.norm(ref[:, :3] - d[:, :3], axis=1) / dn
+    e_v = np.linalg.norm(out[:, :3] - d[:, :3], axis=1) / dn
+    assert np.median(e_v) < 0.5 * np.median(e_ref)

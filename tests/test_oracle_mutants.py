@@ -41,6 +41,14 @@ MUTANTS = [
     ("unstable_order", "return (a > b) - (a < b);", "return (a < b) - (a > b);"),
     ("direct_self_pair", "if (j == self) continue;", "if (j == -7) continue;"),
     ("direct_sign", "d[a] = (double)src[4 * j + a] - x[a];", "d[a] = x[a] - (double)src[4 * j + a];"),
+    ("vote_first_member_decides", "if (!accept) any_open = 1;",
+     "if (k == 0) any_open = !accept;"),
+    ("vote_all_must_open", "if (!accept) any_open = 1;\n    }",
+     "if (!accept) any_open += 1;\n    }\n    any_open = any_open == g->m;"),
+    ("vote_leaf_self_kept", "            int64_t p = t->idx[cell->off + q];\n            if (p == w->self) continue;",
+     "            int64_t p = t->idx[cell->off + q];"),
+    ("vote_leaf_monopole", "            interact(&g->w[k], cell->mass, cell->com);",
+     "            interact(&g->w[k], cell->mass, g->w[k].x);"),
 ]
 
 PIN_TESTS = [name for name in dir(pins) if name.startswith("test_")]
