@@ -23,7 +23,10 @@ BH_ERR_CAPACITY = -4
 BH_ERR_NONFINITE = -5
 BH_ERR_NOT_BUILT = -6
 
-EXPORTS = ("bh_create", "bh_build", "bh_gravity", "bh_gravity_counted", "bh_direct", "bh_sync", "bh_destroy",
+WALK_VOTE = 1        # BH_WALK_VOTE
+WALK_UNSORTED = 2    # BH_WALK_UNSORTED
+
+EXPORTS = ("bh_create", "bh_build", "bh_gravity", "bh_gravity_counted", "bh_gravity_ex", "bh_direct", "bh_sync", "bh_destroy",
            "bh_status_string", "bh_get_keys", "bh_get_node_count", "bh_get_nodes", "bh_get_bbox",
            "bh_set_profiling", "bh_get_profile")
 
@@ -60,6 +63,7 @@ def load_library():
         "bh_build": [P, P, i64, P],
         "bh_gravity": [P, P, i64, f32, f32, f32, P, P],
         "bh_gravity_counted": [P, P, i64, f32, f32, f32, P, P, P],
+        "bh_gravity_ex": [P, P, i64, f32, f32, f32, ctypes.c_uint32, P, P, P],
         "bh_direct": [P, i64, P, i64, f32, f32, P, P],
         "bh_sync": [P],
         "bh_destroy": [P],
@@ -135,12 +139,13 @@ class BarnesHut:
                                        _stream()), "bh_build")
         self.n = t.shape[0]
 
-    def gravity(self, theta, G=1.0, eps=0.0, targets=None, out=None, interactions=None):
+    def gravity(self, theta, G=1.0, eps=0.0, targets=None, out=None, interactions=None,
+                flags=0):
         """(n_targets, 4) float32: ax, ay, az, phi in the caller's order.
 
         targets=None: the built sources, each excluding itself.
         interactions: optional uint64 (int64) CUDA tensor of 1 element that the
-        interaction count is added to."""
+        interaction count is added to.  flags: WALK_VOTE / WALK_UNSORTED."""
         import torch
         if targets is not None:
             targets = _rows(targets, "targets")
@@ -154,7 +159,12 @@ class BarnesHut:
         else:
             _rows(out, "out")
         L = load_library()
-        if interactions is None:
+        if flags:
+            cp = ctypes.c_void_p() if interactions is None else ctypes.c_void_p(
+                interactions.data_ptr())
+            st = L.bh_gravity_ex(self._h, tp, nt, float(theta), float(G), float(eps), int(flags),
+                                 ctypes.c_void_p(out.data_ptr()), cp, _stream())
+        elif interactions is None:
             st = L.bh_gravity(self._h, tp, nt, float(theta), float(G), float(eps),
                               ctypes.c_void_p(out.data_ptr()), _stream())
         else:
@@ -164,10 +174,10 @@ class BarnesHut:
         _check(st, "bh_gravity")
         return out
 
-    def count_interactions(self, theta, eps=0.0, targets=None):
+    def count_interactions(self, theta, eps=0.0, targets=None, flags=0):
         import torch
         cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
-        self.gravity(theta, 1.0, eps, targets=targets, interactions=cnt)
+        self.gravity(theta, 1.0, eps, targets=targets, interactions=cnt, flags=flags)
         return int(cnt.item())
 
     def sync(self):

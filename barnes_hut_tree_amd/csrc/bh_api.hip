@@ -29,6 +29,7 @@ struct bh_ctx {
     float4 *spos = nullptr;
     uint64_t *keys_sorted = nullptr;  // aliases keys or keys_alt after a build
     uint32_t *perm = nullptr;         // aliases vals or vals_alt after a build
+    uint32_t *inv = nullptr;          // Morton rank of each caller index (unsorted walks)
     BuildScratch bw = {};
     Node *nodes = nullptr;
 
@@ -64,7 +65,7 @@ void free_all(bh_ctx *c)
     void *ptrs[] = {c->prm, c->bbox_part, c->keys, c->keys_alt, c->vals, c->vals_alt, c->spine,
                     c->spos, c->bw.dc, c->bw.tile_counts, c->bw.tile_sums, c->bw.tile_scan,
                     c->bw.first_node, c->bw.P, c->nodes, c->tkeys, c->tkeys_alt, c->tvals,
-                    c->tvals_alt, c->tspine, c->tpos};
+                    c->tvals_alt, c->tspine, c->tpos, c->inv};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
     if (c->host_prm) (void)hipHostFree(c->host_prm);
@@ -148,6 +149,7 @@ bh_status bh_create(bh_ctx **out, int64_t max_sources, int64_t max_targets,
     ok &= dalloc(&c->bw.first_node, ns + 1) == hipSuccess;
     ok &= dalloc(&c->bw.P, ns + 1) == hipSuccess;
     ok &= dalloc(&c->nodes, (size_t)c->node_cap + 1) == hipSuccess;
+    ok &= dalloc(&c->inv, ns) == hipSuccess;
     if (nt) {
         ok &= dalloc(&c->tkeys, nt) == hipSuccess;
         ok &= dalloc(&c->tkeys_alt, nt) == hipSuccess;
@@ -208,11 +210,13 @@ bh_status bh_build(bh_ctx *c, const float *src_pos_mass, int64_t n, void *stream
 }
 
 static bh_status gravity_impl(bh_ctx *c, const float *targets, int64_t n_targets, float theta,
-                              float G, float eps, float *out, uint64_t *count, void *stream)
+                              float G, float eps, uint32_t flags, float *out, uint64_t *count,
+                              void *stream)
 {
     if (!c) return BH_ERR_INVALID;
     if (!c->built) return BH_ERR_NOT_BUILT;
     if (n_targets < 0 || !(theta >= 0.f) || !(eps >= 0.f) || !__builtin_isfinite(G)) return BH_ERR_INVALID;
+    if (flags & ~(uint32_t)(BH_WALK_VOTE | BH_WALK_UNSORTED)) return BH_ERR_INVALID;
     if (n_targets > 0 && (!out || !aligned16(out))) return BH_ERR_INVALID;
     if (targets) {
         if (n_targets > c->max_tgt || !aligned16(targets)) return BH_ERR_INVALID;
@@ -237,18 +241,30 @@ static bh_status gravity_impl(bh_ctx *c, const float *targets, int64_t n_targets
     a.eps = eps;
     a.out = (float4 *)out;
     a.count = (unsigned long long *)count;
-    if (targets) {
+    a.vote = (flags & BH_WALK_VOTE) != 0;
+    a.unsorted = (flags & BH_WALK_UNSORTED) != 0;
+    if (a.unsorted) {
+        a.self = targets == nullptr;
+        if (targets) {
+            a.tpos = (const float4 *)targets;
+            a.tmap = nullptr;
+        } else {
+            launch_invert(c->perm, nt, c->inv, s);
+            a.tpos = c->spos;
+            a.tmap = c->inv;
+        }
+    } else if (targets) {
         uint64_t *ko;
         uint32_t *vo;
         launch_morton((const float4 *)targets, nt, c->prm, c->bits, c->tkeys, c->tvals, s);
         radix_sort(c->tkeys, c->tvals, c->tkeys_alt, c->tvals_alt, &ko, &vo, nt, c->key_bits,
                    c->tspine, (const float4 *)targets, c->tpos, s);
         a.tpos = c->tpos;
-        a.tperm = vo;
+        a.tmap = vo;
         a.self = 0;
     } else {
         a.tpos = c->spos;
-        a.tperm = c->perm;
+        a.tmap = c->perm;
         a.self = 1;
     }
     record(c, 5, s);
@@ -260,7 +276,7 @@ static bh_status gravity_impl(bh_ctx *c, const float *targets, int64_t n_targets
 bh_status bh_gravity(bh_ctx *c, const float *targets, int64_t n_targets, float theta, float G,
                      float eps, float *out_acc_pot, void *stream)
 {
-    return gravity_impl(c, targets, n_targets, theta, G, eps, out_acc_pot, nullptr, stream);
+    return gravity_impl(c, targets, n_targets, theta, G, eps, 0u, out_acc_pot, nullptr, stream);
 }
 
 bh_status bh_gravity_counted(bh_ctx *c, const float *targets, int64_t n_targets, float theta,
@@ -268,7 +284,16 @@ bh_status bh_gravity_counted(bh_ctx *c, const float *targets, int64_t n_targets,
                              void *stream)
 {
     if (!interactions) return BH_ERR_INVALID;
-    return gravity_impl(c, targets, n_targets, theta, G, eps, out_acc_pot, interactions, stream);
+    return gravity_impl(c, targets, n_targets, theta, G, eps, 0u, out_acc_pot, interactions,
+                        stream);
+}
+
+bh_status bh_gravity_ex(bh_ctx *c, const float *targets, int64_t n_targets, float theta, float G,
+                        float eps, uint32_t flags, float *out_acc_pot, uint64_t *interactions,
+                        void *stream)
+{
+    return gravity_impl(c, targets, n_targets, theta, G, eps, flags, out_acc_pot, interactions,
+                        stream);
 }
 
 bh_status bh_direct(const float *src_pos_mass, int64_t n_src, const float *targets,

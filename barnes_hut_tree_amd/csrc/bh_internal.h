@@ -106,16 +106,20 @@ void build_tree(const uint64_t *keys_sorted, const float4 *spos, uint32_t n, int
 struct WalkArgs {
     const Node *nodes;
     const float4 *src;          // sources in Morton order
-    const float4 *tpos;         // targets in Morton order
-    const uint32_t *tperm;      // caller index of each sorted target
+    const float4 *tpos;         // target positions (Morton order, or as given when unsorted)
+    const uint32_t *tmap;       // sorted: caller index of each target; unsorted self: Morton rank
     const DevParams *prm;
     uint32_t n_targets;
     int self;                   // targets are the sources (exclude i == j)
+    int vote;                   // wave-wide vote instead of the per-lane walk
+    int unsorted;               // walk the targets in the caller's order
     float theta, G, eps;
     float4 *out;
     unsigned long long *count;  // optional interaction counter
 };
 void launch_walk(const WalkArgs &a, hipStream_t s);
+// inv[perm[k]] = k
+void launch_invert(const uint32_t *perm, uint32_t n, uint32_t *inv, hipStream_t s);
 void launch_fill_zero(float4 *out, uint32_t n, hipStream_t s);
 
 // direct.hip: all-pairs sum over the caller's sources (self: tgt is ignored,

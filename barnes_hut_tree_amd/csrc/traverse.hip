@@ -75,7 +75,7 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
 // ops directly, the node address is a 32-bit byte offset, and the lane masks
 // come straight from the comparisons.  The one scalar load per node is not
 // prefetched; the other waves on the SIMD cover its latency.
-template <bool SOFT, bool SELF, bool COUNT, bool EXACT_T>
+template <bool SOFT, bool SELF, bool COUNT, bool EXACT_T, bool ANY_MINE>
 __device__ __attribute__((always_inline)) inline void walk_wave(
     const Node *__restrict__ nodes, const float4 *__restrict__ src, uint32_t nn, float4 p,
     uint32_t i, uint32_t wave_base, bool valid, float T0, uint32_t T0_bits, uint32_t T_step,
@@ -126,7 +126,7 @@ __device__ __attribute__((always_inline)) inline void walk_wave(
             // lanes that opened a leaf sum its particles; a leaf holding some
             // of this wave's own targets needs the self pair removed
             const uint32_t b = hi.x, e = hi.x + hi.y;
-            if (SELF && b < wave_base + 64 && e > wave_base)
+            if (SELF && (ANY_MINE || (b < wave_base + 64 && e > wave_base)))
                 leaf_tile<SOFT, true>(src, b, e, i, p, eps2, ax, ay, az, pot);
             else
                 leaf_tile<SOFT, false>(src, b, e, i, p, eps2, ax, ay, az, pot);
@@ -138,11 +138,69 @@ __device__ __attribute__((always_inline)) inline void walk_wave(
     }
 }
 
-template <bool SOFT, bool SELF, bool COUNT>
+// The warp vote of [GASPHiA] 性能瓶颈分析, kept for comparison: the wave
+// moves as one, and when the opening test fails for any of its valid lanes,
+// every lane uses the node's children (or, for a leaf, its particles);
+// otherwise every lane uses the node whole.  Results then depend on which
+// targets share a wave; every lane sees at least the nodes of its own walk.
+template <bool SOFT, bool SELF, bool COUNT, bool EXACT_T, bool ANY_MINE>
+__device__ __attribute__((always_inline)) inline void walk_vote(
+    const Node *__restrict__ nodes, const float4 *__restrict__ src, uint32_t nn, float4 p,
+    uint32_t i, uint32_t wave_base, bool valid, float T0, uint32_t T0_bits, uint32_t T_step,
+    float eps2, float &ax, float &ay, float &az, float &pot, uint32_t &n_int)
+{
+    const char *node_bytes = reinterpret_cast<const char *>(nodes);
+    uint32_t X = 0;
+    while (X < nn) {
+        const uint4 *rec = reinterpret_cast<const uint4 *>(node_bytes + X * (uint32_t)sizeof(Node));
+        const uint4 lo = rec[0], hi = rec[1];
+        const float cx = __uint_as_float(lo.x), cy = __uint_as_float(lo.y);
+        const float cz = __uint_as_float(lo.z), m = __uint_as_float(lo.w);
+        const uint32_t skip = hi.z, meta = hi.w;
+        const uint32_t level = node_level(meta);
+        const float T = EXACT_T ? ldexpf(T0, -2 * (int)level)
+                                : __uint_as_float(sgpr(T0_bits - level * T_step));
+        const float dx = cx - p.x, dy = cy - p.y, dz = cz - p.z;
+        const float r2 = fmaf(dz, dz, fmaf(dy, dy, dx * dx));
+        if (__ballot(valid && !(T < r2)) == 0) {   // no lane opens: all use X whole
+            const float inv = __builtin_amdgcn_rsqf(r2 + eps2);
+            const float mi = m * inv;
+            const float f = mi * inv * inv;
+            ax = fmaf(f, dx, ax);
+            ay = fmaf(f, dy, ay);
+            az = fmaf(f, dz, az);
+            pot -= mi;
+            if (COUNT) ++n_int;
+            X = skip;
+            continue;
+        }
+        if (meta & kLeafBit) {   // every lane sums the leaf's particles
+            const uint32_t b = hi.x, e = hi.x + hi.y;
+            if (SELF && (ANY_MINE || (b < wave_base + 64 && e > wave_base)))
+                leaf_tile<SOFT, true>(src, b, e, i, p, eps2, ax, ay, az, pot);
+            else
+                leaf_tile<SOFT, false>(src, b, e, i, p, eps2, ax, ay, az, pot);
+            if (COUNT) n_int += (e - b) - ((SELF && i >= b && i < e) ? 1u : 0u);
+            X = skip;
+            continue;
+        }
+        X = X + 1;
+    }
+}
+
+// One wave per 64 consecutive targets of the walk order.  Sorted order (the
+// product path): lane position c is the target's Morton rank, its position
+// is tpos[c] and its result goes to tmap[c], the caller's index.  Unsorted
+// order (kept to measure what the Morton order of targets buys, [GASPHiA]
+// 排序算法): c is the caller's index and the output slot; for self-gravity
+// tmap[c] is the target's Morton rank, which locates it (tpos is then the
+// sorted sources) and identifies the self pair; separate targets are read
+// from tpos[c] as given.
+template <bool SOFT, bool SELF, bool COUNT, bool VOTE, bool UNSORTED>
 __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ nodes,
                                                        const float4 *__restrict__ src,
                                                        const float4 *__restrict__ tpos,
-                                                       const uint32_t *__restrict__ tperm,
+                                                       const uint32_t *__restrict__ tmap,
                                                        const DevParams *__restrict__ prm,
                                                        uint32_t n, float theta, float G,
                                                        float eps2, float4 *__restrict__ out,
@@ -151,12 +209,17 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t blk = xcd_block(blockIdx.x, gridDim.x);
     const uint32_t wave_base = blk * kWalkThreads + (threadIdx.x & ~63u);
-    const uint32_t i = wave_base + lane;
-    const bool valid = i < n;
+    const uint32_t c = wave_base + lane;
+    const bool valid = c < n;
     if (wave_base >= n) return;
+    uint32_t i = c, slot = c;   // self index (Morton rank) and output slot
+    if (valid) {
+        if (!UNSORTED) slot = tmap[c];
+        else if (SELF) i = tmap[c];
+    }
 
     if (prm->status != 0) {
-        if (valid) out[tperm[i]] = make_float4(NAN, NAN, NAN, NAN);
+        if (valid) out[slot] = make_float4(NAN, NAN, NAN, NAN);
         return;
     }
     const uint32_t nn = prm->n_nodes;
@@ -174,19 +237,39 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
 
     float ax = 0.f, ay = 0.f, az = 0.f, pot = 0.f;
     uint32_t n_int = 0;
-    if (exact)
-        walk_wave<SOFT, SELF, COUNT, true>(nodes, src, nn, p, i, wave_base, valid, T0, T0_bits,
-                                           T_step, eps2, ax, ay, az, pot, n_int);
-    else
-        walk_wave<SOFT, SELF, COUNT, false>(nodes, src, nn, p, i, wave_base, valid, T0, T0_bits,
-                                            T_step, eps2, ax, ay, az, pot, n_int);
-
-    if (valid) out[tperm[i]] = make_float4(G * ax, G * ay, G * az, G * pot);
-    if (COUNT) {
-        unsigned long long c = n_int;
-        for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
-        if (lane == 0) atomicAdd(count, c);
+    if (VOTE) {
+        if (exact)
+            walk_vote<SOFT, SELF, COUNT, true, UNSORTED>(nodes, src, nn, p, i, wave_base, valid, T0,
+                                                         T0_bits, T_step, eps2, ax, ay, az, pot,
+                                                         n_int);
+        else
+            walk_vote<SOFT, SELF, COUNT, false, UNSORTED>(nodes, src, nn, p, i, wave_base, valid,
+                                                          T0, T0_bits, T_step, eps2, ax, ay, az,
+                                                          pot, n_int);
+    } else {
+        if (exact)
+            walk_wave<SOFT, SELF, COUNT, true, UNSORTED>(nodes, src, nn, p, i, wave_base, valid, T0,
+                                                         T0_bits, T_step, eps2, ax, ay, az, pot,
+                                                         n_int);
+        else
+            walk_wave<SOFT, SELF, COUNT, false, UNSORTED>(nodes, src, nn, p, i, wave_base, valid,
+                                                          T0, T0_bits, T_step, eps2, ax, ay, az,
+                                                          pot, n_int);
     }
+
+    if (valid) out[slot] = make_float4(G * ax, G * ay, G * az, G * pot);
+    if (COUNT) {
+        unsigned long long cnt = valid ? n_int : 0u;
+        for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+        if (lane == 0) atomicAdd(count, cnt);
+    }
+}
+
+// inv[perm[k]] = k: the Morton rank of each caller index.
+__global__ void k_invert(const uint32_t *__restrict__ perm, uint32_t n, uint32_t *__restrict__ inv)
+{
+    const uint32_t k = blockIdx.x * blockDim.x + threadIdx.x;
+    if (k < n) inv[perm[k]] = k;
 }
 
 __global__ void k_fill_zero(float4 *out, uint32_t n)
@@ -195,13 +278,25 @@ __global__ void k_fill_zero(float4 *out, uint32_t n)
     if (i < n) out[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
+template <bool SOFT, bool SELF, bool COUNT, bool VOTE, bool UNSORTED>
+void launch5(const WalkArgs &a, hipStream_t s)
+{
+    const uint32_t grid = (a.n_targets + kWalkThreads - 1) / kWalkThreads;
+    hipLaunchKernelGGL((k_walk<SOFT, SELF, COUNT, VOTE, UNSORTED>), dim3(grid), dim3(kWalkThreads),
+                       0, s, a.nodes, a.src, a.tpos, a.tmap, a.prm, a.n_targets, a.theta, a.G,
+                       a.eps * a.eps, a.out, a.count);
+}
+
 template <bool SOFT, bool SELF, bool COUNT>
 void launch3(const WalkArgs &a, hipStream_t s)
 {
-    const uint32_t grid = (a.n_targets + kWalkThreads - 1) / kWalkThreads;
-    hipLaunchKernelGGL((k_walk<SOFT, SELF, COUNT>), dim3(grid), dim3(kWalkThreads), 0, s, a.nodes,
-                       a.src, a.tpos, a.tperm, a.prm, a.n_targets, a.theta, a.G, a.eps * a.eps,
-                       a.out, a.count);
+    if (a.vote) {
+        if (a.unsorted) launch5<SOFT, SELF, COUNT, true, true>(a, s);
+        else launch5<SOFT, SELF, COUNT, true, false>(a, s);
+    } else {
+        if (a.unsorted) launch5<SOFT, SELF, COUNT, false, true>(a, s);
+        else launch5<SOFT, SELF, COUNT, false, false>(a, s);
+    }
 }
 
 template <bool SOFT, bool SELF>
@@ -223,6 +318,12 @@ void launch_walk(const WalkArgs &a, hipStream_t s)
     if (a.n_targets == 0) return;
     // Plummer softening with eps^2 > 0 never meets r^2 + eps^2 == 0
     if (a.eps * a.eps > 0.f) launch1<true>(a, s); else launch1<false>(a, s);
+}
+
+void launch_invert(const uint32_t *perm, uint32_t n, uint32_t *inv, hipStream_t s)
+{
+    if (n == 0) return;
+    hipLaunchKernelGGL(k_invert, dim3((n + 255) / 256), dim3(256), 0, s, perm, n, inv);
 }
 
 void launch_fill_zero(float4 *out, uint32_t n, hipStream_t s)

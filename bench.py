@@ -170,6 +170,73 @@ def theta_sweep(args):
                       "direct_ms": round(direct_ms, 3), "rows": len(rows)}), flush=True)
 
 
+def ablations(args):
+    """The pages' design comparisons on MI355X, one JSON line each.
+
+    Target order ([GASPHiA] 排序算法 compares a random order, a regular lattice
+    order and the tree-sorted order on 1M particles): the 1M lattice walked in
+    the caller's order, shuffled and in lattice order, against the Morton-ordered
+    walk.  Warp vote ([GASPHiA] 性能瓶颈分析): the default workload with the
+    per-target walk and with the vote, time, interactions and accuracy against
+    the GPU direct sum."""
+    import numpy as np
+    import torch
+
+    import barnes_hut_tree_amd as bh
+    import workloads as W
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    theta, eps = 0.5, 1e-3
+    for shuffled in (True, False):
+        p = W.lattice(100, shuffled=shuffled, seed=2)
+        n = p.shape[0]
+        src = torch.from_numpy(p).cuda()
+        out = torch.empty((n, 4), dtype=torch.float32, device="cuda")
+        tree = bh.BarnesHut(n, 0, args.key_bits, args.leaf_cap)
+        tree.build(src)
+        tree.sync()
+        modes = [("caller_order", bh.WALK_UNSORTED)] + ([("morton_order", 0)] if shuffled else [])
+        for name, flags in modes:
+            ms = timed(lambda: tree.gravity(theta, 1.0, eps, out=out, flags=flags))
+            inter = tree.count_interactions(theta, eps, flags=flags)
+            print(json.dumps({"ablation": "target_order", "workload": "lattice_n1000000_" +
+                              ("shuffled" if shuffled else "lattice_order"), "walk": name,
+                              "theta": theta, "eps": eps, "walk_ms": round(ms, 3),
+                              "interactions": inter}), flush=True)
+        tree.close()
+
+    p, prm, wname = make_workload("plummer")
+    n = p.shape[0]
+    src = torch.from_numpy(p).cuda()
+    ref = bh.direct(src, prm["G"], prm["eps"]).double()
+    ref_n = ref[:, :3].norm(dim=1)
+    tree = bh.BarnesHut(n, 0, args.key_bits, args.leaf_cap)
+    tree.build(src)
+    out = torch.empty((n, 4), dtype=torch.float32, device="cuda")
+    for th in (0.3, 0.5, 0.7):
+        for name, flags in (("per_target", 0), ("vote", bh.WALK_VOTE)):
+            ms = timed(lambda: tree.gravity(th, prm["G"], prm["eps"], out=out, flags=flags))
+            inter = tree.count_interactions(th, prm["eps"], flags=flags)
+            err = ((out.double()[:, :3] - ref[:, :3]).norm(dim=1) / ref_n).cpu().numpy()
+            print(json.dumps({"ablation": "warp_vote", "workload": wname, "walk": name,
+                              "theta": th, "walk_ms": round(ms, 3), "interactions": inter,
+                              "interactions_per_s": inter / (ms * 1e-3),
+                              "median_rel_err": float(np.median(err)),
+                              "mean_rel_err": float(err.mean()), "max_rel_err": float(err.max())}),
+                  flush=True)
+    tree.close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,6 +249,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="theta sweep against the GPU direct sum instead of the step benchmark")
+    ap.add_argument("--ablations", action="store_true",
+                    help="the pages' design comparisons (target order, warp vote)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB (3 times), "
                          "the reference kernel for scaling HBM byte counters")
@@ -198,6 +267,9 @@ def main():
     torch.cuda.set_device(0)
     if args.sweep:
         theta_sweep(args)
+        return
+    if args.ablations:
+        ablations(args)
         return
 
     if args.copy_calibration_mib:

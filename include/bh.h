@@ -111,6 +111,27 @@ bh_status bh_gravity_counted(bh_ctx *ctx, const float *targets, int64_t n_target
                              float theta, float G, float eps, float *out_acc_pot,
                              uint64_t *interactions, void *stream);
 
+/* Walk variants for measuring the pages' design choices (flags, OR-ed):
+ *   BH_WALK_VOTE      the warp vote of [GASPHiA] 性能瓶颈分析: the 64 targets of a
+ *                     wave walk together, and when the opening test fails for any
+ *                     of them, every one of them uses the node's children (or,
+ *                     for a leaf, its particles).  Results depend on which
+ *                     targets share a wave (64 consecutive targets of the walk
+ *                     order) and are at least as accurate as the per-target walk.
+ *   BH_WALK_UNSORTED  walk the targets in the caller's order instead of their
+ *                     Morton order ([GASPHiA] 排序算法 measures what this order
+ *                     buys).  Without BH_WALK_VOTE the results are bit-identical
+ *                     to the default walk; only the speed changes. */
+#define BH_WALK_VOTE 1u
+#define BH_WALK_UNSORTED 2u
+
+/* bh_gravity with walk variant flags (0 = bh_gravity) and an optional
+ * interaction counter (NULL = none; else as bh_gravity_counted).  Unknown
+ * flag bits are rejected with BH_ERR_INVALID. */
+bh_status bh_gravity_ex(bh_ctx *ctx, const float *targets, int64_t n_targets, float theta,
+                        float G, float eps, uint32_t flags, float *out_acc_pot,
+                        uint64_t *interactions, void *stream);
+
 /* All-pairs direct sum, no tree and no context: every target against every
  * source with the interaction of bh_gravity.  This is the brute-force
  * reference that [GASPHiA] 精度与加速比验证 measures the walk's speed-up and
