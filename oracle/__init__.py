@@ -164,3 +164,47 @@ def direct(pos_mass, G=1.0, eps=0.0, targets=None, which=None):
 
 def threads():
     return lib().orc_threads()
+
+
+# ---------------------------------------------------------------------------
+# Time stepping.  The pages advance their 5M-particle galaxy collision in time
+# ([GASPHiA], page header) without naming the integrator; the reading taken is
+# the kick-drift-kick leapfrog with the tree rebuilt every step.  The state is
+# fp64; the tree of each step is built from the positions rounded to fp32,
+# the precision sources are given in.
+# ---------------------------------------------------------------------------
+def _forces(x, m, theta, G, eps, key_bits, leaf_cap):
+    p32 = np.concatenate([x, m[:, None]], axis=1).astype(np.float32)
+    out, _, _ = Tree(p32, key_bits, leaf_cap).gravity(theta, G, eps)
+    return out
+
+
+def leapfrog(pos_mass, vel, dt, steps, theta, G=1.0, eps=0.0, key_bits=63, leaf_cap=16):
+    """Kick-drift-kick leapfrog: per step v += a dt/2, x += v dt, a = a(x),
+    v += a dt/2.  pos_mass (n, 4): x, y, z, m; vel (n, >= 3).  Returns fp64
+    positions (n, 3), velocities (n, 3) and the last (n, 4) accelerations and
+    potentials."""
+    x = np.asarray(pos_mass, dtype=np.float64)[:, :3].copy()
+    m = np.asarray(pos_mass, dtype=np.float64)[:, 3].copy()
+    v = np.asarray(vel, dtype=np.float64)[:, :3].copy()
+    a = _forces(x, m, theta, G, eps, key_bits, leaf_cap)
+    for _ in range(steps):
+        v += 0.5 * dt * a[:, :3]
+        x += dt * v
+        a = _forces(x, m, theta, G, eps, key_bits, leaf_cap)
+        v += 0.5 * dt * a[:, :3]
+    return x, v, a
+
+
+def diagnostics(x, m, v, phi):
+    """Conserved quantities, by their definitions: total mass, kinetic energy
+    sum m v^2 / 2, potential energy sum m phi / 2 (phi: each particle's
+    potential from all others), momentum sum m v and angular momentum
+    sum m x cross v."""
+    x = np.asarray(x, np.float64)
+    v = np.asarray(v, np.float64)
+    m = np.asarray(m, np.float64)
+    phi = np.asarray(phi, np.float64)
+    return dict(mass=m.sum(), kinetic=0.5 * np.sum(m * np.sum(v * v, axis=1)),
+                potential=0.5 * np.sum(m * phi), momentum=(m[:, None] * v).sum(axis=0),
+                angular_momentum=(m[:, None] * np.cross(x, v)).sum(axis=0))
