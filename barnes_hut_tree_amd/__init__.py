@@ -26,7 +26,8 @@ BH_ERR_NOT_BUILT = -6
 WALK_VOTE = 1        # BH_WALK_VOTE
 WALK_UNSORTED = 2    # BH_WALK_UNSORTED
 
-EXPORTS = ("bh_create", "bh_build", "bh_gravity", "bh_gravity_counted", "bh_gravity_ex", "bh_direct", "bh_sync", "bh_destroy",
+EXPORTS = ("bh_create", "bh_build", "bh_gravity", "bh_gravity_counted", "bh_gravity_ex", "bh_direct", "bh_kick_drift",
+           "bh_leapfrog_step", "bh_diagnostics", "bh_sync", "bh_destroy",
            "bh_status_string", "bh_get_keys", "bh_get_node_count", "bh_get_nodes", "bh_get_bbox",
            "bh_set_profiling", "bh_get_profile")
 
@@ -65,6 +66,9 @@ def load_library():
         "bh_gravity_counted": [P, P, i64, f32, f32, f32, P, P, P],
         "bh_gravity_ex": [P, P, i64, f32, f32, f32, ctypes.c_uint32, P, P, P],
         "bh_direct": [P, i64, P, i64, f32, f32, P, P],
+        "bh_kick_drift": [P, P, P, i64, f32, f32, P],
+        "bh_leapfrog_step": [P, P, P, P, i64, f32, f32, f32, f32, P],
+        "bh_diagnostics": [P, P, P, P, i64, P, P],
         "bh_sync": [P],
         "bh_destroy": [P],
         "bh_get_keys": [P, P, P, P],
@@ -218,6 +222,36 @@ class BarnesHut:
                "bh_get_bbox")
         return list(lo), list(hi), L.value
 
+    def leapfrog_step(self, pos_mass, vel, acc_pot, dt, theta, G=1.0, eps=0.0):
+        """One kick-drift-kick step in place (bh_leapfrog_step); acc_pot must
+        hold the forces at the current positions."""
+        pos_mass = _rows(pos_mass, "pos_mass")
+        vel = _rows(vel, "vel")
+        acc_pot = _rows(acc_pot, "acc_pot")
+        n = pos_mass.shape[0]
+        if vel.shape[0] != n or acc_pot.shape[0] != n:
+            raise ValueError("pos_mass, vel and acc_pot need the same number of rows")
+        _check(load_library().bh_leapfrog_step(
+            self._h, ctypes.c_void_p(pos_mass.data_ptr()), ctypes.c_void_p(vel.data_ptr()),
+            ctypes.c_void_p(acc_pot.data_ptr()), n, float(dt), float(theta), float(G),
+            float(eps), _stream()), "bh_leapfrog_step")
+        self.n = n
+
+    def diagnostics(self, pos_mass, vel, acc_pot):
+        """dict of fp64 conserved quantities (bh_diagnostics); waits for them."""
+        import torch
+        pos_mass = _rows(pos_mass, "pos_mass")
+        vel = _rows(vel, "vel")
+        acc_pot = _rows(acc_pot, "acc_pot")
+        out = torch.empty(10, dtype=torch.float64, device="cuda")
+        _check(load_library().bh_diagnostics(
+            self._h, ctypes.c_void_p(pos_mass.data_ptr()), ctypes.c_void_p(vel.data_ptr()),
+            ctypes.c_void_p(acc_pot.data_ptr()), pos_mass.shape[0],
+            ctypes.c_void_p(out.data_ptr()), _stream()), "bh_diagnostics")
+        o = out.cpu().tolist()
+        return dict(mass=o[0], kinetic=o[1], potential=o[2], momentum=o[3:6],
+                    angular_momentum=o[6:9], count=o[9])
+
     def set_profiling(self, on=True):
         _check(load_library().bh_set_profiling(self._h, int(bool(on))), "bh_set_profiling")
 
@@ -248,6 +282,19 @@ def direct(src, G=1.0, eps=0.0, targets=None, out=None):
                                     float(G), float(eps), ctypes.c_void_p(out.data_ptr()),
                                     _stream()), "bh_direct")
     return out
+
+
+def kick_drift(pos_mass, vel, acc_pot, dt_kick, dt_drift):
+    """vel += acc dt_kick; pos += vel dt_drift, in place (bh_kick_drift)."""
+    vel = _rows(vel, "vel")
+    n = vel.shape[0]
+    pp = ctypes.c_void_p() if pos_mass is None else ctypes.c_void_p(_rows(pos_mass, "pos_mass")
+                                                                     .data_ptr())
+    ap = ctypes.c_void_p() if acc_pot is None else ctypes.c_void_p(_rows(acc_pot, "acc_pot")
+                                                                    .data_ptr())
+    _check(load_library().bh_kick_drift(pp, ctypes.c_void_p(vel.data_ptr()), ap, n,
+                                        float(dt_kick), float(dt_drift), _stream()),
+           "bh_kick_drift")
 
 
 def nodes_numpy(node_tensor):

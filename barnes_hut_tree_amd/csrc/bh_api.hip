@@ -30,6 +30,7 @@ struct bh_ctx {
     uint64_t *keys_sorted = nullptr;  // aliases keys or keys_alt after a build
     uint32_t *perm = nullptr;         // aliases vals or vals_alt after a build
     uint32_t *inv = nullptr;          // Morton rank of each caller index (unsorted walks)
+    double *diag = nullptr;           // partial sums of bh_diagnostics
     BuildScratch bw = {};
     Node *nodes = nullptr;
 
@@ -65,7 +66,7 @@ void free_all(bh_ctx *c)
     void *ptrs[] = {c->prm, c->bbox_part, c->keys, c->keys_alt, c->vals, c->vals_alt, c->spine,
                     c->spos, c->bw.dc, c->bw.tile_counts, c->bw.tile_sums, c->bw.tile_scan,
                     c->bw.first_node, c->bw.P, c->nodes, c->tkeys, c->tkeys_alt, c->tvals,
-                    c->tvals_alt, c->tspine, c->tpos, c->inv};
+                    c->tvals_alt, c->tspine, c->tpos, c->inv, c->diag};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
     if (c->host_prm) (void)hipHostFree(c->host_prm);
@@ -150,6 +151,7 @@ bh_status bh_create(bh_ctx **out, int64_t max_sources, int64_t max_targets,
     ok &= dalloc(&c->bw.P, ns + 1) == hipSuccess;
     ok &= dalloc(&c->nodes, (size_t)c->node_cap + 1) == hipSuccess;
     ok &= dalloc(&c->inv, ns) == hipSuccess;
+    ok &= dalloc(&c->diag, (size_t)kDiagMaxPartials * kDiagTerms) == hipSuccess;
     if (nt) {
         ok &= dalloc(&c->tkeys, nt) == hipSuccess;
         ok &= dalloc(&c->tkeys_alt, nt) == hipSuccess;
@@ -317,6 +319,53 @@ bh_status bh_direct(const float *src_pos_mass, int64_t n_src, const float *targe
     else
         launch_direct((const float4 *)src_pos_mass, (uint32_t)n_src, (const float4 *)targets, nt,
                       targets == nullptr, G, eps, (float4 *)out_acc_pot, s);
+    return launch_status();
+}
+
+bh_status bh_kick_drift(float *pos_mass, float *vel, const float *acc_pot, int64_t n,
+                        float dt_kick, float dt_drift, void *stream)
+{
+    if (n < 0 || n > kMaxCount || !__builtin_isfinite(dt_kick) || !__builtin_isfinite(dt_drift))
+        return BH_ERR_INVALID;
+    if (n == 0) return BH_OK;
+    if (!vel || !aligned16(vel)) return BH_ERR_INVALID;
+    if (dt_kick != 0.f && (!acc_pot || !aligned16(acc_pot))) return BH_ERR_INVALID;
+    if (dt_drift != 0.f && (!pos_mass || !aligned16(pos_mass))) return BH_ERR_INVALID;
+    launch_kick_drift((float4 *)pos_mass, (float4 *)vel, (const float4 *)acc_pot, (uint32_t)n,
+                      dt_kick, dt_drift, (hipStream_t)stream);
+    return launch_status();
+}
+
+bh_status bh_leapfrog_step(bh_ctx *c, float *pos_mass, float *vel, float *acc_pot, int64_t n,
+                           float dt, float theta, float G, float eps, void *stream)
+{
+    if (!c || n < 0 || n > c->max_src || !__builtin_isfinite(dt)) return BH_ERR_INVALID;
+    if (!(theta >= 0.f) || !(eps >= 0.f) || !__builtin_isfinite(G)) return BH_ERR_INVALID;
+    if (n > 0 && (!pos_mass || !vel || !acc_pot || !aligned16(pos_mass) || !aligned16(vel) ||
+                  !aligned16(acc_pot)))
+        return BH_ERR_INVALID;
+    hipStream_t s = (hipStream_t)stream;
+    const uint32_t un = (uint32_t)n;
+    launch_kick_drift((float4 *)pos_mass, (float4 *)vel, (const float4 *)acc_pot, un, 0.5f * dt,
+                      dt, s);
+    bh_status st = bh_build(c, pos_mass, n, stream);
+    if (st != BH_OK) return st;
+    st = gravity_impl(c, nullptr, n, theta, G, eps, 0u, acc_pot, nullptr, stream);
+    if (st != BH_OK) return st;
+    launch_kick_drift((float4 *)pos_mass, (float4 *)vel, (const float4 *)acc_pot, un, 0.5f * dt,
+                      0.f, s);
+    return launch_status();
+}
+
+bh_status bh_diagnostics(bh_ctx *c, const float *pos_mass, const float *vel,
+                         const float *acc_pot, int64_t n, double *out, void *stream)
+{
+    if (!c || n < 0 || n > kMaxCount || !out) return BH_ERR_INVALID;
+    if (n > 0 && (!pos_mass || !vel || !acc_pot || !aligned16(pos_mass) || !aligned16(vel) ||
+                  !aligned16(acc_pot)))
+        return BH_ERR_INVALID;
+    launch_diagnostics((const float4 *)pos_mass, (const float4 *)vel, (const float4 *)acc_pot,
+                       (uint32_t)n, c->diag, out, (hipStream_t)stream);
     return launch_status();
 }
 

@@ -122,6 +122,15 @@ void launch_walk(const WalkArgs &a, hipStream_t s);
 void launch_invert(const uint32_t *perm, uint32_t n, uint32_t *inv, hipStream_t s);
 void launch_fill_zero(float4 *out, uint32_t n, hipStream_t s);
 
+// integrate.hip: leapfrog kick/drift and conserved-quantity sums
+constexpr int kDiagTerms = 10;           // mass, kinetic, potential, p xyz, L xyz, count
+constexpr uint32_t kDiagMaxPartials = 1024;
+void launch_kick_drift(float4 *pos, float4 *vel, const float4 *acc, uint32_t n, float dt_kick,
+                       float dt_drift, hipStream_t s);
+uint32_t diag_partials(uint32_t n);
+void launch_diagnostics(const float4 *pos, const float4 *vel, const float4 *acc, uint32_t n,
+                        double *partials, double *out, hipStream_t s);
+
 // direct.hip: all-pairs sum over the caller's sources (self: tgt is ignored,
 // the sources are the targets and each excludes itself)
 void launch_direct(const float4 *src, uint32_t n, const float4 *tgt, uint32_t nt, bool self,

@@ -237,6 +237,48 @@ def ablations(args):
     tree.close()
 
 
+def leapfrog(args):
+    """Time stepping of the 5M galaxy pair ([GASPHiA] page header): kick-drift-
+    kick leapfrog with the tree rebuilt every step (bh_leapfrog_step), timed
+    over --steps steps after --warmup steps; the conserved quantities before
+    and after.  One JSON line."""
+    import numpy as np
+    import torch
+
+    import barnes_hut_tree_amd as bh
+    import workloads as W
+    p, v = W.galaxy_pair()
+    n = p.shape[0]
+    theta = 0.5 if args.theta is None else args.theta
+    eps, dt = 0.02, 0.05
+    tp = torch.from_numpy(p).cuda()
+    tv = torch.from_numpy(np.concatenate([v, np.zeros((n, 1), np.float32)], 1)).cuda()
+    tree = bh.BarnesHut(n, 0, args.key_bits, args.leaf_cap)
+    tree.build(tp)
+    ta = tree.gravity(theta, 1.0, eps)
+    for _ in range(args.warmup):
+        tree.leapfrog_step(tp, tv, ta, dt, theta, 1.0, eps)
+    d0 = tree.diagnostics(tp, tv, ta)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        tree.leapfrog_step(tp, tv, ta, dt, theta, 1.0, eps)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    d1 = tree.diagnostics(tp, tv, ta)
+    tree.sync()
+    e0, e1 = d0["kinetic"] + d0["potential"], d1["kinetic"] + d1["potential"]
+    print(json.dumps({
+        "leapfrog": "galaxy_pair_n5000000", "n": n, "theta": theta, "eps": eps, "dt": dt,
+        "steps": args.steps, "warmup_steps": args.warmup, "ms_per_step": round(ms, 3),
+        "energy_before": e0, "energy_after": e1, "rel_energy_change": (e1 - e0) / abs(e0),
+        "kinetic_before": d0["kinetic"], "kinetic_after": d1["kinetic"],
+        "momentum_before": d0["momentum"], "momentum_after": d1["momentum"],
+        "angular_momentum_before": d0["angular_momentum"],
+        "angular_momentum_after": d1["angular_momentum"]}), flush=True)
+    tree.close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -251,6 +293,8 @@ def main():
                     help="theta sweep against the GPU direct sum instead of the step benchmark")
     ap.add_argument("--ablations", action="store_true",
                     help="the pages' design comparisons (target order, warp vote)")
+    ap.add_argument("--leapfrog", action="store_true",
+                    help="time-step the 5M galaxy pair (kick-drift-kick, rebuild every step)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB (3 times), "
                          "the reference kernel for scaling HBM byte counters")
@@ -270,6 +314,9 @@ def main():
         return
     if args.ablations:
         ablations(args)
+        return
+    if args.leapfrog:
+        leapfrog(args)
         return
 
     if args.copy_calibration_mib:

@@ -149,6 +149,39 @@ bh_status bh_gravity_ex(bh_ctx *ctx, const float *targets, int64_t n_targets, fl
 bh_status bh_direct(const float *src_pos_mass, int64_t n_src, const float *targets,
                     int64_t n_targets, float G, float eps, float *out_acc_pot, void *stream);
 
+/* ---- time stepping ------------------------------------------------------
+ * The pages advance their 5M-particle galaxy collision in time ([GASPHiA],
+ * page header) without naming the integrator; these calls give the
+ * kick-drift-kick leapfrog, with the tree rebuilt every step.  Velocities are
+ * float4 rows (vx, vy, vz, unused), 16-byte aligned, in the order of the
+ * positions. */
+
+/* vel += acc_pot.xyz * dt_kick, then pos_mass.xyz += vel * dt_drift, per
+ * particle (the mass in pos_mass.w is untouched).  A zero dt skips its half:
+ * acc_pot may be NULL when dt_kick == 0, pos_mass when dt_drift == 0.  dt
+ * values must be finite.  Asynchronous; no context needed. */
+bh_status bh_kick_drift(float *pos_mass, float *vel, const float *acc_pot, int64_t n,
+                        float dt_kick, float dt_drift, void *stream);
+
+/* One leapfrog step of the n particles:
+ *   vel += a dt/2; pos += vel dt; bh_build(pos); a = bh_gravity(self);
+ *   vel += a dt/2.
+ * acc_pot must hold the accelerations and potentials at the current positions
+ * on entry (from bh_gravity or the previous step) and holds those at the new
+ * positions on return.  n <= max_sources.  Asynchronous; device errors of the
+ * build (non-finite positions) are reported by bh_sync as for bh_build. */
+bh_status bh_leapfrog_step(bh_ctx *ctx, float *pos_mass, float *vel, float *acc_pot, int64_t n,
+                           float dt, float theta, float G, float eps, void *stream);
+
+/* Conserved quantities of the state, summed in fp64 in a fixed order
+ * (deterministic), into out[10] (device): total mass, kinetic energy
+ * sum m |v|^2 / 2, potential energy sum m phi / 2 (phi = acc_pot.w, each
+ * particle's potential from all others, G included), momentum sum m v (3),
+ * angular momentum sum m x cross v (3), and the particle count.  Uses the
+ * context's scratch: calls on one context must not overlap.  Asynchronous. */
+bh_status bh_diagnostics(bh_ctx *ctx, const float *pos_mass, const float *vel,
+                         const float *acc_pot, int64_t n, double *out, void *stream);
+
 /* Wait for the context's last stream and return the device status word
  * (BH_OK, BH_ERR_NONFINITE or BH_ERR_CAPACITY).  Synchronous. */
 bh_status bh_sync(bh_ctx *ctx);
