@@ -47,6 +47,12 @@ def lib():
         L.orc_bh.argtypes = [P, P, P, i64, ctypes.c_double, ctypes.c_double, ctypes.c_double,
                              ctypes.c_int, P, P, P]
         L.orc_direct.argtypes = [P, i64, P, P, i64, ctypes.c_double, ctypes.c_double, P]
+        L.orc_philox4x32_10.argtypes = [P, P, P]
+        L.orc_target_order.restype = ctypes.c_int
+        L.orc_target_order.argtypes = [P, P, i64, P]
+        L.orc_sbh.restype = ctypes.c_int
+        L.orc_sbh.argtypes = [P, P, P, i64, P, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
+                              ctypes.c_double, ctypes.c_double, P, P, P]
         L.orc_bh_vote.restype = ctypes.c_int
         L.orc_bh_vote.argtypes = [P, i64, P, i64, ctypes.c_double, ctypes.c_double,
                                   ctypes.c_double, ctypes.c_int, P, P, P]
@@ -128,6 +134,37 @@ class Tree:
                      int(tie_mode), _ptr(out), _ptr(ni), _ptr(nties))
         return out, ni, nties
 
+    def target_order(self, targets):
+        """Stable Morton order of separate query points on this tree's root cube."""
+        q = _f4(targets)
+        order = np.zeros(q.shape[0], np.int64)
+        if lib().orc_target_order(self._h, _ptr(q), q.shape[0], _ptr(order)) != 0:
+            raise MemoryError("orc_target_order")
+        return order
+
+    def sbh(self, targets, d=2, samples=1, seed=0, G=1.0, eps=0.0, which=None, group=64):
+        """Stochastic Barnes-Hut estimate at separate query points (the tree
+        must have leaf capacity 1): (n, 4) fp64 ax, ay, az, phi averaged over
+        `samples`, the mean square of the per-sample potential, and the number
+        of roulette draws within 1e-5 of their probability per query.  Queries
+        share random numbers in groups of `group` consecutive queries of the
+        Morton order."""
+        q = _f4(targets)
+        rank = np.empty(q.shape[0], np.int64)
+        rank[self.target_order(q)] = np.arange(q.shape[0])
+        w = np.arange(q.shape[0], dtype=np.int64) if which is None else \
+            np.ascontiguousarray(which, dtype=np.int64)
+        grp = np.ascontiguousarray(rank[w] // group, dtype=np.int64)
+        out = np.zeros((w.shape[0], 4))
+        sq = np.zeros(w.shape[0])
+        near = np.zeros(w.shape[0], np.int64)
+        rc = lib().orc_sbh(self._h, _ptr(q), _ptr(w), w.shape[0], _ptr(grp), int(d),
+                           int(samples), int(seed) & 0xFFFFFFFFFFFFFFFF, float(G), float(eps),
+                           _ptr(out), _ptr(sq), _ptr(near))
+        if rc != 0:
+            raise ValueError("orc_sbh: bad arguments")
+        return out, sq, near
+
     def gravity_vote(self, theta, G=1.0, eps=0.0, group=64, groups=None, tie_mode=0):
         """Self-gravity by the warp vote over groups of `group` consecutive sorted
         sources: (n, 4) fp64 in the caller's order, interactions and near-ties
@@ -148,6 +185,15 @@ class Tree:
         else:
             members = np.concatenate([perm[k * group:(k + 1) * group] for k in g])
         return out, ni, nties, members
+
+
+def philox4x32_10(ctr, key):
+    """The four output words of Philox4x32-10 for a 4-word counter and 2-word key."""
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, np.uint32)
+    lib().orc_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
 
 
 def direct(pos_mass, G=1.0, eps=0.0, targets=None, which=None):

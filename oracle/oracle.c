@@ -557,6 +557,201 @@ int orc_bh_vote(const orc_tree *t, int64_t group, const int64_t *groups, int64_t
 }
 
 /* ------------------------------------------------------------------------ */
+/* Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and    */
+/* Shaw, "Parallel random numbers: as easy as 1, 2, 3" (SC 2011): ten rounds; */
+/* each multiplies counter words 0 and 2 by 0xD2511F53 and 0xCD9E8D57 (full  */
+/* 64-bit products), xors the high halves with words 1 and 3 and the key,    */
+/* and the key is bumped by 0x9E3779B9 and 0xBB67AE85 after every round.     */
+/* ------------------------------------------------------------------------ */
+void orc_philox4x32_10(const uint32_t *ctr, const uint32_t *key, uint32_t *out)
+{
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c1 = (uint32_t)p1;
+        c3 = (uint32_t)p0;
+        c0 = n0;
+        c2 = n2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+/* Separate query points are ordered by their Morton keys on the sources'   */
+/* root cube (the quantisation of step 2, clamped to the cube on both sides) */
+/* and stably sorted; consecutive runs of that order form the groups that    */
+/* share random numbers below.                                               */
+int orc_target_order(const orc_tree *t, const float *targets, int64_t nt, int64_t *order)
+{
+    uint64_t *keys = (uint64_t *)malloc((size_t)(nt > 0 ? nt : 1) * sizeof(uint64_t));
+    if (!keys) return -2;
+    const uint64_t top = ((uint64_t)1 << t->bits) - 1;
+    const double S = (t->L > 0.0) ? ldexp(1.0, t->bits) / t->L : 0.0;
+    for (int64_t i = 0; i < nt; ++i) {
+        uint64_t key = 0;
+        for (int a = 0; a < 3; ++a) {
+            double f = floor(((double)targets[4 * i + a] - t->lo[a]) * S);
+            uint64_t qa = !(f >= 0.0) ? 0 : (f >= (double)top) ? top : (uint64_t)f;
+            for (int k = 0; k < t->bits; ++k) key |= ((qa >> k) & 1u) << (3 * k + a);
+        }
+        keys[i] = key;
+        order[i] = i;
+    }
+    g_sort_keys = keys;
+    qsort(order, (size_t)nt, sizeof(int64_t), cmp_by_key_then_index);
+    free(keys);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Stochastic Barnes-Hut ([SBH] 方法, 关键设计).  Each source's contribution  */
+/* is written as a telescoping sum along its root-to-leaf path, every step   */
+/* replacing a cell's monopole by its children's.  A sample picks a path     */
+/* index I uniformly among the sources and a path length by Russian roulette */
+/* (continuing from depth k with probability                                 */
+/* p_k = min(1, max(1, b_k) / b_{k+1}), b = |q - centre of mass| / box edge), */
+/* and adds for each step taken the exchange term                            */
+/*   Delta_T = sum over children c of m_c f(c, q) - m_T f(T, q)              */
+/* divided by P(I in T) * P(K >= k).  Strata: the children of the root, one  */
+/* path per stratum with I uniform over its sources, plus each stratum's     */
+/* monopole.  Readings: the tree is the octree with single-source leaves     */
+/* (B = 1; a leaf of coincident sources at the finest level has Delta = 0    */
+/* and ends the path); branching d = 2 per axis steps one octree level, d = 4 */
+/* two (a child that is a leaf stands for itself); the random numbers are    */
+/* shared by a group of consecutive targets (the same seed across a warp),   */
+/* drawn from Philox4x32-10 with key = seed and counter = (group, sample,    */
+/* stratum, j), j = 0 for the path index and j = k + 1 for the roulette at   */
+/* depth k; I = start + floor(r * count / 2^32) on the first output word r,  */
+/* u = (r >> 8) 2^-24.  S samples are averaged.                              */
+/* ------------------------------------------------------------------------ */
+static int64_t dchildren(const orc_tree *t, int64_t c, int d, int64_t *out)
+{
+    const orc_cell *cell = &t->cells[c];
+    int64_t n = 0;
+    for (int o = 0; o < 8; ++o) {
+        const int64_t ch = cell->child[o];
+        if (ch < 0) continue;
+        if (d == 2 || t->cells[ch].is_leaf) {
+            out[n++] = ch;
+            continue;
+        }
+        for (int o2 = 0; o2 < 8; ++o2)
+            if (t->cells[ch].child[o2] >= 0) out[n++] = t->cells[ch].child[o2];
+    }
+    return n;
+}
+
+static void kernel_f(const double *q, double m, const double *p, double eps_sq, double *f)
+{
+    double d[3], r2 = eps_sq;
+    for (int a = 0; a < 3; ++a) {
+        d[a] = p[a] - q[a];
+        r2 += d[a] * d[a];
+    }
+    if (r2 == 0.0) {
+        f[0] = f[1] = f[2] = f[3] = 0.0;
+        return;
+    }
+    const double inv = 1.0 / sqrt(r2);
+    for (int a = 0; a < 3; ++a) f[a] = m * d[a] * inv * inv * inv;
+    f[3] = -m * inv;
+}
+
+static double far_ratio(const orc_tree *t, const orc_cell *c, const double *q)
+{
+    double r2 = 0.0;
+    for (int a = 0; a < 3; ++a) {
+        double d = q[a] - c->com[a];
+        r2 += d * d;
+    }
+    return sqrt(r2) / ldexp(t->L, -c->level);
+}
+
+int orc_sbh(const orc_tree *t, const float *targets, const int64_t *which, int64_t nt,
+            const int64_t *group, int d, int samples, uint64_t seed, double G, double eps,
+            double *out, double *pot_sq, int64_t *n_near)
+{
+    if ((d != 2 && d != 4) || samples < 1) return -1;
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    const double eps_sq = eps * eps;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t k = 0; k < nt; ++k) {
+        const int64_t i = which ? which[k] : k;
+        const double q[3] = {(double)targets[4 * i], (double)targets[4 * i + 1],
+                             (double)targets[4 * i + 2]};
+        double sum[4] = {0.0, 0.0, 0.0, 0.0}, sq = 0.0, f[4];
+        int64_t near = 0;
+        int64_t strata[64], kids[64];
+        int64_t n_strata = 0;
+        if (t->n_cells > 0 && !t->cells[0].is_leaf) n_strata = dchildren(t, 0, d, strata);
+        for (int s = 0; s < samples; ++s) {
+            double est[4] = {0.0, 0.0, 0.0, 0.0};
+            if (t->n_cells > 0 && t->cells[0].is_leaf) {   /* one leaf: the exact sum */
+                const orc_cell *leaf = &t->cells[0];
+                for (int64_t j = 0; j < leaf->count; ++j) {
+                    const int64_t p = t->idx[leaf->off + j];
+                    const double xs[3] = {t->src[4 * p], t->src[4 * p + 1], t->src[4 * p + 2]};
+                    kernel_f(q, (double)t->src[4 * p + 3], xs, eps_sq, f);
+                    for (int a = 0; a < 4; ++a) est[a] += f[a];
+                }
+            }
+            for (int64_t ci = 0; ci < n_strata; ++ci) {
+                const orc_cell *c = &t->cells[strata[ci]];
+                kernel_f(q, c->mass, c->com, eps_sq, f);
+                for (int a = 0; a < 4; ++a) est[a] += f[a];
+                if (c->is_leaf) continue;
+                uint32_t ctr[4] = {(uint32_t)group[k], (uint32_t)s, (uint32_t)ci, 0u}, r[4];
+                orc_philox4x32_10(ctr, key, r);
+                const int64_t I = c->off + (int64_t)(((uint64_t)r[0] * (uint64_t)c->count) >> 32);
+                int64_t T = strata[ci];
+                double w = 1.0;
+                for (uint32_t depth = 0; !t->cells[T].is_leaf; ++depth) {
+                    const orc_cell *cell = &t->cells[T];
+                    const int64_t nk = dchildren(t, T, d, kids);
+                    int64_t next = -1;
+                    for (int64_t j = 0; j < nk; ++j) {
+                        const orc_cell *ch = &t->cells[kids[j]];
+                        if (I >= ch->off && I < ch->off + ch->count) next = kids[j];
+                    }
+                    const double b0 = far_ratio(t, cell, q);
+                    const double b1 = far_ratio(t, &t->cells[next], q);
+                    const double pk = (b1 > 0.0) ? fmin(1.0, fmax(1.0, b0) / b1) : 1.0;
+                    ctr[3] = depth + 1;
+                    orc_philox4x32_10(ctr, key, r);
+                    const double u = ldexp((double)(r[0] >> 8), -24);
+                    if (fabs(u - pk) <= 1e-5) near++;
+                    if (!(u < pk)) break;
+                    w /= pk;
+                    const double scale = w * (double)c->count / (double)cell->count;
+                    for (int64_t j = 0; j < nk; ++j) {
+                        const orc_cell *ch = &t->cells[kids[j]];
+                        kernel_f(q, ch->mass, ch->com, eps_sq, f);
+                        for (int a = 0; a < 4; ++a) est[a] += scale * f[a];
+                    }
+                    kernel_f(q, cell->mass, cell->com, eps_sq, f);
+                    for (int a = 0; a < 4; ++a) est[a] -= scale * f[a];
+                    T = next;
+                }
+            }
+            for (int a = 0; a < 4; ++a) sum[a] += est[a];
+            sq += est[3] * est[3];
+        }
+        for (int a = 0; a < 4; ++a) out[4 * k + a] = G * sum[a] / samples;
+        if (pot_sq) pot_sq[k] = G * G * sq / samples;
+        if (n_near) n_near[k] = near;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Direct sum, the plain definition the tree approximates ([GASPHiA]          */
 /* 如何计算自引力: every pair of particles attracts; O(N^2)):                   */
 /*   a_i = G sum_{j != i} m_j d_ij / (|d_ij|^2 + eps^2)^(3/2),                */

@@ -472,3 +472,83 @@ def test_vote_is_more_accurate_than_the_per_particle_walk(orc):
     e_ref = np.linalg.norm(ref[:, :3] - d[:, :3], axis=1) / dn
     e_v = np.linalg.norm(out[:, :3] - d[:, :3], axis=1) / dn
     assert np.median(e_v) < 0.5 * np.median(e_ref)
+
+
+# ---------------------------------------------------------------------------
+# stochastic Barnes-Hut ([SBH] 方法, 关键设计) and its random numbers
+# ---------------------------------------------------------------------------
+def test_philox_known_answers(orc):
+    path = os.path.join(os.path.dirname(__file__), "golden", "philox4x32_10_kat.txt")
+    rows = [line.split() for line in open(path) if line.strip() and not line.startswith("#")]
+    assert len(rows) == 3
+    for r in rows:
+        w = [int(x, 16) for x in r]
+        assert orc.philox4x32_10(w[:4], w[4:6]).tolist() == w[6:10]
+
+
+def test_target_order_matches_source_order_and_clamps(orc):
+    p = W.plummer(3000, seed=31)
+    t = orc.Tree(p)
+    assert np.array_equal(t.target_order(p), t.perm())
+    lo, hi, L = t.bbox()
+    top = lo + L   # the root cube's upper corner
+    q = f4([lo - 1.0, top + 1.0, lo, top], 0.0)   # below, above, at the two corners
+    order = t.target_order(q)
+    # below the cube and at its low corner both quantise to key 0, above and
+    # at the high corner to the top key: the stable order is 0, 2, 1, 3
+    assert order.tolist() == [0, 2, 1, 3]
+
+
+def test_sbh_exact_cases(orc):
+    # one source: the estimate is the exact pair term for any seed
+    p = f4([[0.3, -0.2, 0.7]], 2.5)
+    q = f4([[1.0, 1.0, 1.0], [-2.0, 0.5, 0.0]], 0.0)
+    d = orc.direct(p, 1.0, 0.0, targets=q)
+    for seed in (1, 2):
+        out, _, _ = orc.Tree(p, leaf_cap=1).sbh(q, d=2, seed=seed)
+        assert np.allclose(out, d, rtol=1e-14, atol=0)
+    # one source per octant of the root: every stratum is a leaf, so the
+    # estimate is the exact sum
+    g = np.array([[x, y, z] for z in (0.1, 0.9) for y in (0.2, 0.8) for x in (0.15, 0.85)])
+    p = f4(g, np.arange(1, 9) / 8.0)
+    q = f4([[0.5, 0.5, 0.5], [2.0, -1.0, 0.3]], 0.0)
+    d = orc.direct(p, 1.3, 0.0, targets=q)
+    for dd in (2, 4):
+        out, _, _ = orc.Tree(p, leaf_cap=1).sbh(q, d=dd, seed=9, G=1.3)
+        assert np.allclose(out, d, rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("d", [2, 4])
+def test_sbh_is_unbiased(orc, d):
+    src = W.surface_sources(1 << 11, seed=12)
+    rng = np.random.default_rng(32)
+    q = f4(rng.uniform(-1, 1, (8, 3)), 0.0)
+    exact = orc.direct(src, 1.0, 0.0, targets=q)
+    t = orc.Tree(src, leaf_cap=1)
+    S = 20000
+    out, sq, _ = t.sbh(q, d=d, samples=S, seed=77)
+    se = np.sqrt(np.maximum(sq - out[:, 3] ** 2, 0.0) / S)
+    z = (out[:, 3] - exact[:, 3]) / se
+    assert np.all(np.abs(z) < 4.5), z
+    assert np.all(se > 0)
+    # the acceleration is estimated on the same paths: close to exact on average
+    rel = np.linalg.norm(out[:, :3] - exact[:, :3], axis=1) / np.linalg.norm(exact[:, :3], axis=1)
+    assert np.median(rel) < 0.02
+
+
+def test_sbh_far_field_is_nearly_exact(orc):
+    src = W.surface_sources(1 << 11, seed=13)
+    q = f4([[40.0, -30.0, 25.0], [-60.0, 5.0, 10.0]], 0.0)
+    exact = orc.direct(src, 1.0, 0.0, targets=q)
+    out, _, _ = orc.Tree(src, leaf_cap=1).sbh(q, d=2, seed=5)
+    assert np.max(np.abs(out[:, 3] / exact[:, 3] - 1.0)) < 1e-4
+
+
+def test_sbh_group_shares_random_numbers(orc):
+    src = W.surface_sources(1 << 10, seed=14)
+    q = f4(np.repeat([[0.1, 0.2, 0.3]], 3, axis=0), 0.0)
+    out, _, _ = orc.Tree(src, leaf_cap=1).sbh(q, d=2, seed=3)
+    assert np.array_equal(out[0], out[1]) and np.array_equal(out[0], out[2])
+    # queries one group apart draw other numbers
+    out2, _, _ = orc.Tree(src, leaf_cap=1).sbh(q, d=2, seed=3, group=1)
+    assert not np.array_equal(out2[0], out2[1])

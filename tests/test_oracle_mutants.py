@@ -47,6 +47,13 @@ MUTANTS = [
      "if (!accept) any_open += 1;\n    }\n    any_open = any_open == g->m;"),
     ("vote_leaf_self_kept", "            int64_t p = t->idx[cell->off + q];\n            if (p == w->self) continue;",
      "            int64_t p = t->idx[cell->off + q];"),
+    ("sbh_no_count_ratio", "const double scale = w * (double)c->count / (double)cell->count;",
+     "const double scale = w;"),
+    ("sbh_no_roulette_weight", "w /= pk;", "w /= 1.0;"),
+    ("sbh_exchange_sign", "est[a] -= scale * f[a];", "est[a] += scale * f[a];"),
+    ("sbh_roulette_inverted", "if (!(u < pk)) break;", "if (u < pk) break;"),
+    ("philox_multiplier", "(uint64_t)0xD2511F53u * c0", "(uint64_t)0xD2511F55u * c0"),
+    ("target_clamp_low", "uint64_t qa = !(f >= 0.0) ? 0 :", "uint64_t qa = !(f >= 0.0) ? top :"),
     ("vote_leaf_monopole", "            interact(&g->w[k], cell->mass, cell->com);",
      "            interact(&g->w[k], cell->mass, g->w[k].x);"),
 ]
