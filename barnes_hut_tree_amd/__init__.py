@@ -26,7 +26,7 @@ BH_ERR_NOT_BUILT = -6
 WALK_VOTE = 1        # BH_WALK_VOTE
 WALK_UNSORTED = 2    # BH_WALK_UNSORTED
 
-EXPORTS = ("bh_create", "bh_build", "bh_gravity", "bh_gravity_counted", "bh_gravity_ex", "bh_direct", "bh_kick_drift",
+EXPORTS = ("bh_create", "bh_build", "bh_gravity", "bh_gravity_counted", "bh_gravity_ex", "bh_sbh", "bh_direct", "bh_kick_drift",
            "bh_leapfrog_step", "bh_diagnostics", "bh_sync", "bh_destroy",
            "bh_status_string", "bh_get_keys", "bh_get_node_count", "bh_get_nodes", "bh_get_bbox",
            "bh_set_profiling", "bh_get_profile")
@@ -65,6 +65,7 @@ def load_library():
         "bh_gravity": [P, P, i64, f32, f32, f32, P, P],
         "bh_gravity_counted": [P, P, i64, f32, f32, f32, P, P, P],
         "bh_gravity_ex": [P, P, i64, f32, f32, f32, ctypes.c_uint32, P, P, P],
+        "bh_sbh": [P, P, i64, ctypes.c_int, ctypes.c_int, ctypes.c_uint64, f32, f32, P, P],
         "bh_direct": [P, i64, P, i64, f32, f32, P, P],
         "bh_kick_drift": [P, P, P, i64, f32, f32, P],
         "bh_leapfrog_step": [P, P, P, P, i64, f32, f32, f32, f32, P],
@@ -176,6 +177,24 @@ class BarnesHut:
                                       ctypes.c_void_p(out.data_ptr()),
                                       ctypes.c_void_p(interactions.data_ptr()), _stream())
         _check(st, "bh_gravity")
+        return out
+
+    def sbh(self, targets, d=2, samples=1, seed=0, G=1.0, eps=0.0, out=None):
+        """Stochastic Barnes-Hut estimate at separate targets (bh_sbh; the
+        context needs leaf_cap=1): (n_targets, 4) float32 in the caller's order."""
+        import torch
+        targets = _rows(targets, "targets")
+        nt = targets.shape[0]
+        if out is None:
+            out = torch.empty((nt, 4), dtype=torch.float32, device="cuda")
+        else:
+            _rows(out, "out")
+        if nt == 0:
+            return out
+        _check(load_library().bh_sbh(self._h, ctypes.c_void_p(targets.data_ptr()), nt, int(d),
+                                     int(samples), int(seed) & 0xFFFFFFFFFFFFFFFF, float(G),
+                                     float(eps), ctypes.c_void_p(out.data_ptr()), _stream()),
+               "bh_sbh")
         return out
 
     def count_interactions(self, theta, eps=0.0, targets=None, flags=0):

@@ -211,6 +211,19 @@ bh_status bh_build(bh_ctx *c, const float *src_pos_mass, int64_t n, void *stream
     return BH_OK;
 }
 
+// Morton keys of separate targets on the sources' root cube (clamped), their
+// stable sort, and the sorted copy in c->tpos; returns the caller index of each
+// sorted target.
+static const uint32_t *sort_targets(bh_ctx *c, const float *targets, uint32_t nt, hipStream_t s)
+{
+    uint64_t *ko;
+    uint32_t *vo;
+    launch_morton((const float4 *)targets, nt, c->prm, c->bits, c->tkeys, c->tvals, s);
+    radix_sort(c->tkeys, c->tvals, c->tkeys_alt, c->tvals_alt, &ko, &vo, nt, c->key_bits,
+               c->tspine, (const float4 *)targets, c->tpos, s);
+    return vo;
+}
+
 static bh_status gravity_impl(bh_ctx *c, const float *targets, int64_t n_targets, float theta,
                               float G, float eps, uint32_t flags, float *out, uint64_t *count,
                               void *stream)
@@ -256,13 +269,8 @@ static bh_status gravity_impl(bh_ctx *c, const float *targets, int64_t n_targets
             a.tmap = c->inv;
         }
     } else if (targets) {
-        uint64_t *ko;
-        uint32_t *vo;
-        launch_morton((const float4 *)targets, nt, c->prm, c->bits, c->tkeys, c->tvals, s);
-        radix_sort(c->tkeys, c->tvals, c->tkeys_alt, c->tvals_alt, &ko, &vo, nt, c->key_bits,
-                   c->tspine, (const float4 *)targets, c->tpos, s);
         a.tpos = c->tpos;
-        a.tmap = vo;
+        a.tmap = sort_targets(c, targets, nt, s);
         a.self = 0;
     } else {
         a.tpos = c->spos;
@@ -319,6 +327,41 @@ bh_status bh_direct(const float *src_pos_mass, int64_t n_src, const float *targe
     else
         launch_direct((const float4 *)src_pos_mass, (uint32_t)n_src, (const float4 *)targets, nt,
                       targets == nullptr, G, eps, (float4 *)out_acc_pot, s);
+    return launch_status();
+}
+
+bh_status bh_sbh(bh_ctx *c, const float *targets, int64_t n_targets, int d, int samples,
+                 uint64_t seed, float G, float eps, float *out_acc_pot, void *stream)
+{
+    if (!c) return BH_ERR_INVALID;
+    if (!c->built) return BH_ERR_NOT_BUILT;
+    if (c->leaf_cap != 1 || (d != 2 && d != 4) || samples < 1) return BH_ERR_INVALID;
+    if (n_targets < 0 || n_targets > c->max_tgt || !(eps >= 0.f) || !__builtin_isfinite(G))
+        return BH_ERR_INVALID;
+    if (n_targets > 0 && (!targets || !out_acc_pot || !aligned16(targets) ||
+                          !aligned16(out_acc_pot)))
+        return BH_ERR_INVALID;
+    hipStream_t s = (hipStream_t)stream;
+    c->last_stream = s;
+    const uint32_t nt = (uint32_t)n_targets;
+    if (nt == 0) return BH_OK;
+    if (c->n_src == 0) {
+        launch_fill_zero((float4 *)out_acc_pot, nt, s);
+        return launch_status();
+    }
+    SbhArgs a;
+    a.nodes = c->nodes;
+    a.tperm = sort_targets(c, targets, nt, s);
+    a.tpos = c->tpos;
+    a.prm = c->prm;
+    a.n_targets = nt;
+    a.d = d;
+    a.samples = samples;
+    a.seed = seed;
+    a.G = G;
+    a.eps = eps;
+    a.out = (float4 *)out_acc_pot;
+    launch_sbh(a, s);
     return launch_status();
 }
 

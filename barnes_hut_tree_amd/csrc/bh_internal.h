@@ -122,6 +122,21 @@ void launch_walk(const WalkArgs &a, hipStream_t s);
 void launch_invert(const uint32_t *perm, uint32_t n, uint32_t *inv, hipStream_t s);
 void launch_fill_zero(float4 *out, uint32_t n, hipStream_t s);
 
+// sbh.hip: stochastic Barnes-Hut at separate targets (sorted; leaf capacity 1)
+struct SbhArgs {
+    const Node *nodes;
+    const float4 *tpos;         // targets in Morton order
+    const uint32_t *tperm;      // caller index of each sorted target
+    const DevParams *prm;
+    uint32_t n_targets;
+    int d;                      // 2 or 4
+    int samples;
+    uint64_t seed;
+    float G, eps;
+    float4 *out;
+};
+void launch_sbh(const SbhArgs &a, hipStream_t s);
+
 // integrate.hip: leapfrog kick/drift and conserved-quantity sums
 constexpr int kDiagTerms = 10;           // mass, kinetic, potential, p xyz, L xyz, count
 constexpr uint32_t kDiagMaxPartials = 1024;

@@ -132,6 +132,29 @@ bh_status bh_gravity_ex(bh_ctx *ctx, const float *targets, int64_t n_targets, fl
                         float G, float eps, uint32_t flags, float *out_acc_pot,
                         uint64_t *interactions, void *stream);
 
+/* Stochastic Barnes-Hut ([SBH] 方法, 关键设计): an unbiased Monte-Carlo estimate
+ * of the sum at separate query points, on the context's tree, which must be
+ * built with leaf_cap = 1 (paths end at single sources).  Per sample, one path
+ * per stratum (the children of the root in the d-ary tree): the path index I
+ * is uniform over the stratum's sources, the path length is set by Russian
+ * roulette with continuation probability min(1, max(1, b_k) / b_{k+1}),
+ * b = |q - centre of mass| / cell edge, and each step adds the children's
+ * monopoles minus the cell's, divided by P(I in cell) P(K >= k).
+ *   d        2: one octree level per step; 4: two (a leaf child stands for itself).
+ *   samples  S >= 1 samples are averaged.
+ *   seed     Philox4x32-10 key (low, high word); counter = (group, sample,
+ *            stratum, j), j = 0 for I, j = k + 1 for the roulette at depth k;
+ *            a group is the 64 consecutive queries of the queries' Morton
+ *            order, which share their random numbers (so a wave follows one
+ *            path).  I = start + floor(r count / 2^32) and u = (r >> 8) 2^-24 from
+ *            the first output word r.
+ *   targets  device, n_targets float4 rows (w ignored), at most max_targets.
+ *   out_acc_pot as for bh_gravity.
+ * Errors: BH_ERR_INVALID (leaf_cap != 1, bad d or samples, bad arguments),
+ * BH_ERR_NOT_BUILT.  Asynchronous. */
+bh_status bh_sbh(bh_ctx *ctx, const float *targets, int64_t n_targets, int d, int samples,
+                 uint64_t seed, float G, float eps, float *out_acc_pot, void *stream);
+
 /* All-pairs direct sum, no tree and no context: every target against every
  * source with the interaction of bh_gravity.  This is the brute-force
  * reference that [GASPHiA] 精度与加速比验证 measures the walk's speed-up and
