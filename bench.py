@@ -279,6 +279,74 @@ def leapfrog(args):
     tree.close()
 
 
+def sbh_compare(args):
+    """Stochastic Barnes-Hut against the per-target Barnes-Hut walk at separate
+    query points ([SBH] 实验结果's table): sources on 3-6 spheres and tori
+    (area weights), M = 2^15, 2^17, 2^20, 10^6 queries on a 100^3 grid or
+    uniform in [-1, 1]^3, G = 1, eps = 0, potential errors against the GPU
+    direct sum, 8 source seeds (10-17), mean and spread over the seeds.  BH:
+    theta = 0.5 (far-field ratio 2), leaf capacity 16; SBH: S = 1 sample per
+    stratum, leaf capacity 1, d = 4 and d = 2.  Times are device times of the
+    query call (the target ordering included), mean of 5; the build is listed
+    apart.  One JSON line per (M, queries, method)."""
+    import numpy as np
+    import torch
+
+    import barnes_hut_tree_amd as bh
+    import workloads as W
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    seeds = list(range(10, 18))
+    sizes = [1 << 15, 1 << 17, 1 << 20]
+    qsets = {"grid100": W.grid_queries(), "uniform1e6": W.box_queries()}
+    for qname, qa in qsets.items():
+        q = torch.from_numpy(qa).cuda()
+        nq = q.shape[0]
+        out = torch.empty((nq, 4), dtype=torch.float32, device="cuda")
+        for m in sizes:
+            res = {k: [] for k in ("bh", "sbh_d4", "sbh_d2")}
+            for sd in seeds:
+                src = torch.from_numpy(W.surface_sources(m, seed=sd)).cuda()
+                exact = bh.direct(src, 1.0, 0.0, targets=q)[:, 3].double()
+                t16 = bh.BarnesHut(m, nq, args.key_bits, 16)
+                build16 = timed(lambda: t16.build(src))
+                ms = timed(lambda: t16.gravity(0.5, 1.0, 0.0, targets=q, out=out))
+                err = (out[:, 3].double() - exact).abs()
+                res["bh"].append((ms, build16, err))
+                t16.close()
+                t1 = bh.BarnesHut(m, nq, args.key_bits, 1)
+                build1 = timed(lambda: t1.build(src))
+                for d in (4, 2):
+                    ms = timed(lambda: t1.sbh(q, d=d, samples=1, seed=sd, out=out))
+                    err = (out[:, 3].double() - exact).abs()
+                    res["sbh_d%d" % d].append((ms, build1, err))
+                t1.close()
+            for meth, rows in res.items():
+                ms = np.array([r[0] for r in rows])
+                bms = np.array([r[1] for r in rows])
+                mean = np.array([float(r[2].mean()) for r in rows])
+                med = np.array([float(r[2].median()) for r in rows])
+                mx = np.array([float(r[2].max()) for r in rows])
+                print(json.dumps({
+                    "compare": "sbh_vs_bh", "sources": "surfaces", "m": m, "queries": qname,
+                    "method": meth, "seeds": len(seeds),
+                    "ms_mean": round(float(ms.mean()), 4), "ms_sd": round(float(ms.std()), 4),
+                    "build_ms_mean": round(float(bms.mean()), 4),
+                    "mean_abs_err": [float(mean.mean()), float(mean.std())],
+                    "median_abs_err": [float(med.mean()), float(med.std())],
+                    "max_abs_err": [float(mx.mean()), float(mx.std())]}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -295,6 +363,8 @@ def main():
                     help="the pages' design comparisons (target order, warp vote)")
     ap.add_argument("--leapfrog", action="store_true",
                     help="time-step the 5M galaxy pair (kick-drift-kick, rebuild every step)")
+    ap.add_argument("--sbh", action="store_true",
+                    help="stochastic Barnes-Hut vs the tree walk at separate query points")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB (3 times), "
                          "the reference kernel for scaling HBM byte counters")
@@ -317,6 +387,9 @@ def main():
         return
     if args.leapfrog:
         leapfrog(args)
+        return
+    if args.sbh:
+        sbh_compare(args)
         return
 
     if args.copy_calibration_mib:
