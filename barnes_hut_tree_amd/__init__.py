@@ -22,11 +22,13 @@ BH_ERR_HIP = -3
 BH_ERR_CAPACITY = -4
 BH_ERR_NONFINITE = -5
 BH_ERR_NOT_BUILT = -6
+BH_ERR_CONTENTION = -7
 
 WALK_VOTE = 1        # BH_WALK_VOTE
 WALK_UNSORTED = 2    # BH_WALK_UNSORTED
 
-EXPORTS = ("bh_create", "bh_build", "bh_gravity", "bh_gravity_counted", "bh_gravity_ex", "bh_sbh", "bh_direct", "bh_kick_drift",
+EXPORTS = ("bh_create", "bh_build", "bh_gravity", "bh_gravity_counted", "bh_gravity_ex", "bh_sbh", "bh_build_locked",
+           "bh_get_locked_tree", "bh_direct", "bh_kick_drift",
            "bh_leapfrog_step", "bh_diagnostics", "bh_sync", "bh_destroy",
            "bh_status_string", "bh_get_keys", "bh_get_node_count", "bh_get_nodes", "bh_get_bbox",
            "bh_set_profiling", "bh_get_profile")
@@ -66,6 +68,8 @@ def load_library():
         "bh_gravity_counted": [P, P, i64, f32, f32, f32, P, P, P],
         "bh_gravity_ex": [P, P, i64, f32, f32, f32, ctypes.c_uint32, P, P, P],
         "bh_sbh": [P, P, i64, ctypes.c_int, ctypes.c_int, ctypes.c_uint64, f32, f32, P, P],
+        "bh_build_locked": [P, P, i64, P],
+        "bh_get_locked_tree": [P, ctypes.POINTER(i64), ctypes.POINTER(i64), P, P, P, P],
         "bh_direct": [P, i64, P, i64, f32, f32, P, P],
         "bh_kick_drift": [P, P, P, i64, f32, f32, P],
         "bh_leapfrog_step": [P, P, P, P, i64, f32, f32, f32, f32, P],
@@ -178,6 +182,31 @@ class BarnesHut:
                                       ctypes.c_void_p(interactions.data_ptr()), _stream())
         _check(st, "bh_gravity")
         return out
+
+    def build_locked(self, pos_mass):
+        """The lock-based dense build (bh_build_locked); replaces the tree."""
+        t = _rows(pos_mass, "pos_mass")
+        _check(load_library().bh_build_locked(self._h, ctypes.c_void_p(t.data_ptr()), t.shape[0],
+                                              _stream()), "bh_build_locked")
+        self.n = t.shape[0]
+
+    def locked_tree(self):
+        """(child (n_cells, 8), level (n_cells,), next (n,), cap) of the last
+        lock-based build as CUDA int32 tensors; row r is cell cap - n_cells + r."""
+        import torch
+        L = load_library()
+        nc, cap = ctypes.c_int64(), ctypes.c_int64()
+        _check(L.bh_get_locked_tree(self._h, ctypes.byref(nc), ctypes.byref(cap), None, None, None,
+                                    _stream()), "bh_get_locked_tree")
+        child = torch.empty((max(nc.value, 1), 8), dtype=torch.int32, device="cuda")
+        level = torch.empty(max(nc.value, 1), dtype=torch.int32, device="cuda")
+        nxt = torch.empty(max(self.n, 1), dtype=torch.int32, device="cuda")
+        _check(L.bh_get_locked_tree(self._h, ctypes.byref(nc), ctypes.byref(cap),
+                                    ctypes.c_void_p(child.data_ptr()),
+                                    ctypes.c_void_p(level.data_ptr()),
+                                    ctypes.c_void_p(nxt.data_ptr()), _stream()),
+               "bh_get_locked_tree")
+        return child[:nc.value], level[:nc.value], nxt[:self.n], cap.value
 
     def sbh(self, targets, d=2, samples=1, seed=0, G=1.0, eps=0.0, out=None):
         """Stochastic Barnes-Hut estimate at separate targets (bh_sbh; the

@@ -31,6 +31,11 @@ struct bh_ctx {
     uint32_t *perm = nullptr;         // aliases vals or vals_alt after a build
     uint32_t *inv = nullptr;          // Morton rank of each caller index (unsorted walks)
     double *diag = nullptr;           // partial sums of bh_diagnostics
+
+    // lock-based dense build (allocated on first use)
+    int32_t *lk_child = nullptr, *lk_level = nullptr, *lk_next = nullptr, *lk_counter = nullptr;
+    int32_t lk_cap = 0;
+    uint32_t lk_n = 0;
     BuildScratch bw = {};
     Node *nodes = nullptr;
 
@@ -66,7 +71,8 @@ void free_all(bh_ctx *c)
     void *ptrs[] = {c->prm, c->bbox_part, c->keys, c->keys_alt, c->vals, c->vals_alt, c->spine,
                     c->spos, c->bw.dc, c->bw.tile_counts, c->bw.tile_sums, c->bw.tile_scan,
                     c->bw.first_node, c->bw.P, c->nodes, c->tkeys, c->tkeys_alt, c->tvals,
-                    c->tvals_alt, c->tspine, c->tpos, c->inv, c->diag};
+                    c->tvals_alt, c->tspine, c->tpos, c->inv, c->diag, c->lk_child,
+                    c->lk_level, c->lk_next, c->lk_counter};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
     if (c->host_prm) (void)hipHostFree(c->host_prm);
@@ -98,6 +104,7 @@ const char *bh_status_string(int status)
     case BH_ERR_CAPACITY: return "tree node capacity exceeded";
     case BH_ERR_NONFINITE: return "non-finite source coordinate or mass";
     case BH_ERR_NOT_BUILT: return "no successful build";
+    case BH_ERR_CONTENTION: return "lock-based build: an insertion ran out of retries";
     default: return "unknown status";
     }
 }
@@ -365,6 +372,60 @@ bh_status bh_sbh(bh_ctx *c, const float *targets, int64_t n_targets, int d, int 
     return launch_status();
 }
 
+bh_status bh_build_locked(bh_ctx *c, const float *src_pos_mass, int64_t n, void *stream)
+{
+    if (!c || n < 0 || n > c->max_src) return BH_ERR_INVALID;
+    if (n > 0 && (!src_pos_mass || !aligned16(src_pos_mass))) return BH_ERR_INVALID;
+    if (!c->lk_child) {   // first use: cells for the worst case of the key depth
+        const uint64_t cap = (uint64_t)c->max_src * (uint64_t)(c->bits - 1) + 1;
+        if (cap > 0x7ffffff0ull) return BH_ERR_INVALID;
+        c->lk_cap = (int32_t)cap;
+        bool ok = dalloc(&c->lk_child, (size_t)cap * 8) == hipSuccess;
+        ok &= dalloc(&c->lk_level, (size_t)cap) == hipSuccess;
+        ok &= dalloc(&c->lk_next, (size_t)c->max_src) == hipSuccess;
+        ok &= dalloc(&c->lk_counter, 1) == hipSuccess;
+        if (!ok) return BH_ERR_OOM;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    c->last_stream = s;
+    c->built = false;   // the keys and the root cube are replaced below
+    const uint32_t un = (uint32_t)n;
+    const float4 *src = (const float4 *)src_pos_mass;
+    launch_bbox(src, un, c->bbox_part, bbox_partials(un), c->prm, c->bits, s);
+    if (un > 0) launch_morton(src, un, c->prm, c->bits, c->keys, c->vals, s);
+    launch_lock_build(c->keys, un, c->bits, c->lk_child, c->lk_level, c->lk_next, c->lk_cap,
+                      c->lk_counter, c->prm, s);
+    c->lk_n = un;
+    return launch_status();
+}
+
+bh_status bh_get_locked_tree(bh_ctx *c, int64_t *n_cells, int64_t *cap, int32_t *child,
+                             int32_t *level, int32_t *next, void *stream)
+{
+    if (!c || !n_cells || !cap || !c->lk_child) return BH_ERR_INVALID;
+    hipStream_t s = (hipStream_t)stream;
+    int32_t counter = 0;
+    if (hipMemcpyAsync(&counter, c->lk_counter, sizeof(int32_t), hipMemcpyDeviceToHost, s) !=
+            hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return BH_ERR_HIP;
+    const int32_t first = counter < 0 ? 0 : counter;
+    *cap = c->lk_cap;
+    *n_cells = c->lk_cap - first;
+    const size_t nc = (size_t)(c->lk_cap - first);
+    bool ok = true;
+    if (child)
+        ok &= hipMemcpyAsync(child, c->lk_child + (size_t)first * 8, nc * 8 * sizeof(int32_t),
+                             hipMemcpyDeviceToDevice, s) == hipSuccess;
+    if (level)
+        ok &= hipMemcpyAsync(level, c->lk_level + first, nc * sizeof(int32_t),
+                             hipMemcpyDeviceToDevice, s) == hipSuccess;
+    if (next && c->lk_n)
+        ok &= hipMemcpyAsync(next, c->lk_next, (size_t)c->lk_n * sizeof(int32_t),
+                             hipMemcpyDeviceToDevice, s) == hipSuccess;
+    return ok ? BH_OK : BH_ERR_HIP;
+}
+
 bh_status bh_kick_drift(float *pos_mass, float *vel, const float *acc_pot, int64_t n,
                         float dt_kick, float dt_drift, void *stream)
 {
@@ -435,6 +496,7 @@ bh_status bh_sync(bh_ctx *c)
         c->built = false;
         return BH_ERR_CAPACITY;
     }
+    if (w & kStatusLockRetry) return BH_ERR_CONTENTION;
     return BH_OK;
 }
 

@@ -15,6 +15,7 @@ constexpr int kSourcePad = 8;       // readable slack after the sorted sources
 // Device status bits (a word in DevParams; 0 = fine).
 constexpr uint32_t kStatusNonFinite = 1u;
 constexpr uint32_t kStatusCapacity = 2u;
+constexpr uint32_t kStatusLockRetry = 4u;   // lock-based build: an insertion ran out of retries
 
 // Per-build scalars kept in device memory, so that no step needs the host to
 // read back an intermediate value.
@@ -136,6 +137,12 @@ struct SbhArgs {
     float4 *out;
 };
 void launch_sbh(const SbhArgs &a, hipStream_t s);
+
+// lockbuild.hip: the pages' lock-based dense build (cells allocated downward
+// from cap - 1, the root; slots: -1 empty, -2 locked, particle, n + cell id)
+void launch_lock_build(const uint64_t *keys, uint32_t n, int bits, int32_t *child,
+                       int32_t *level, int32_t *next, int32_t cap, int32_t *counter,
+                       DevParams *prm, hipStream_t s);
 
 // integrate.hip: leapfrog kick/drift and conserved-quantity sums
 constexpr int kDiagTerms = 10;           // mass, kinetic, potential, p xyz, L xyz, count

@@ -42,7 +42,8 @@ typedef enum bh_status {
     BH_ERR_HIP = -3,        /* a HIP runtime call or kernel launch failed */
     BH_ERR_CAPACITY = -4,   /* the tree needed more nodes than node_capacity */
     BH_ERR_NONFINITE = -5,  /* a source coordinate or mass is NaN or infinite */
-    BH_ERR_NOT_BUILT = -6   /* bh_gravity before a successful bh_build */
+    BH_ERR_NOT_BUILT = -6,  /* bh_gravity before a successful bh_build */
+    BH_ERR_CONTENTION = -7  /* bh_build_locked: an insertion ran out of retries */
 } bh_status;
 
 /* Build parameters, fixed for the life of a context.
@@ -131,6 +132,32 @@ bh_status bh_gravity_counted(bh_ctx *ctx, const float *targets, int64_t n_target
 bh_status bh_gravity_ex(bh_ctx *ctx, const float *targets, int64_t n_targets, float theta,
                         float G, float eps, uint32_t flags, float *out_acc_pot,
                         uint64_t *interactions, void *stream);
+
+/* The lock-based dense build of [Tree] 构建树结构 / 核心代码片段 / 并发与同步 and
+ * its embedded article on dense storage, kept to measure that design against
+ * bh_build on the same device.  One thread per source walks down from the
+ * root; at the first slot that is not a cell it takes the slot with a
+ * compare-and-swap (empty -> locked); an empty slot receives the source, a
+ * slot holding another source is subdivided into new cells (allocated
+ * downward by an atomic decrement) until the two separate, and the slot is
+ * released after a fence.  Octants come from the Morton keys, so the result
+ * is the leaf-capacity-1 octree; sources with identical keys are chained at
+ * the finest level.  The walk does not use this tree; bh_get_locked_tree
+ * returns it.  Replaces the context's tree (bh_gravity needs bh_build again).
+ * Allocates its arrays on first use (synchronous): max_sources * (key_bits/3
+ * - 1) + 1 cells of 36 bytes.  Device status (bh_sync): BH_ERR_NONFINITE,
+ * BH_ERR_CAPACITY, BH_ERR_CONTENTION (an insertion gave up after 4096
+ * steps; the tree is then incomplete). */
+bh_status bh_build_locked(bh_ctx *ctx, const float *src_pos_mass, int64_t n, void *stream);
+
+/* The tree of the last bh_build_locked (synchronous).  Cells have ids
+ * cap - n_cells .. cap - 1 (the root is cap - 1); row r of the copies is cell
+ * cap - n_cells + r.  child: n_cells * 8 slots (-1 empty, 0..n-1 a source, the
+ * head of its chain, n + id a cell), in octant order; level: n_cells levels;
+ * next: n entries, the next source with the same key or -1.  Device buffers;
+ * any may be NULL. */
+bh_status bh_get_locked_tree(bh_ctx *ctx, int64_t *n_cells, int64_t *cap, int32_t *child,
+                             int32_t *level, int32_t *next, void *stream);
 
 /* Stochastic Barnes-Hut ([SBH] 方法, 关键设计): an unbiased Monte-Carlo estimate
  * of the sum at separate query points, on the context's tree, which must be

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_status_strings(lib):
     import barnes_hut_tree_amd as bh
     for code in (bh.BH_OK, bh.BH_ERR_INVALID, bh.BH_ERR_OOM, bh.BH_ERR_HIP, bh.BH_ERR_CAPACITY,
-                 bh.BH_ERR_NONFINITE, bh.BH_ERR_NOT_BUILT):
+                 bh.BH_ERR_NONFINITE, bh.BH_ERR_NOT_BUILT, bh.BH_ERR_CONTENTION):
         s = bh.status_string(code)
         assert s and s != "unknown status"
     assert bh.status_string(12345) == "unknown status"
