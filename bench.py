@@ -215,6 +215,30 @@ def ablations(args):
                               "interactions": inter}), flush=True)
         tree.close()
 
+    # tree build: the pages' lock-based dense build against the sorted-key build
+    builds = [("lattice_n1000000_shuffled", W.lattice(100, shuffled=True, seed=2)),
+              ("lattice_n1000000_lattice_order", W.lattice(100, shuffled=False, seed=2)),
+              ("plummer_n1048576_random_order", W.plummer(1 << 20, seed=3)),
+              ("galaxy_pair_n5000000", W.galaxy_pair()[0])]
+    for wl, p in builds:
+        n = p.shape[0]
+        src = torch.from_numpy(p).cuda()
+        t1 = bh.BarnesHut(n, 0, args.key_bits, 1)
+        ms_lock = timed(lambda: t1.build_locked(src))
+        t1.sync()
+        ms_sorted1 = timed(lambda: t1.build(src))
+        t1.sync()
+        t1.close()
+        t16 = bh.BarnesHut(n, 0, args.key_bits, args.leaf_cap)
+        ms_sorted16 = timed(lambda: t16.build(src))
+        t16.close()
+        print(json.dumps({"ablation": "tree_build", "workload": wl, "n": n,
+                          "lock_based_dense_b1_ms": round(ms_lock, 3),
+                          "sorted_key_b1_ms": round(ms_sorted1, 3),
+                          "sorted_key_b%d_ms" % args.leaf_cap: round(ms_sorted16, 3)}),
+              flush=True)
+        del src
+
     p, prm, wname = make_workload("plummer")
     n = p.shape[0]
     src = torch.from_numpy(p).cuda()
