@@ -355,3 +355,30 @@ def test_invalid_arguments():
     with pytest.raises(bh.BHError):
         t.build(big)
     t.close()
+
+
+# ---------------------------------------------------------------------------
+# other build parameters: 30-bit keys, very small and very large leaves
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("key_bits,B", [(30, 16), (63, 2), (63, 256), (30, 256)])
+def test_gravity_other_build_parameters(orc, key_bits, B):
+    p = W.plummer(1 << 16, seed=12)
+    log("gravity plummer 2^16 key_bits", key_bits, "B", B)
+    _sampled_parity(orc, p, 0.5, 0.01, B, 2048, 35, "plummer2^16 bits=%d B=%d" % (key_bits, B),
+                    key_bits=key_bits)
+
+
+def test_separate_targets_30bit_keys(orc):
+    import barnes_hut_tree_amd as bh
+    src = W.surface_sources(1 << 15, seed=13)
+    q = W.box_queries()[:100003]
+    t = bh.BarnesHut(src.shape[0], q.shape[0], 30, 16)
+    t.build(torch.from_numpy(src).cuda())
+    got = t.gravity(0.5, 1.0, 0.0, targets=torch.from_numpy(q).cuda()).cpu().numpy()
+    t.sync()
+    which = np.sort(np.random.default_rng(36).choice(q.shape[0], 2048, replace=False))
+    ref = orc.Tree(src, key_bits=30, leaf_cap=16)
+    modes = [ref.gravity(0.5, 1.0, 0.0, targets=q, which=which, tie_mode=m) for m in (0, 1, 2)]
+    p99a, p99p = assert_walk_parity(got[which], [m[0] for m in modes], modes[0][2], "30-bit queries")
+    log("  30-bit keys, separate queries: p99 acc %.3g pot %.3g" % (p99a, p99p))
+    t.close()
