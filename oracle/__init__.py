@@ -37,6 +37,8 @@ def lib():
         i64 = ctypes.c_int64
         L.orc_build.restype = P
         L.orc_build.argtypes = [P, i64, ctypes.c_int, ctypes.c_int]
+        L.orc_build_curve.restype = P
+        L.orc_build_curve.argtypes = [P, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         L.orc_free.argtypes = [P]
         L.orc_bbox.argtypes = [P, P, P, P]
         L.orc_keys.argtypes = [P, P]
@@ -75,12 +77,16 @@ def _f4(pos_mass):
 class Tree:
     """The oracle's octree over fp32 (x, y, z, m) sources, built in fp64."""
 
-    def __init__(self, pos_mass, key_bits=63, leaf_cap=16):
+    CURVES = {"morton": 0, "hilbert": 1}
+
+    def __init__(self, pos_mass, key_bits=63, leaf_cap=16, curve="morton"):
         self.src = _f4(pos_mass)  # kept alive: the C side keeps a pointer to it
         self.n = self.src.shape[0]
         self.key_bits = key_bits
         self.leaf_cap = leaf_cap
-        self._h = lib().orc_build(_ptr(self.src), self.n, key_bits, leaf_cap)
+        self.curve = curve
+        self._h = lib().orc_build_curve(_ptr(self.src), self.n, key_bits, leaf_cap,
+                                        self.CURVES[curve])
         if not self._h:
             raise ValueError("invalid oracle build arguments")
 

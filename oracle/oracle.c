@@ -38,7 +38,7 @@ typedef struct {
     int64_t corner[3];   /* integer corner on the level-l grid, in [0, 2^l) */
     int64_t off;         /* first member in the partitioned index array */
     int64_t count;       /* number of member particles */
-    int64_t child[8];    /* cell index per octant, -1 when that octant is empty */
+    int64_t child[8];    /* cell index per key digit (the octant for Morton keys), -1 if empty */
     int32_t n_children;
     double mass;         /* M_c = sum of member masses */
     double com[3];       /* X_c = sum(m x) / M_c, or the cell centre if M_c = 0 */
@@ -48,6 +48,7 @@ typedef struct {
     int64_t n;
     int bits;            /* bits per axis: 21 (63-bit keys) or 10 (30-bit keys) */
     int leaf_cap;        /* B: a cell with more than B particles is split */
+    int curve;           /* key order: 0 Morton (Z), 1 Hilbert */
     const float *src;    /* caller's float4 array (x, y, z, m), not owned */
     double lo[3], hi[3], L;
     uint64_t *q;         /* 3 integer coordinates per particle */
@@ -95,6 +96,39 @@ static void step_bbox(orc_tree *t)
 /* 3k+1 <- y bit k, 3k+2 <- z bit k.  That order is the octant numbering of   */
 /* [Tree] 构建树结构 (childIndex = 1 for the upper x half, +2 for y, +4 for z). */
 /* ------------------------------------------------------------------------ */
+/* Hilbert index of integer coordinates (x, y, z) of `bits` bits each, after
+   Skilling, "Programming the Hilbert curve" (AIP Conf. Proc. 707, 2004): the
+   coordinates are turned into the transposed index in place (undo excess
+   work from the top bit down, then Gray-encode), and the transposed index is
+   read out one bit level at a time, x bit first, so that each 3-bit digit
+   names a child cell of the cell above it, in the curve's order. */
+static uint64_t hilbert_key(uint64_t x, uint64_t y, uint64_t z, int bits)
+{
+    uint64_t X[3] = {x, y, z};
+    const uint64_t M = (uint64_t)1 << (bits - 1);
+    for (uint64_t Q = M; Q > 1; Q >>= 1) {
+        const uint64_t P = Q - 1;
+        for (int i = 0; i < 3; ++i) {
+            if (X[i] & Q) {
+                X[0] ^= P;
+            } else {
+                const uint64_t t = (X[0] ^ X[i]) & P;
+                X[0] ^= t;
+                X[i] ^= t;
+            }
+        }
+    }
+    for (int i = 1; i < 3; ++i) X[i] ^= X[i - 1];
+    uint64_t t = 0;
+    for (uint64_t Q = M; Q > 1; Q >>= 1)
+        if (X[2] & Q) t ^= Q - 1;
+    for (int i = 0; i < 3; ++i) X[i] ^= t;
+    uint64_t key = 0;
+    for (int b = bits - 1; b >= 0; --b)
+        for (int i = 0; i < 3; ++i) key = (key << 1) | ((X[i] >> b) & 1u);
+    return key;
+}
+
 static void step_keys(orc_tree *t)
 {
     const uint64_t top = ((uint64_t)1 << t->bits) - 1;
@@ -110,6 +144,8 @@ static void step_keys(orc_tree *t)
             for (int k = 0; k < t->bits; ++k)
                 key |= ((qa >> k) & 1u) << (3 * k + a);
         }
+        if (t->curve == 1)
+            key = hilbert_key(t->q[3 * i], t->q[3 * i + 1], t->q[3 * i + 2], t->bits);
         t->keys[i] = key;
     }
 }
@@ -144,7 +180,9 @@ static void step_order(orc_tree *t)
 /* division.  Readings: a cell with more than B particles is split unless it  */
 /* is at the finest level (bits); membership of an octant is decided by the  */
 /* integer coordinates, the upper half of each axis taking the set bit;      */
-/* empty octants produce no cell; children are visited in octant order 0..7. */
+/* empty octants produce no cell; children are visited in the order of the   */
+/* key digit that names them: octant order 0..7 for Morton keys, the curve's */
+/* order for Hilbert keys (the same cells, in another order).                */
 /* ------------------------------------------------------------------------ */
 static int64_t new_cell(orc_tree *t)
 {
@@ -167,6 +205,12 @@ static int octant_of(const orc_tree *t, int64_t p, int child_level)
     return ox + 2 * oy + 4 * oz;
 }
 
+/* the key digit naming the level-child_level cell that holds particle p */
+static int digit_of(const orc_tree *t, int64_t p, int child_level)
+{
+    return (int)((t->keys[p] >> (3 * (t->bits - child_level))) & 7u);
+}
+
 static int64_t subdivide(orc_tree *t, int level, const int64_t corner[3],
                          int64_t off, int64_t count, int64_t *scratch)
 {
@@ -182,29 +226,32 @@ static int64_t subdivide(orc_tree *t, int level, const int64_t corner[3],
         return c;
     }
 
-    /* Stable partition of the members into octants 0..7. */
-    int64_t octant_count[8] = {0};
+    /* Stable partition of the members by the key digit of their child cell
+       (for Morton keys the digit is the octant). */
+    int64_t digit_count[8] = {0};
     for (int64_t k = 0; k < count; ++k)
-        octant_count[octant_of(t, t->idx[off + k], level + 1)]++;
-    int64_t octant_off[8];
-    octant_off[0] = 0;
-    for (int o = 1; o < 8; ++o) octant_off[o] = octant_off[o - 1] + octant_count[o - 1];
+        digit_count[digit_of(t, t->idx[off + k], level + 1)]++;
+    int64_t digit_off[8];
+    digit_off[0] = 0;
+    for (int o = 1; o < 8; ++o) digit_off[o] = digit_off[o - 1] + digit_count[o - 1];
     int64_t fill[8];
-    memcpy(fill, octant_off, sizeof(fill));
+    memcpy(fill, digit_off, sizeof(fill));
     for (int64_t k = 0; k < count; ++k) {
         int64_t p = t->idx[off + k];
-        scratch[fill[octant_of(t, p, level + 1)]++] = p;
+        scratch[fill[digit_of(t, p, level + 1)]++] = p;
     }
     memcpy(&t->idx[off], scratch, (size_t)count * sizeof(int64_t));
 
     for (int o = 0; o < 8; ++o) {
-        if (octant_count[o] == 0) continue;
+        if (digit_count[o] == 0) continue;
+        /* the child's place on the level+1 grid, from its members' coordinates */
+        const int oct = octant_of(t, t->idx[off + digit_off[o]], level + 1);
         int64_t child_corner[3];
-        child_corner[0] = 2 * corner[0] + (o & 1);
-        child_corner[1] = 2 * corner[1] + ((o >> 1) & 1);
-        child_corner[2] = 2 * corner[2] + ((o >> 2) & 1);
-        int64_t ch = subdivide(t, level + 1, child_corner, off + octant_off[o],
-                               octant_count[o], scratch);
+        child_corner[0] = 2 * corner[0] + (oct & 1);
+        child_corner[1] = 2 * corner[1] + ((oct >> 1) & 1);
+        child_corner[2] = 2 * corner[2] + ((oct >> 2) & 1);
+        int64_t ch = subdivide(t, level + 1, child_corner, off + digit_off[o],
+                               digit_count[o], scratch);
         /* t->cells may have moved during the recursion: index, not pointer. */
         t->cells[c].child[o] = ch;
         t->cells[c].n_children++;
@@ -254,11 +301,14 @@ static void step_com(orc_tree *t)
 /* ------------------------------------------------------------------------ */
 /* Public: build                                                             */
 /* ------------------------------------------------------------------------ */
-orc_tree *orc_build(const float *pos_mass, int64_t n, int key_bits, int leaf_cap)
+orc_tree *orc_build_curve(const float *pos_mass, int64_t n, int key_bits, int leaf_cap,
+                          int curve)
 {
-    if (n < 0 || leaf_cap < 1 || (key_bits != 30 && key_bits != 63)) return NULL;
+    if (n < 0 || leaf_cap < 1 || (key_bits != 30 && key_bits != 63) || (curve != 0 && curve != 1))
+        return NULL;
     orc_tree *t = (orc_tree *)calloc(1, sizeof(orc_tree));
     t->n = n;
+    t->curve = curve;
     t->bits = key_bits / 3;
     t->leaf_cap = leaf_cap;
     t->src = pos_mass;
@@ -273,6 +323,11 @@ orc_tree *orc_build(const float *pos_mass, int64_t n, int key_bits, int leaf_cap
     step_tree(t);
     step_com(t);
     return t;
+}
+
+orc_tree *orc_build(const float *pos_mass, int64_t n, int key_bits, int leaf_cap)
+{
+    return orc_build_curve(pos_mass, n, key_bits, leaf_cap, 0);
 }
 
 void orc_free(orc_tree *t)
@@ -596,13 +651,14 @@ int orc_target_order(const orc_tree *t, const float *targets, int64_t nt, int64_
     const uint64_t top = ((uint64_t)1 << t->bits) - 1;
     const double S = (t->L > 0.0) ? ldexp(1.0, t->bits) / t->L : 0.0;
     for (int64_t i = 0; i < nt; ++i) {
-        uint64_t key = 0;
+        uint64_t key = 0, qq[3];
         for (int a = 0; a < 3; ++a) {
             double f = floor(((double)targets[4 * i + a] - t->lo[a]) * S);
             uint64_t qa = !(f >= 0.0) ? 0 : (f >= (double)top) ? top : (uint64_t)f;
             for (int k = 0; k < t->bits; ++k) key |= ((qa >> k) & 1u) << (3 * k + a);
+            qq[a] = qa;
         }
-        keys[i] = key;
+        keys[i] = (t->curve == 1) ? hilbert_key(qq[0], qq[1], qq[2], t->bits) : key;
         order[i] = i;
     }
     g_sort_keys = keys;

@@ -552,3 +552,48 @@ def test_sbh_group_shares_random_numbers(orc):
     # queries one group apart draw other numbers
     out2, _, _ = orc.Tree(src, leaf_cap=1).sbh(q, d=2, seed=3, group=1)
     assert not np.array_equal(out2[0], out2[1])
+
+
+# ---------------------------------------------------------------------------
+# Hilbert keys (Skilling's transpose algorithm) and the tree in Hilbert order
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("side,bits", [(8, 63), (16, 63), (8, 30)])
+def test_hilbert_keys_walk_the_grid_one_step_at_a_time(orc, side, bits):
+    # points at i/(side-1) fall one per cell of the side^3 grid of the root
+    # cube [0, 1]^3, so the top digits of their keys are the curve's index of
+    # that cell: the curve must visit every cell once, start at the origin and
+    # move to a face neighbour at every step
+    g = np.arange(side) / (side - 1.0)
+    z, y, x = np.meshgrid(g, g, g, indexing="ij")
+    p = f4(np.stack([x.ravel(), y.ravel(), z.ravel()], 1), 1.0)
+    t = orc.Tree(p, key_bits=bits, leaf_cap=1, curve="hilbert")
+    levels = int(np.log2(side))
+    top = t.keys() >> np.uint64(3 * (bits // 3 - levels))
+    assert np.array_equal(np.sort(top), np.arange(side ** 3, dtype=np.uint64))
+    cells = np.stack([np.round(x.ravel() * (side - 1)), np.round(y.ravel() * (side - 1)),
+                      np.round(z.ravel() * (side - 1))], 1).astype(np.int64)
+    path = cells[np.argsort(top)]
+    assert np.array_equal(path[0], [0, 0, 0])
+    assert np.all(np.abs(np.diff(path, axis=0)).sum(1) == 1)
+
+
+@pytest.mark.parametrize("case,B", [("uniform4096", 16), ("plummer5000", 4), ("dups", 1)])
+def test_hilbert_tree_has_the_morton_cells(orc, case, B):
+    p = {"uniform4096": lambda: W.uniform_cube(4096, seed=1),
+         "plummer5000": lambda: W.plummer(5000, seed=15),
+         "dups": lambda: np.concatenate([W.uniform_cube(700, seed=16)] * 2)}[case]()
+    tm = orc.Tree(p, leaf_cap=B, curve="morton")
+    th = orc.Tree(p, leaf_cap=B, curve="hilbert")
+
+    def cellset(t):
+        c = t.cells()
+        perm = t.perm()
+        return {(int(l), int(pre), int(lf), int(cnt), tuple(sorted(perm[s:s + cnt].tolist())))
+                for l, pre, lf, s, cnt in zip(c["level"], c["prefix"], c["is_leaf"], c["start"],
+                                              c["count"])}
+    assert cellset(tm) == cellset(th)
+    # the same cells in another order: forces agree to rounding
+    a, na, _ = tm.gravity(0.5, 1.0, 1e-3)
+    b, nb, _ = th.gravity(0.5, 1.0, 1e-3)
+    assert np.array_equal(na, nb)
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-14)

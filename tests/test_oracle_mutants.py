@@ -54,6 +54,12 @@ MUTANTS = [
     ("sbh_roulette_inverted", "if (!(u < pk)) break;", "if (u < pk) break;"),
     ("philox_multiplier", "(uint64_t)0xD2511F53u * c0", "(uint64_t)0xD2511F55u * c0"),
     ("target_clamp_low", "uint64_t qa = !(f >= 0.0) ? 0 :", "uint64_t qa = !(f >= 0.0) ? top :"),
+    ("hilbert_no_gray_code", "for (int i = 1; i < 3; ++i) X[i] ^= X[i - 1];",
+     "for (int i = 1; i < 3; ++i) X[i] ^= 0;"),
+    ("hilbert_half_exchange", "                X[0] ^= t;\n                X[i] ^= t;",
+     "                X[0] ^= t;"),
+    ("partition_by_octant_not_digit", "digit_count[digit_of(t, t->idx[off + k], level + 1)]++;",
+     "digit_count[octant_of(t, t->idx[off + k], level + 1)]++;"),
     ("vote_leaf_monopole", "            interact(&g->w[k], cell->mass, cell->com);",
      "            interact(&g->w[k], cell->mass, g->w[k].x);"),
 ]
