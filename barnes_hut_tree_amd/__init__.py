@@ -45,7 +45,11 @@ class BHError(RuntimeError):
 
 class _Params(ctypes.Structure):
     _fields_ = [("key_bits", ctypes.c_int32), ("leaf_cap", ctypes.c_int32),
-                ("node_capacity", ctypes.c_int64)]
+                ("node_capacity", ctypes.c_int64), ("key_curve", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+CURVES = {"morton": 0, "hilbert": 1}   # BH_CURVE_MORTON, BH_CURVE_HILBERT
 
 
 _lib = None
@@ -119,16 +123,18 @@ def _rows(t, name):
 class BarnesHut:
     """One octree context (bh_ctx) on the current device."""
 
-    def __init__(self, max_sources, max_targets=0, key_bits=63, leaf_cap=16, node_capacity=0):
+    def __init__(self, max_sources, max_targets=0, key_bits=63, leaf_cap=16, node_capacity=0,
+                 curve="morton"):
         L = load_library()
         self._h = ctypes.c_void_p()
-        p = _Params(int(key_bits), int(leaf_cap), int(node_capacity))
+        p = _Params(int(key_bits), int(leaf_cap), int(node_capacity), CURVES[curve], 0)
         _check(L.bh_create(ctypes.byref(self._h), int(max_sources), int(max_targets),
                            ctypes.byref(p)), "bh_create")
         self.max_sources = int(max_sources)
         self.max_targets = int(max_targets)
         self.key_bits = int(key_bits)
         self.leaf_cap = int(leaf_cap)
+        self.curve = curve
         self.n = 0
 
     def close(self):

@@ -4,7 +4,9 @@
 // particles by a reduction; they fix the root cell.  The root cube is
 // anchored at the min corner with side L = the largest extent.
 //
-// Keys: [Tree] 实现步骤 orders particles by Morton (Z-order) code.  Each axis
+// Keys: [Tree] 实现步骤 orders particles by Morton (Z-order) code; a Hilbert
+// key is the other curve a context can choose (same cells, sibling order of
+// the curve).  Each axis
 // is quantised on the root cube in fp64, q = floor((x - lo) * 2^bits / L),
 // clamped to [0, 2^bits - 1], and the bits are interleaved x, y, z from the
 // least significant end, which matches the octant numbering of [Tree]
@@ -118,17 +120,47 @@ __device__ inline uint64_t spread3(uint64_t v)
     return v;
 }
 
-__device__ inline uint64_t quantise(float x, double lo, double scale, uint64_t top)
+
+// Hilbert index of 21-bit-or-less integer coordinates, after Skilling,
+// "Programming the Hilbert curve" (AIP Conf. Proc. 707, 2004): the transposed
+// index is formed in place (undo excess work from the top bit down, then Gray
+// encoding) and its bits are interleaved x, y, z from the most significant
+// end, so each 3-bit digit names a child cell in the curve's order.  Every
+// cell is still one contiguous key range: the tree is the same, only the
+// order of siblings changes.
+__device__ inline uint64_t hilbert3(uint32_t x, uint32_t y, uint32_t z, int bits)
 {
-#pragma clang fp contract(off)
-    double d = (double)x - lo;
-    double u = d * scale;
-    double f = floor(u);
-    if (!(f >= 0.0)) return 0;        // below the cube (separate targets) or NaN
-    if (f >= (double)top) return top; // the max face and beyond clamp to the top cell
-    return (uint64_t)f;
+    const uint32_t M = 1u << (bits - 1);
+    for (uint32_t Q = M; Q > 1; Q >>= 1) {
+        const uint32_t P = Q - 1;
+        if (x & Q) x ^= P;
+        if (y & Q) {
+            x ^= P;
+        } else {
+            const uint32_t t = (x ^ y) & P;
+            x ^= t;
+            y ^= t;
+        }
+        if (z & Q) {
+            x ^= P;
+        } else {
+            const uint32_t t = (x ^ z) & P;
+            x ^= t;
+            z ^= t;
+        }
+    }
+    y ^= x;
+    z ^= y;
+    uint32_t t = 0;
+    for (uint32_t Q = M; Q > 1; Q >>= 1)
+        if (z & Q) t ^= Q - 1;
+    x ^= t;
+    y ^= t;
+    z ^= t;
+    return spread3(z) | (spread3(y) << 1) | (spread3(x) << 2);
 }
 
+template <bool HILBERT>
 __global__ __launch_bounds__(256) void k_morton(const float4 *__restrict__ pts, uint32_t n,
                                                 const DevParams *__restrict__ prm, int bits,
                                                 uint64_t *__restrict__ keys,
@@ -139,10 +171,11 @@ __global__ __launch_bounds__(256) void k_morton(const float4 *__restrict__ pts, 
     const float4 p = pts[i];
     const uint64_t top = (1ull << bits) - 1;
     const double s = prm->scale;
-    uint64_t qx = quantise(p.x, prm->lo[0], s, top);
-    uint64_t qy = quantise(p.y, prm->lo[1], s, top);
-    uint64_t qz = quantise(p.z, prm->lo[2], s, top);
-    keys[i] = spread3(qx) | (spread3(qy) << 1) | (spread3(qz) << 2);
+    const uint64_t qx = quantise(p.x, prm->lo[0], s, top);
+    const uint64_t qy = quantise(p.y, prm->lo[1], s, top);
+    const uint64_t qz = quantise(p.z, prm->lo[2], s, top);
+    keys[i] = HILBERT ? hilbert3((uint32_t)qx, (uint32_t)qy, (uint32_t)qz, bits)
+                      : spread3(qx) | (spread3(qy) << 1) | (spread3(qz) << 2);
     idx[i] = i;
 }
 
@@ -165,12 +198,16 @@ void launch_bbox(const float4 *src, uint32_t n, float *partials, uint32_t n_part
                        n, bits, prm);
 }
 
-void launch_morton(const float4 *pts, uint32_t n, const DevParams *prm, int bits,
+void launch_morton(const float4 *pts, uint32_t n, const DevParams *prm, int bits, int curve,
                    uint64_t *keys, uint32_t *idx, hipStream_t s)
 {
     if (n == 0) return;
-    hipLaunchKernelGGL(k_morton, dim3((n + 255) / 256), dim3(256), 0, s, pts, n, prm, bits, keys,
-                       idx);
+    if (curve == 1)
+        hipLaunchKernelGGL(k_morton<true>, dim3((n + 255) / 256), dim3(256), 0, s, pts, n, prm,
+                           bits, keys, idx);
+    else
+        hipLaunchKernelGGL(k_morton<false>, dim3((n + 255) / 256), dim3(256), 0, s, pts, n, prm,
+                           bits, keys, idx);
 }
 
 }  // namespace bh

@@ -17,7 +17,7 @@ using namespace bh;
 struct bh_ctx {
     int device = 0;
     int64_t max_src = 0, max_tgt = 0;
-    int key_bits = 63, bits = 21, leaf_cap = 16;
+    int key_bits = 63, bits = 21, leaf_cap = 16, curve = 0;
     uint64_t node_cap = 0;
 
     DevParams *prm = nullptr;
@@ -116,10 +116,11 @@ bh_status bh_create(bh_ctx **out, int64_t max_sources, int64_t max_targets,
     *out = nullptr;
     if (max_sources < 0 || max_targets < 0 || max_sources > kMaxCount || max_targets > kMaxCount)
         return BH_ERR_INVALID;
-    bh_build_params p = {63, 16, 0};
+    bh_build_params p = {63, 16, 0, 0, 0};
     if (params) p = *params;
     if ((p.key_bits != 63 && p.key_bits != 30) || p.leaf_cap < 1 || p.leaf_cap > kMaxLeafCap ||
-        p.node_capacity < 0)
+        p.node_capacity < 0 || (p.key_curve != BH_CURVE_MORTON && p.key_curve != BH_CURVE_HILBERT) ||
+        p.reserved != 0)
         return BH_ERR_INVALID;
 
     bh_ctx *c = new (std::nothrow) bh_ctx();
@@ -133,6 +134,7 @@ bh_status bh_create(bh_ctx **out, int64_t max_sources, int64_t max_targets,
     c->key_bits = p.key_bits;
     c->bits = p.key_bits / 3;
     c->leaf_cap = p.leaf_cap;
+    c->curve = p.key_curve;
     const uint64_t worst = (uint64_t)max_sources * (uint64_t)(c->bits + 1) + 1;
     c->node_cap = p.node_capacity ? (uint64_t)p.node_capacity : worst;
     if (c->node_cap > 0xfffffff0ull) c->node_cap = 0xfffffff0ull;
@@ -200,7 +202,7 @@ bh_status bh_build(bh_ctx *c, const float *src_pos_mass, int64_t n, void *stream
     record(c, 0, s);
     launch_bbox(src, un, c->bbox_part, bbox_partials(un), c->prm, c->bits, s);
     if (un > 0) {
-        launch_morton(src, un, c->prm, c->bits, c->keys, c->vals, s);
+        launch_morton(src, un, c->prm, c->bits, c->curve, c->keys, c->vals, s);
         record(c, 1, s);
         radix_sort(c->keys, c->vals, c->keys_alt, c->vals_alt, &c->keys_sorted, &c->perm, un,
                    c->key_bits, c->spine, src, c->spos, s);
@@ -225,7 +227,7 @@ static const uint32_t *sort_targets(bh_ctx *c, const float *targets, uint32_t nt
 {
     uint64_t *ko;
     uint32_t *vo;
-    launch_morton((const float4 *)targets, nt, c->prm, c->bits, c->tkeys, c->tvals, s);
+    launch_morton((const float4 *)targets, nt, c->prm, c->bits, c->curve, c->tkeys, c->tvals, s);
     radix_sort(c->tkeys, c->tvals, c->tkeys_alt, c->tvals_alt, &ko, &vo, nt, c->key_bits,
                c->tspine, (const float4 *)targets, c->tpos, s);
     return vo;
@@ -392,7 +394,8 @@ bh_status bh_build_locked(bh_ctx *c, const float *src_pos_mass, int64_t n, void 
     const uint32_t un = (uint32_t)n;
     const float4 *src = (const float4 *)src_pos_mass;
     launch_bbox(src, un, c->bbox_part, bbox_partials(un), c->prm, c->bits, s);
-    if (un > 0) launch_morton(src, un, c->prm, c->bits, c->keys, c->vals, s);
+    // the dense build indexes slots by octant: Morton keys whatever the curve
+    if (un > 0) launch_morton(src, un, c->prm, c->bits, 0, c->keys, c->vals, s);
     launch_lock_build(c->keys, un, c->bits, c->lk_child, c->lk_level, c->lk_next, c->lk_cap,
                       c->lk_counter, c->prm, s);
     c->lk_n = un;

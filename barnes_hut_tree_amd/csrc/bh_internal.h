@@ -65,13 +65,28 @@ constexpr int kBuildThreads = 256;
 constexpr int kBuildTile = 1024;
 constexpr int kTileScanThreads = 256;
 
+// Quantised coordinate of x on the root cube: floor((x - lo) * scale) in fp64,
+// each step one correctly rounded IEEE operation, clamped to [0, top] (below the
+// cube and NaN give 0, the max face and beyond the top cell).
+__device__ inline uint64_t quantise(float x, double lo, double scale, uint64_t top)
+{
+#pragma clang fp contract(off)
+    const double d = (double)x - lo;
+    const double u = d * scale;
+    const double f = floor(u);
+    if (!(f >= 0.0)) return 0;
+    if (f >= (double)top) return top;
+    return (uint64_t)f;
+}
+
 // ---- launchers (each defined in its own .hip file) ------------------------
 
 // bbox.hip
 void launch_bbox(const float4 *src, uint32_t n, float *partials, uint32_t n_partials,
                  DevParams *prm, int bits, hipStream_t s);
 uint32_t bbox_partials(uint32_t n);
-void launch_morton(const float4 *pts, uint32_t n, const DevParams *prm, int bits,
+// curve 0: Morton keys, 1: Hilbert keys
+void launch_morton(const float4 *pts, uint32_t n, const DevParams *prm, int bits, int curve,
                    uint64_t *keys, uint32_t *idx, hipStream_t s);
 
 // radix_sort.hip

@@ -288,24 +288,15 @@ __global__ __launch_bounds__(kTileScanThreads) void k_scan_tiles(
     }
 }
 
-// Integer coordinate of axis `axis` from a Morton key (inverse interleave).
-__device__ inline uint32_t compact3(uint64_t k)
+// Geometric centre of the level-l cell holding the source at p (for massless
+// cells), from its quantised coordinates: valid for either key curve.
+__device__ inline float3 cell_centre(float4 p, int level, int bits, const DevParams *prm)
 {
-    k &= 0x1249249249249249ull;
-    k = (k ^ (k >> 2)) & 0x10c30c30c30c30c3ull;
-    k = (k ^ (k >> 4)) & 0x100f00f00f00f00full;
-    k = (k ^ (k >> 8)) & 0x001f0000ff0000ffull;
-    k = (k ^ (k >> 16)) & 0x001f00000000ffffull;
-    k = (k ^ (k >> 32)) & 0x00000000001fffffull;
-    return (uint32_t)k;
-}
-
-// Geometric centre of the level-l cell holding `key` (for massless cells).
-__device__ inline float3 cell_centre(uint64_t key, int level, int bits, const DevParams *prm)
-{
+    const uint64_t top = (1ull << bits) - 1;
+    const float xyz[3] = {p.x, p.y, p.z};
     float c[3];
     for (int a = 0; a < 3; ++a) {
-        const uint32_t corner = compact3(key >> a) >> (bits - level);
+        const uint64_t corner = quantise(xyz[a], prm->lo[a], prm->scale, top) >> (bits - level);
         const double w = __builtin_ldexp(prm->L, -level);
         c[a] = (float)(prm->lo[a] + w * ((double)corner + 0.5));
     }
@@ -313,6 +304,7 @@ __device__ inline float3 cell_centre(uint64_t key, int level, int bits, const De
 }
 
 __global__ __launch_bounds__(256) void k_ranges(const uint64_t *__restrict__ keys,
+                                                const float4 *__restrict__ spos,
                                                 const D4 *__restrict__ P, uint32_t n,
                                                 int bits, uint64_t cap,
                                                 const uint32_t *__restrict__ first_node,
@@ -348,7 +340,7 @@ __global__ __launch_bounds__(256) void k_ranges(const uint64_t *__restrict__ key
                               (float)(prm->lo[1] + sum.y / sum.m),
                               (float)(prm->lo[2] + sum.z / sum.m), (float)sum.m);
         } else {
-            const float3 c = cell_centre(keys[a], l, bits, prm);
+            const float3 c = cell_centre(spos[a], l, bits, prm);
             com = make_float4(c.x, c.y, c.z, 0.f);
         }
         *reinterpret_cast<float4 *>(&nodes[X]) = com;
@@ -382,7 +374,7 @@ void build_tree(const uint64_t *keys_sorted, const float4 *spos, uint32_t n, int
     hipLaunchKernelGGL(k_emit, dim3(tiles), dim3(kBuildThreads), 0, s, (const uint16_t *)w.dc, spos,
                        n, (const TileScan *)w.tile_scan, tiles, node_capacity, w.first_node, w.P,
                        nodes, prm);
-    hipLaunchKernelGGL(k_ranges, dim3(grid_for(n, 2048)), dim3(256), 0, s, keys_sorted,
+    hipLaunchKernelGGL(k_ranges, dim3(grid_for(n, 2048)), dim3(256), 0, s, keys_sorted, spos,
                        (const D4 *)w.P, n, bits, node_capacity, (const uint32_t *)w.first_node,
                        nodes, (const DevParams *)prm);
 }

@@ -4,8 +4,9 @@
 
 Default workload: an equal-mass Plummer sphere of N = 2^20 particles (scale
 radius 1, truncated at 20), fp32 float4, theta = 0.5, G = 1, Plummer
-softening eps = 0.01, leaf capacity 16, 63-bit Morton keys, fed in random
-(generation) order.  Inputs are synthetic (workloads.py) and resident in
+softening eps = 0.01, leaf capacity 16, 63-bit keys on the Hilbert curve
+(--curve morton for the Z-order of the pages; the same tree cells), fed in
+random (generation) order.  Inputs are synthetic (workloads.py) and resident in
 device memory before timing starts.  One step = bh_build + bh_gravity (keys,
 sort, tree, centre of mass, walk), from caller-order input to caller-order
 output.  Prints one JSON line.
@@ -59,9 +60,10 @@ def walk_source_hash():
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload):
+def read_traffic(workload, curve):
     """HBM bytes per walk launch from the committed rocprofv3 counter summary,
-    or None when absent or taken for a different walk kernel source."""
+    or None when absent, taken for a different walk kernel source, or for the
+    other key curve."""
     path = os.path.join(PROFILES, "walk_%s_traffic.txt" % workload)
     if not os.path.exists(path):
         return None
@@ -70,7 +72,7 @@ def read_traffic(workload):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("walk_source_sha256_16") != walk_source_hash():
+    if vals.get("walk_source_sha256_16") != walk_source_hash() or vals.get("key_curve") != curve:
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -147,7 +149,7 @@ def theta_sweep(args):
                       "tflops_at_20_per_pair": round(20 * pairs / (direct_ms * 1e-3) / 1e12, 2)}),
           flush=True)
 
-    tree = bh.BarnesHut(n, 0, args.key_bits, args.leaf_cap)
+    tree = bh.BarnesHut(n, 0, args.key_bits, args.leaf_cap, curve=args.curve)
     build_ms = timed(lambda: tree.build(src), 5)
     tree.sync()
     out = torch.empty_like(ref)
@@ -167,6 +169,7 @@ def theta_sweep(args):
         print(json.dumps(row), flush=True)
     tree.close()
     print(json.dumps({"sweep": wname, "n": n, "eps": prm["eps"], "leaf_cap": args.leaf_cap,
+                      "key_curve": args.curve,
                       "direct_ms": round(direct_ms, 3), "rows": len(rows)}), flush=True)
 
 
@@ -277,7 +280,7 @@ def leapfrog(args):
     eps, dt = 0.02, 0.05
     tp = torch.from_numpy(p).cuda()
     tv = torch.from_numpy(np.concatenate([v, np.zeros((n, 1), np.float32)], 1)).cuda()
-    tree = bh.BarnesHut(n, 0, args.key_bits, args.leaf_cap)
+    tree = bh.BarnesHut(n, 0, args.key_bits, args.leaf_cap, curve=args.curve)
     tree.build(tp)
     ta = tree.gravity(theta, 1.0, eps)
     for _ in range(args.warmup):
@@ -294,6 +297,7 @@ def leapfrog(args):
     e0, e1 = d0["kinetic"] + d0["potential"], d1["kinetic"] + d1["potential"]
     print(json.dumps({
         "leapfrog": "galaxy_pair_n5000000", "n": n, "theta": theta, "eps": eps, "dt": dt,
+        "key_curve": args.curve,
         "steps": args.steps, "warmup_steps": args.warmup, "ms_per_step": round(ms, 3),
         "energy_before": e0, "energy_after": e1, "rel_energy_change": (e1 - e0) / abs(e0),
         "kinetic_before": d0["kinetic"], "kinetic_after": d1["kinetic"],
@@ -310,7 +314,7 @@ def sbh_compare(args):
     uniform in [-1, 1]^3, G = 1, eps = 0, potential errors against the GPU
     direct sum, 8 source seeds (10-17), mean and spread over the seeds.  BH:
     theta = 0.5 (far-field ratio 2), leaf capacity 16; SBH: S = 1 sample per
-    stratum, leaf capacity 1, d = 4 and d = 2.  Times are device times of the
+    stratum, leaf capacity 1, d = 4 and d = 2; Morton keys.  Times are device times of the
     query call (the target ordering included), mean of 5; the build is listed
     apart.  One JSON line per (M, queries, method)."""
     import numpy as np
@@ -379,6 +383,9 @@ def main():
     ap.add_argument("--workload", default="plummer")
     ap.add_argument("--leaf-cap", type=int, default=16)
     ap.add_argument("--key-bits", type=int, default=63)
+    ap.add_argument("--curve", default="hilbert", choices=["morton", "hilbert"],
+                    help="key curve of the tree (sort order of the sources and targets); "
+                         "the same cells either way, Hilbert waves walk fewer nodes")
     ap.add_argument("--theta", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
@@ -434,7 +441,7 @@ def main():
     n = p.shape[0]
     src = torch.from_numpy(p).cuda()
     out = torch.empty((n, 4), dtype=torch.float32, device="cuda")
-    tree = bh.BarnesHut(n, 0, args.key_bits, args.leaf_cap)
+    tree = bh.BarnesHut(n, 0, args.key_bits, args.leaf_cap, curve=args.curve)
 
     def step():
         tree.build(src)
@@ -472,7 +479,7 @@ def main():
     achieved = FLOPS_PER_INTERACTION * interactions / (walk_ms * 1e-3) / 1e12
     roofline = {"bound": "alu", "achieved": round(achieved, 3), "peak": FP32_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK_TFLOPS, 4),
-                "traffic": read_traffic(wname)}
+                "traffic": read_traffic(wname, args.curve)}
 
     rec = {
         "metric": METRIC, "value": value, "unit": "interactions/s", "n_gpus": 1,
@@ -481,6 +488,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wname, "n": n, "theta": prm["theta"], "G": prm["G"],
                    "eps": prm["eps"], "leaf_cap": args.leaf_cap, "key_bits": args.key_bits,
+                   "key_curve": args.curve,
                    "interactions_per_step": interactions,
                    "walk_ms": round(walk_ms, 4),
                    "phase_ms": {k: round(v, 4) for k, v in zip(

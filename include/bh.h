@@ -46,6 +46,15 @@ typedef enum bh_status {
     BH_ERR_CONTENTION = -7  /* bh_build_locked: an insertion ran out of retries */
 } bh_status;
 
+/* Key curves: the order in which sources are sorted and siblings appear in the
+ * node array.  Morton is the Z-order of [Tree] 实现步骤; Hilbert visits the same
+ * cells (each still one contiguous run of the order) with every step between
+ * neighbouring cells, so the 64 consecutive targets of a wave are more compact
+ * and the walk visits fewer nodes.  Results differ only by rounding (the same
+ * cells, summed in another order). */
+#define BH_CURVE_MORTON 0
+#define BH_CURVE_HILBERT 1
+
 /* Build parameters, fixed for the life of a context.
  *   key_bits      63 (21 bits per axis) or 30 (10 bits per axis): the depth of
  *                 the Morton key of [Tree] 实现步骤 and the deepest tree level.
@@ -53,17 +62,24 @@ typedef enum bh_status {
  *                 octants unless it is at the deepest level ([Tree] 实现步骤: a
  *                 leaf holds a few particles).  At most 256.
  *   node_capacity maximum number of tree nodes; 0 selects the worst case
- *                 max_sources * (key_bits/3 + 1) + 1, which can never overflow. */
+ *                 max_sources * (key_bits/3 + 1) + 1, which can never overflow.
+ *   key_curve     BH_CURVE_MORTON (default) or BH_CURVE_HILBERT (keys after
+ *                 Skilling, "Programming the Hilbert curve", 2004); bh_get_keys
+ *                 returns keys of this curve.  Separate targets are ordered by
+ *                 the same curve. */
 typedef struct bh_build_params {
     int32_t key_bits;
     int32_t leaf_cap;
     int64_t node_capacity;
+    int32_t key_curve;
+    int32_t reserved;   /* must be 0 */
 } bh_build_params;
 
 /* One tree node as stored on the device (32 bytes), in pre-order: a node's
  * subtree is the index range [self, skip).  Children follow their parent in
- * octant order 0..7, the octant numbering of [Tree] 构建树结构 (x upper half
- * = 1, y = 2, z = 4).  com_x..mass follow [GASPHiA] 计算节点质心. */
+ * key order: octant order 0..7 for Morton keys (the octant numbering of [Tree]
+ * 构建树结构: x upper half = 1, y = 2, z = 4), the curve's order for Hilbert
+ * keys.  com_x..mass follow [GASPHiA] 计算节点质心. */
 typedef struct bh_node {
     float com_x, com_y, com_z;  /* centre of mass (cell centre when mass is 0) */
     float mass;                 /* total mass of the cell */

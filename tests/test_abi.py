@@ -52,8 +52,9 @@ def test_create_rejects_bad_arguments_before_touching_the_device(lib):
     assert lib.bh_create(None, 10, 0, None) == bh.BH_ERR_INVALID
     assert lib.bh_create(ctypes.byref(h), -1, 0, None) == bh.BH_ERR_INVALID
     assert lib.bh_create(ctypes.byref(h), 1 << 31, 0, None) == bh.BH_ERR_INVALID
-    for kb, B in ((31, 16), (63, 0), (63, 257)):
-        p = bh._Params(kb, B, 0)
+    for kb, B, curve, res in ((31, 16, 0, 0), (63, 0, 0, 0), (63, 257, 0, 0), (63, 16, 2, 0),
+                              (63, 16, 0, 1)):
+        p = bh._Params(kb, B, 0, curve, res)
         assert lib.bh_create(ctypes.byref(h), 10, 0, ctypes.byref(p)) == bh.BH_ERR_INVALID
     assert lib.bh_build(None, None, 0, None) == bh.BH_ERR_INVALID
     assert lib.bh_gravity(None, None, 0, 0.5, 1.0, 0.0, None, None) == bh.BH_ERR_INVALID

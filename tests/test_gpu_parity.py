@@ -35,9 +35,10 @@ def log(*a):
     print(*a, flush=True)
 
 
-def make_tree(p, key_bits=63, leaf_cap=16, max_targets=0, node_capacity=0):
+def make_tree(p, key_bits=63, leaf_cap=16, max_targets=0, node_capacity=0, curve="morton"):
     import barnes_hut_tree_amd as bh
-    t = bh.BarnesHut(max(p.shape[0], 1), max_targets, key_bits, leaf_cap, node_capacity)
+    t = bh.BarnesHut(max(p.shape[0], 1), max_targets, key_bits, leaf_cap, node_capacity,
+                     curve=curve)
     t.build(torch.from_numpy(p).cuda())
     t.sync()
     return t
@@ -193,12 +194,13 @@ def test_repeat_runs_bit_identical():
 # full-size workloads, in the benchmark's launch configuration, on a sample
 # of targets the oracle evaluates one by one
 # ---------------------------------------------------------------------------
-def _sampled_parity(orc, p, theta, eps, B, n_sample, seed, label, key_bits=63, direct=True):
-    t = make_tree(p, key_bits=key_bits, leaf_cap=B)
+def _sampled_parity(orc, p, theta, eps, B, n_sample, seed, label, key_bits=63, direct=True,
+                    curve="morton"):
+    t = make_tree(p, key_bits=key_bits, leaf_cap=B, curve=curve)
     got = t.gravity(theta, 1.0, eps).cpu().numpy()
     assert np.all(np.isfinite(got)), label
     which = np.sort(np.random.default_rng(seed).choice(p.shape[0], n_sample, replace=False))
-    ref = orc.Tree(p, key_bits=key_bits, leaf_cap=B)
+    ref = orc.Tree(p, key_bits=key_bits, leaf_cap=B, curve=curve)
     modes = [ref.gravity(theta, 1.0, eps, which=which, tie_mode=m) for m in (0, 1, 2)]
     ties = modes[0][2]
     p99a, p99p = assert_walk_parity(got[which], [m[0] for m in modes], ties, label)
