@@ -121,62 +121,80 @@ __device__ inline uint64_t spread3(uint64_t v)
 }
 
 
-// Hilbert index of 21-bit-or-less integer coordinates, after Skilling,
+// Hilbert index of BITS-bit integer coordinates, after Skilling,
 // "Programming the Hilbert curve" (AIP Conf. Proc. 707, 2004): the transposed
 // index is formed in place (undo excess work from the top bit down, then Gray
 // encoding) and its bits are interleaved x, y, z from the most significant
 // end, so each 3-bit digit names a child cell in the curve's order.  Every
 // cell is still one contiguous key range: the tree is the same, only the
 // order of siblings changes.
-__device__ inline uint64_t hilbert3(uint32_t x, uint32_t y, uint32_t z, int bits)
+//
+// The level loop is unrolled for the two key widths, each level's choices
+// are selects rather than branches, and the final correction (bit i of t is
+// the parity of the bits of z above i) is a suffix-parity of z >> 1 in five
+// shift-xor steps.
+template <int BITS>
+__device__ inline uint64_t hilbert3(uint32_t x, uint32_t y, uint32_t z)
 {
-    const uint32_t M = 1u << (bits - 1);
-    for (uint32_t Q = M; Q > 1; Q >>= 1) {
-        const uint32_t P = Q - 1;
-        if (x & Q) x ^= P;
-        if (y & Q) {
-            x ^= P;
-        } else {
+#pragma unroll
+    for (int q = BITS - 1; q >= 1; --q) {
+        const uint32_t P = (1u << q) - 1u;
+        x ^= ((x >> q) & 1u) ? P : 0u;
+        {
             const uint32_t t = (x ^ y) & P;
-            x ^= t;
-            y ^= t;
+            const bool set = (y >> q) & 1u;
+            x ^= set ? P : t;
+            y ^= set ? 0u : t;
         }
-        if (z & Q) {
-            x ^= P;
-        } else {
+        {
             const uint32_t t = (x ^ z) & P;
-            x ^= t;
-            z ^= t;
+            const bool set = (z >> q) & 1u;
+            x ^= set ? P : t;
+            z ^= set ? 0u : t;
         }
     }
     y ^= x;
     z ^= y;
-    uint32_t t = 0;
-    for (uint32_t Q = M; Q > 1; Q >>= 1)
-        if (z & Q) t ^= Q - 1;
+    uint32_t t = z >> 1;
+    t ^= t >> 1;
+    t ^= t >> 2;
+    t ^= t >> 4;
+    t ^= t >> 8;
+    t ^= t >> 16;
     x ^= t;
     y ^= t;
     z ^= t;
     return spread3(z) | (spread3(y) << 1) | (spread3(x) << 2);
 }
 
-template <bool HILBERT>
+template <bool HILBERT, int BITS>
 __global__ __launch_bounds__(256) void k_morton(const float4 *__restrict__ pts, uint32_t n,
-                                                const DevParams *__restrict__ prm, int bits,
+                                                const DevParams *__restrict__ prm,
                                                 uint64_t *__restrict__ keys,
                                                 uint32_t *__restrict__ idx)
 {
     const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     const float4 p = pts[i];
-    const uint64_t top = (1ull << bits) - 1;
+    const uint64_t top = (1ull << BITS) - 1;
     const double s = prm->scale;
     const uint64_t qx = quantise(p.x, prm->lo[0], s, top);
     const uint64_t qy = quantise(p.y, prm->lo[1], s, top);
     const uint64_t qz = quantise(p.z, prm->lo[2], s, top);
-    keys[i] = HILBERT ? hilbert3((uint32_t)qx, (uint32_t)qy, (uint32_t)qz, bits)
+    keys[i] = HILBERT ? hilbert3<BITS>((uint32_t)qx, (uint32_t)qy, (uint32_t)qz)
                       : spread3(qx) | (spread3(qy) << 1) | (spread3(qz) << 2);
     idx[i] = i;
+}
+
+template <bool HILBERT>
+void launch_keys(const float4 *pts, uint32_t n, const DevParams *prm, int bits, uint64_t *keys,
+                 uint32_t *idx, hipStream_t s)
+{
+    const dim3 grid((n + 255) / 256), block(256);
+    if (bits == 21)
+        hipLaunchKernelGGL((k_morton<HILBERT, 21>), grid, block, 0, s, pts, n, prm, keys, idx);
+    else
+        hipLaunchKernelGGL((k_morton<HILBERT, 10>), grid, block, 0, s, pts, n, prm, keys, idx);
 }
 
 }  // namespace
@@ -202,12 +220,9 @@ void launch_morton(const float4 *pts, uint32_t n, const DevParams *prm, int bits
                    uint64_t *keys, uint32_t *idx, hipStream_t s)
 {
     if (n == 0) return;
-    if (curve == 1)
-        hipLaunchKernelGGL(k_morton<true>, dim3((n + 255) / 256), dim3(256), 0, s, pts, n, prm,
-                           bits, keys, idx);
-    else
-        hipLaunchKernelGGL(k_morton<false>, dim3((n + 255) / 256), dim3(256), 0, s, pts, n, prm,
-                           bits, keys, idx);
+    // bits is 21 (63-bit keys) or 10 (30-bit keys); bh_create admits no other
+    if (curve == 1) launch_keys<true>(pts, n, prm, bits, keys, idx, s);
+    else launch_keys<false>(pts, n, prm, bits, keys, idx, s);
 }
 
 }  // namespace bh

@@ -69,7 +69,7 @@ hipError_t dalloc(T **p, size_t count)
 void free_all(bh_ctx *c)
 {
     void *ptrs[] = {c->prm, c->bbox_part, c->keys, c->keys_alt, c->vals, c->vals_alt, c->spine,
-                    c->spos, c->bw.dc, c->bw.tile_counts, c->bw.tile_sums, c->bw.tile_scan,
+                    c->spos, c->bw.dc, c->bw.tile_counts, c->bw.tile_sums, c->bw.chunk_tot, c->bw.tile_scan,
                     c->bw.first_node, c->bw.P, c->nodes, c->tkeys, c->tkeys_alt, c->tvals,
                     c->tvals_alt, c->tspine, c->tpos, c->inv, c->diag, c->lk_child,
                     c->lk_level, c->lk_next, c->lk_counter};
@@ -155,6 +155,7 @@ bh_status bh_create(bh_ctx **out, int64_t max_sources, int64_t max_targets,
     ok &= dalloc(&c->bw.dc, ns) == hipSuccess;
     ok &= dalloc(&c->bw.tile_counts, tiles) == hipSuccess;
     ok &= dalloc(&c->bw.tile_sums, tiles) == hipSuccess;
+    ok &= dalloc(&c->bw.chunk_tot, tiles + 1) == hipSuccess;
     ok &= dalloc(&c->bw.tile_scan, tiles + 1) == hipSuccess;
     ok &= dalloc(&c->bw.first_node, ns + 1) == hipSuccess;
     ok &= dalloc(&c->bw.P, ns + 1) == hipSuccess;

@@ -54,16 +54,28 @@ static_assert(sizeof(Node) == sizeof(bh_node), "node matches the public record")
 constexpr uint32_t kLeafBit = 1u << 8;
 __host__ __device__ inline uint32_t node_level(uint32_t meta) { return meta & 0xffu; }
 
-// Radix sort geometry: a tile of 2048 keys per workgroup of 256 threads.
+// Radix sort geometry: a tile of 2048 keys per workgroup of 256 threads, or
+// 4096 from kSortLargeN keys on (the spine is sized for the smaller tile).
 constexpr int kSortThreads = 256;
 constexpr int kSortItems = 8;
+constexpr int kSortItemsLarge = 16;
+constexpr uint32_t kSortLargeN = 1u << 22;
 constexpr int kSortTile = kSortThreads * kSortItems;
 constexpr int kRadix = 256;
+
+// Workgroups are dispatched to the 8 XCDs round-robin (block b to XCD b mod 8).
+// xcd_block(b, nb) renumbers them so each XCD takes one contiguous run of the
+// nb work items, and work items that share data share that XCD's L2.
+__device__ inline uint32_t xcd_block(uint32_t b, uint32_t nb)
+{
+    const uint32_t x = b & 7u, k = b >> 3, q = nb >> 3, r = nb & 7u;
+    return x * q + min(x, r) + k;
+}
 
 // Tree build geometry: 1024 key positions per workgroup of 256 threads.
 constexpr int kBuildThreads = 256;
 constexpr int kBuildTile = 1024;
-constexpr int kTileScanThreads = 256;
+constexpr int kTileScanThreads = 1024;
 
 // Quantised coordinate of x on the root cube: floor((x - lo) * scale) in fp64,
 // each step one correctly rounded IEEE operation, clamped to [0, top] (below the
@@ -110,7 +122,8 @@ struct BuildScratch {
     uint16_t *dc;           // per position: d + 1 (low byte), nodes starting there (high byte)
     uint32_t *tile_counts;  // per tile: nodes starting in the tile
     D4 *tile_sums;          // per tile: particle sums
-    TileScan *tile_scan;    // per tile: exclusive prefix; [n_tiles] = totals
+    TileScan *chunk_tot;    // per chunk of tiles: node count and particle sums
+    TileScan *tile_scan;    // per chunk: exclusive prefix; [n_chunks] = totals
     uint32_t *first_node;   // per position (and n): pre-order index of the first node there
     D4 *P;                  // per position (and n): prefix sums of (m, m (x - lo))
 };

@@ -157,11 +157,104 @@ __device__ inline uint32_t wave_incl_scan(uint32_t v)
     return v;
 }
 
-// tiles: the exclusive scan over tiles of the node counts and particle sums.
+// The exclusive scan over tiles of (node count, particle sums) is split so
+// that every access is coalesced and no single workgroup walks all tiles.
+// Tiles are grouped in chunks of chunk_tiles(n_tiles) consecutive tiles (a
+// multiple of 64, at most kTileScanThreads chunks).  k_chunk_totals reduces
+// each chunk with one wave (64 consecutive tiles per load); k_scan_chunks,
+// one workgroup, scans the chunk totals: out[c] = the sum of the chunks
+// before c, out[n_chunks] = the totals.  Each emit workgroup then adds the
+// tiles before its own within its chunk.
+__device__ inline void wave_sum_tiles(const uint32_t *__restrict__ counts,
+                                      const D4 *__restrict__ sums, uint32_t b, uint32_t e,
+                                      uint32_t &c, D4 &m)
+{
+    const uint32_t lane = threadIdx.x & 63;
+    c = 0;
+    m = D4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 1
+    for (uint32_t t = b + lane; t < e; t += 64) {
+        c += counts[t];
+        m = m + sums[t];
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+        c += __shfl_xor(c, o, 64);
+        m = m + D4{__shfl_xor(m.m, o, 64), __shfl_xor(m.x, o, 64), __shfl_xor(m.y, o, 64),
+                   __shfl_xor(m.z, o, 64)};
+    }
+}
+
+// one wave per chunk
+__global__ __launch_bounds__(64) void k_chunk_totals(const uint32_t *__restrict__ counts,
+                                                     const D4 *__restrict__ sums,
+                                                     uint32_t n_tiles, uint32_t chunk,
+                                                     TileScan *__restrict__ tot)
+{
+    const uint32_t k = blockIdx.x;
+    uint32_t c;
+    D4 m;
+    wave_sum_tiles(counts, sums, k * chunk, min(n_tiles, (k + 1) * chunk), c, m);
+    if (threadIdx.x == 0) {
+        tot[k].nodes = c;
+        tot[k].sums = m;
+    }
+}
+
+__global__ __launch_bounds__(kTileScanThreads) void k_scan_chunks(
+    const TileScan *__restrict__ tot, uint32_t n_chunks, TileScan *__restrict__ out)
+{
+    constexpr int kWavesScan = kTileScanThreads / 64;
+    __shared__ D4 wsum[kWavesScan + 1];
+    __shared__ uint32_t wcnt[kWavesScan + 1];
+    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t k = threadIdx.x;
+    const uint32_t c = k < n_chunks ? tot[k].nodes : 0u;
+    const D4 m = k < n_chunks ? tot[k].sums : D4{0.0, 0.0, 0.0, 0.0};
+    const uint32_t ic = wave_incl_scan(c);
+    const D4 im = wave_incl_scan_d4(m);
+    if (lane == 63) {
+        wcnt[wave] = ic;
+        wsum[wave] = im;
+    }
+    __syncthreads();
+    // the first wave turns the wave totals into exclusive prefixes
+    if (wave == 0) {
+        const uint32_t c2 = lane < kWavesScan ? wcnt[lane] : 0u;
+        const D4 m2 = lane < kWavesScan ? wsum[lane] : D4{0.0, 0.0, 0.0, 0.0};
+        const uint32_t ic2 = wave_incl_scan(c2);
+        const D4 im2 = wave_incl_scan_d4(m2);
+        if (lane < kWavesScan) {
+            wcnt[lane] = ic2 - c2;
+            wsum[lane] = im2 - m2;
+        }
+        if (lane == kWavesScan - 1) {
+            wcnt[kWavesScan] = ic2;
+            wsum[kWavesScan] = im2;
+        }
+    }
+    __syncthreads();
+    const uint32_t rc = ic - c + wcnt[wave], tc = wcnt[kWavesScan];
+    const D4 rm = (im - m) + wsum[wave], tm = wsum[kWavesScan];
+    if (k < n_chunks) {
+        out[k].nodes = rc;
+        out[k].sums = rm;
+    }
+    if (k == 0) {
+        out[n_chunks].nodes = tc;
+        out[n_chunks].sums = tm;
+    }
+}
+
+// chunk_pref: the exclusive scan over chunks of the tiles' node counts and
+// particle sums ([n_chunks] = the totals); the tiles before this one in its
+// chunk are added here.
 __global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restrict__ dc,
                                                         const float4 *__restrict__ spos, uint32_t n,
-                                                        const TileScan *__restrict__ tiles,
-                                                        uint32_t n_tiles, uint64_t cap,
+                                                        const uint32_t *__restrict__ tile_counts,
+                                                        const D4 *__restrict__ tile_sums,
+                                                        const TileScan *__restrict__ chunk_pref,
+                                                        uint32_t n_tiles, uint32_t chunk,
+                                                        uint64_t cap,
                                                         uint32_t *__restrict__ first_node,
                                                         D4 *__restrict__ P,
                                                         Node *__restrict__ nodes,
@@ -170,8 +263,21 @@ __global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restri
     constexpr int per = kBuildTile / kBuildThreads;  // consecutive positions per thread
     __shared__ uint32_t wtot[kBuildThreads / 64];
     __shared__ D4 wsum[kBuildThreads / 64];
+    __shared__ uint32_t tile_nodes;
+    __shared__ D4 tile_mass;
     const uint32_t blk = blockIdx.x;
-    const uint32_t total = tiles[n_tiles].nodes;   // all nodes
+    const uint32_t n_chunks = (n_tiles + chunk - 1) / chunk;
+    const uint32_t total = chunk_pref[n_chunks].nodes;   // all nodes
+    if (threadIdx.x < 64) {
+        const uint32_t c0 = blk / chunk;
+        uint32_t c;
+        D4 m;
+        wave_sum_tiles(tile_counts, tile_sums, c0 * chunk, blk, c, m);
+        if (threadIdx.x == 0) {
+            tile_nodes = chunk_pref[c0].nodes + c;
+            tile_mass = chunk_pref[c0].sums + m;
+        }
+    }
 
     const int64_t a0 = (int64_t)blk * kBuildTile + per * threadIdx.x;
     int dd[per], cc[per];
@@ -195,8 +301,8 @@ __global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restri
         wsum[wave] = mincl;
     }
     __syncthreads();
-    uint32_t run = tiles[blk].nodes;
-    D4 mrun = tiles[blk].sums;
+    uint32_t run = tile_nodes;
+    D4 mrun = tile_mass;
     for (uint32_t w = 0; w < wave; ++w) {
         run += wtot[w];
         mrun = mrun + wsum[w];
@@ -222,69 +328,11 @@ __global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restri
     }
     if (blk == n_tiles - 1 && threadIdx.x == 0) {
         first_node[n] = total;
-        P[n] = tiles[n_tiles].sums;
+        P[n] = chunk_pref[n_chunks].sums;
     }
     if (blk == 0 && threadIdx.x == 0) {
         prm->n_nodes = total;
         if (total > cap) prm->status |= kStatusCapacity;
-    }
-}
-
-// Exclusive scan over the tiles of (node count, particle sums), one
-// workgroup; tiles[n_tiles] receives the totals.  Each thread sums a
-// contiguous run of tiles, the first wave scans the per-thread totals, and
-// each thread rescans its run.
-__global__ __launch_bounds__(kTileScanThreads) void k_scan_tiles(
-    const uint32_t *__restrict__ counts, const D4 *__restrict__ sums, uint32_t n_tiles,
-    TileScan *__restrict__ out)
-{
-    __shared__ D4 tsum[kTileScanThreads];
-    __shared__ uint32_t tcnt[kTileScanThreads];
-    const uint32_t chunk = (n_tiles + kTileScanThreads - 1) / kTileScanThreads;
-    const uint32_t b = min(n_tiles, threadIdx.x * chunk), e = min(n_tiles, b + chunk);
-    uint32_t c = 0;
-    D4 m = {0.0, 0.0, 0.0, 0.0};
-    for (uint32_t t = b; t < e; ++t) {
-        c += counts[t];
-        m = m + sums[t];
-    }
-    tcnt[threadIdx.x] = c;
-    tsum[threadIdx.x] = m;
-    __syncthreads();
-    if (threadIdx.x < 64) {
-        // lane k owns per-thread totals [k*R, k*R + R)
-        constexpr int R = kTileScanThreads / 64;
-        uint32_t lc = 0;
-        D4 lm = {0.0, 0.0, 0.0, 0.0};
-        for (int r = 0; r < R; ++r) {
-            lc += tcnt[threadIdx.x * R + r];
-            lm = lm + tsum[threadIdx.x * R + r];
-        }
-        const uint32_t ic = wave_incl_scan(lc);
-        const D4 im = wave_incl_scan_d4(lm);
-        uint32_t rc = ic - lc;
-        D4 rm = im - lm;
-        for (int r = 0; r < R; ++r) {
-            const uint32_t vc = tcnt[threadIdx.x * R + r];
-            const D4 vm = tsum[threadIdx.x * R + r];
-            tcnt[threadIdx.x * R + r] = rc;
-            tsum[threadIdx.x * R + r] = rm;
-            rc += vc;
-            rm = rm + vm;
-        }
-        if (threadIdx.x == 63) {
-            out[n_tiles].nodes = rc;
-            out[n_tiles].sums = rm;
-        }
-    }
-    __syncthreads();
-    c = tcnt[threadIdx.x];
-    m = tsum[threadIdx.x];
-    for (uint32_t t = b; t < e; ++t) {
-        out[t].nodes = c;
-        out[t].sums = m;
-        c += counts[t];
-        m = m + sums[t];
     }
 }
 
@@ -356,6 +404,14 @@ uint32_t grid_for(uint64_t items, uint32_t max_blocks)
 
 }  // namespace
 
+// Tiles per chunk of the tile scan: a multiple of 64, with at most
+// kTileScanThreads chunks.
+static uint32_t chunk_tiles(uint32_t tiles)
+{
+    const uint32_t per = (tiles + kTileScanThreads - 1) / kTileScanThreads;
+    return ((per + 63) / 64) * 64;
+}
+
 uint32_t build_blocks(uint32_t n)
 {
     uint32_t t = (n + kBuildTile - 1) / kBuildTile;
@@ -369,11 +425,17 @@ void build_tree(const uint64_t *keys_sorted, const float4 *spos, uint32_t n, int
     const uint32_t tiles = build_blocks(n);
     hipLaunchKernelGGL(k_count, dim3(tiles), dim3(kBuildThreads), 0, s, keys_sorted, spos, n, bits,
                        leaf_cap, w.dc, w.tile_counts, w.tile_sums, (const DevParams *)prm);
-    hipLaunchKernelGGL(k_scan_tiles, dim3(1), dim3(kTileScanThreads), 0, s,
-                       (const uint32_t *)w.tile_counts, (const D4 *)w.tile_sums, tiles, w.tile_scan);
+    const uint32_t chunk = chunk_tiles(tiles);
+    const uint32_t n_chunks = (tiles + chunk - 1) / chunk;
+    hipLaunchKernelGGL(k_chunk_totals, dim3(n_chunks), dim3(64), 0, s,
+                       (const uint32_t *)w.tile_counts, (const D4 *)w.tile_sums, tiles, chunk,
+                       w.chunk_tot);
+    hipLaunchKernelGGL(k_scan_chunks, dim3(1), dim3(kTileScanThreads), 0, s,
+                       (const TileScan *)w.chunk_tot, n_chunks, w.tile_scan);
     hipLaunchKernelGGL(k_emit, dim3(tiles), dim3(kBuildThreads), 0, s, (const uint16_t *)w.dc, spos,
-                       n, (const TileScan *)w.tile_scan, tiles, node_capacity, w.first_node, w.P,
-                       nodes, prm);
+                       n, (const uint32_t *)w.tile_counts, (const D4 *)w.tile_sums,
+                       (const TileScan *)w.tile_scan, tiles, chunk, node_capacity, w.first_node,
+                       w.P, nodes, prm);
     hipLaunchKernelGGL(k_ranges, dim3(grid_for(n, 2048)), dim3(256), 0, s, keys_sorted, spos,
                        (const D4 *)w.P, n, bits, node_capacity, (const uint32_t *)w.first_node,
                        nodes, (const DevParams *)prm);

@@ -49,6 +49,9 @@ __device__ inline uint32_t block_excl_scan_256(uint32_t v, uint32_t *tmp, uint32
     return off + incl - v;
 }
 
+// Per-tile digit counts.  All ITEMS keys of a thread are loaded before the
+// first LDS update, so a wave has its whole share of the tile in flight.
+template <int ITEMS>
 __global__ __launch_bounds__(kSortThreads) void k_hist(const uint64_t *__restrict__ keys, uint32_t n,
                                                        int shift, uint32_t *__restrict__ hist,
                                                        uint32_t n_tiles)
@@ -56,32 +59,39 @@ __global__ __launch_bounds__(kSortThreads) void k_hist(const uint64_t *__restric
     __shared__ uint32_t h[kWaves][kRadix];
     const uint32_t wave = threadIdx.x >> 6;
     for (int d = threadIdx.x; d < kWaves * kRadix; d += kSortThreads) (&h[0][0])[d] = 0;
-    __syncthreads();
-    const uint32_t base = blockIdx.x * kSortTile;
-#pragma unroll 4
-    for (int k = 0; k < kSortItems; ++k) {
-        uint32_t i = base + k * kSortThreads + threadIdx.x;
-        if (i < n) atomicAdd(&h[wave][(keys[i] >> shift) & 0xff], 1u);
+    const uint32_t tile = xcd_block(blockIdx.x, n_tiles);
+    const uint32_t base = tile * (kSortThreads * ITEMS);
+    uint32_t digit[ITEMS];
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+        const uint32_t i = base + k * kSortThreads + threadIdx.x;
+        digit[k] = i < n ? (uint32_t)(keys[i] >> shift) & 0xffu : kRadix;
     }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k)
+        if (digit[k] < kRadix) atomicAdd(&h[wave][digit[k]], 1u);
     __syncthreads();
     const uint32_t d = threadIdx.x;
     uint32_t c = 0;
     for (int w = 0; w < kWaves; ++w) c += h[w][d];
-    hist[d * n_tiles + blockIdx.x] = c;
+    hist[d * n_tiles + tile] = c;
 }
 
-template <bool GATHER>
+template <bool GATHER, int ITEMS>
 __global__ __launch_bounds__(kSortThreads) void k_scatter(
     const uint64_t *__restrict__ kin, const uint32_t *__restrict__ vin,
     uint64_t *__restrict__ kout, uint32_t *__restrict__ vout, uint32_t n, int shift,
     const uint32_t *__restrict__ row_pref, const uint32_t *__restrict__ row_tot,
     uint32_t n_tiles, const float4 *__restrict__ gsrc, float4 *__restrict__ gdst)
 {
-    __shared__ uint64_t skey[kSortTile];
-    __shared__ uint32_t sval[kSortTile];
+    constexpr uint32_t kTile = kSortThreads * ITEMS;
+    __shared__ uint64_t skey[kTile];
+    __shared__ uint32_t sval[kTile];
+    // per wave and digit: the count, then the tile position of the wave's
+    // first key of that digit; in the last phase, row 0 holds per digit the
+    // output position minus the tile position
     __shared__ uint32_t wcnt[kWaves][kRadix];
-    __shared__ uint32_t bstart[kRadix];
-    __shared__ uint32_t gbase[kRadix];
     __shared__ uint32_t tmp[kWaves];
 
     const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
@@ -89,21 +99,22 @@ __global__ __launch_bounds__(kSortThreads) void k_scatter(
     for (int d = threadIdx.x; d < kWaves * kRadix; d += kSortThreads) (&wcnt[0][0])[d] = 0;
     __syncthreads();
 
-    // Each wave owns 1024 consecutive keys of the tile; row k holds keys
-    // [k*64, k*64+64) of that range, so (wave, row, lane) is input order.
-    const uint32_t base = blockIdx.x * kSortTile + wave * (kSortItems * 64);
-    uint64_t key[kSortItems];
-    uint32_t val[kSortItems];
-    uint32_t rank[kSortItems];
+    // Each wave owns ITEMS * 64 consecutive keys of the tile; row k holds
+    // keys [k*64, k*64+64) of that range, so (wave, row, lane) is input order.
+    const uint32_t tile = xcd_block(blockIdx.x, n_tiles);
+    const uint32_t base = tile * kTile + wave * (ITEMS * 64);
+    uint64_t key[ITEMS];
+    uint32_t val[ITEMS];
+    uint32_t rank[ITEMS];
 #pragma unroll
-    for (int k = 0; k < kSortItems; ++k) {
+    for (int k = 0; k < ITEMS; ++k) {
         const uint32_t i = base + k * 64 + lane;
         const bool valid = i < n;
         key[k] = valid ? kin[i] : 0;
         val[k] = valid ? vin[i] : 0;
     }
 #pragma unroll
-    for (int k = 0; k < kSortItems; ++k) {
+    for (int k = 0; k < ITEMS; ++k) {
         const uint32_t i = base + k * 64 + lane;
         const bool valid = i < n;
         const uint32_t digit = (uint32_t)(key[k] >> shift) & 0xffu;
@@ -121,47 +132,52 @@ __global__ __launch_bounds__(kSortThreads) void k_scatter(
     }
     __syncthreads();
 
-    // Per digit: the exclusive prefix over waves, and the tile-local start.
+    // Per digit: the tile-local start plus the exclusive prefix over waves,
+    // and the shift from tile position to output position.
+    uint32_t gshift;
     {
         const uint32_t d = threadIdx.x;
         uint32_t run = 0;
+        for (int w = 0; w < kWaves; ++w) run += wcnt[w][d];
+        uint32_t total;
+        const uint32_t start = block_excl_scan_256(run, tmp, &total);
+        run = start;
         for (int w = 0; w < kWaves; ++w) {
-            uint32_t c = wcnt[w][d];
+            const uint32_t c = wcnt[w][d];
             wcnt[w][d] = run;
             run += c;
         }
-        uint32_t total;
-        const uint32_t start = block_excl_scan_256(run, tmp, &total);
-        bstart[d] = start;
         // global start of digit d for this tile: all smaller digits, plus
         // digit d in earlier tiles
         const uint32_t digit_base = block_excl_scan_256(row_tot[d], tmp, &total);
-        gbase[d] = digit_base + row_pref[d * n_tiles + blockIdx.x];
+        gshift = digit_base + row_pref[d * n_tiles + tile] - start;
     }
     __syncthreads();
 
 #pragma unroll
-    for (int k = 0; k < kSortItems; ++k) {
+    for (int k = 0; k < ITEMS; ++k) {
         const uint32_t i = base + k * 64 + lane;
         if (i < n) {
             const uint32_t digit = (uint32_t)(key[k] >> shift) & 0xffu;
-            const uint32_t pos = bstart[digit] + wcnt[wave][digit] + rank[k];
+            const uint32_t pos = wcnt[wave][digit] + rank[k];
             skey[pos] = key[k];
             sval[pos] = val[k];
         }
     }
     __syncthreads();
+    wcnt[0][threadIdx.x] = gshift;
+    __syncthreads();
 
-    const uint32_t tile_base = blockIdx.x * kSortTile;
-    const uint32_t tile_n = min((uint32_t)kSortTile, n - tile_base);
+    const uint32_t tile_base = tile * kTile;
+    const uint32_t tile_n = min(kTile, n - tile_base);
 #pragma unroll 4
-    for (int k = 0; k < kSortItems; ++k) {
+    for (int k = 0; k < ITEMS; ++k) {
         const uint32_t j = k * kSortThreads + threadIdx.x;
         if (j < tile_n) {
             const uint64_t kk = skey[j];
             const uint32_t vv = sval[j];
             const uint32_t digit = (uint32_t)(kk >> shift) & 0xffu;
-            const uint32_t g = gbase[digit] + (j - bstart[digit]);
+            const uint32_t g = wcnt[0][digit] + j;
             kout[g] = kk;
             vout[g] = vv;
             if (GATHER) gdst[g] = gsrc[vv];
@@ -208,32 +224,55 @@ void launch_scan_rows(const uint32_t *in, uint32_t *pref, uint32_t *tot, uint32_
     hipLaunchKernelGGL(k_scan_rows, dim3(rows), dim3(kScanThreads), 0, s, in, pref, tot, len);
 }
 
+namespace {
+
+template <int ITEMS>
+void sort_passes(uint64_t *&ka, uint32_t *&va, uint64_t *&kb, uint32_t *&vb, uint32_t n,
+                 int key_bits, uint32_t *spine, const float4 *gather_src, float4 *gather_dst,
+                 hipStream_t s)
+{
+    constexpr uint32_t tile = kSortThreads * ITEMS;
+    const uint32_t tiles = (n + tile - 1) / tile;
+    const uint32_t entries = kRadix * tiles;
+    uint32_t *hist = spine, *pref = spine + entries, *tot = spine + 2 * entries;
+    const int passes = (key_bits + 7) / 8;
+    for (int p = 0; p < passes; ++p) {
+        const int shift = 8 * p;
+        const bool last = (p == passes - 1);
+        hipLaunchKernelGGL(k_hist<ITEMS>, dim3(tiles), dim3(kSortThreads), 0, s, ka, n, shift,
+                           hist, tiles);
+        launch_scan_rows(hist, pref, tot, kRadix, tiles, s);
+        if (last && gather_src) {
+            hipLaunchKernelGGL((k_scatter<true, ITEMS>), dim3(tiles), dim3(kSortThreads), 0, s, ka,
+                               va, kb, vb, n, shift, pref, tot, tiles, gather_src, gather_dst);
+        } else {
+            hipLaunchKernelGGL((k_scatter<false, ITEMS>), dim3(tiles), dim3(kSortThreads), 0, s,
+                               ka, va, kb, vb, n, shift, pref, tot, tiles,
+                               (const float4 *)nullptr, (float4 *)nullptr);
+        }
+        uint64_t *tk = ka; ka = kb; kb = tk;
+        uint32_t *tv = va; va = vb; vb = tv;
+    }
+}
+
+}  // namespace
+
+// Small inputs take 2048-key tiles (enough workgroups to fill the device);
+// large ones 4096-key tiles, whose digit runs are twice as long, so more of
+// the scattered writes fill whole cache lines.
 void radix_sort(uint64_t *keys, uint32_t *vals, uint64_t *keys_alt, uint32_t *vals_alt,
                 uint64_t **keys_out, uint32_t **vals_out, uint32_t n, int key_bits,
                 uint32_t *spine, const float4 *gather_src, float4 *gather_dst, hipStream_t s)
 {
     uint64_t *ka = keys, *kb = keys_alt;
     uint32_t *va = vals, *vb = vals_alt;
-    const uint32_t tiles = (n + kSortTile - 1) / kSortTile;
-    const uint32_t entries = kRadix * tiles;
-    uint32_t *hist = spine, *pref = spine + entries, *tot = spine + 2 * entries;
-    const int passes = (key_bits + 7) / 8;
-    for (int p = 0; p < passes && n > 0; ++p) {
-        const int shift = 8 * p;
-        const bool last = (p == passes - 1);
-        hipLaunchKernelGGL(k_hist, dim3(tiles), dim3(kSortThreads), 0, s, ka, n, shift, hist,
-                           tiles);
-        launch_scan_rows(hist, pref, tot, kRadix, tiles, s);
-        if (last && gather_src) {
-            hipLaunchKernelGGL(k_scatter<true>, dim3(tiles), dim3(kSortThreads), 0, s, ka, va, kb,
-                               vb, n, shift, pref, tot, tiles, gather_src, gather_dst);
-        } else {
-            hipLaunchKernelGGL(k_scatter<false>, dim3(tiles), dim3(kSortThreads), 0, s, ka, va,
-                               kb, vb, n, shift, pref, tot, tiles, (const float4 *)nullptr,
-                               (float4 *)nullptr);
-        }
-        uint64_t *tk = ka; ka = kb; kb = tk;
-        uint32_t *tv = va; va = vb; vb = tv;
+    if (n > 0) {
+        if (n >= kSortLargeN)
+            sort_passes<kSortItemsLarge>(ka, va, kb, vb, n, key_bits, spine, gather_src,
+                                         gather_dst, s);
+        else
+            sort_passes<kSortItems>(ka, va, kb, vb, n, key_bits, spine, gather_src, gather_dst,
+                                    s);
     }
     *keys_out = ka;
     *vals_out = va;

@@ -28,15 +28,6 @@ namespace {
 
 constexpr int kWalkThreads = 64;
 
-// Blocks are dispatched to the 8 XCDs round-robin; give each XCD a contiguous
-// run of the Morton order so the nodes and particles its waves share stay in
-// that XCD's L2.
-__device__ inline uint32_t xcd_block(uint32_t b, uint32_t nb)
-{
-    const uint32_t x = b & 7u, k = b >> 3, q = nb >> 3, r = nb & 7u;
-    return x * q + min(x, r) + k;
-}
-
 // Direct sum over the sources [b, e) of an opened leaf, eight at a time (one
 // batch of scalar loads per eight).  MINE: the leaf may hold this lane's own
 // particle i, whose mass is masked out.

@@ -59,6 +59,9 @@ KEY_CASES = {
     "ragged4097": lambda: W.plummer(4097, seed=6),
     "ragged65": lambda: W.uniform_cube(65, seed=7),
     "single": lambda: W.uniform_cube(1, seed=8),
+    # above the size from which the sort takes its larger tiles; every key twice
+    "large_ragged": lambda: W.uniform_cube((1 << 22) + 777, seed=11),
+    "large_duplicates": lambda: np.concatenate([W.plummer((1 << 21) + 5, seed=12)] * 2),
 }
 
 
