@@ -75,6 +75,28 @@ __device__ inline D4 wave_incl_scan_d4(D4 v)
     return v;
 }
 
+// Lowest set bit at or above bit s of the 128-bit value hi:lo (s <= 64), as
+// an offset from s; 128 when there is none.
+__device__ inline int first_from(uint64_t lo, uint64_t hi, int s)
+{
+    const uint64_t x = s < 64 ? (lo >> s) : 0ull;
+    if (x != 0) return __builtin_ctzll(x);
+    if (hi != 0) return (64 - s) + __builtin_ctzll(hi);
+    return 128;
+}
+
+// Per position a of the tile: d(a), whether a leaf starts at a, and the
+// number c(a) of nodes starting there (see the file comment).
+//
+// With B <= 64 (WAVE_ROWS), the searches of a position reach at most one
+// 64-position row either side, so they are answered with ballots: each wave
+// takes one row of 64 positions at a time, and for a depth threshold v the
+// masks of d < v over the previous, current and next rows give every lane
+// the nearest cell boundary shallower than v on either side (the level-d(a)
+// cell around a is [last boundary < d(a) before a, first one after a)), and
+// whether (a, a + B] holds one.  The loops run over the distinct values in
+// the row only.  Larger B scans the window position by position.
+template <bool WAVE_ROWS>
 __global__ __launch_bounds__(kBuildThreads) void k_count(const uint64_t *__restrict__ keys,
                                                          const float4 *__restrict__ spos,
                                                          uint32_t n, int bits, int B,
@@ -85,46 +107,95 @@ __global__ __launch_bounds__(kBuildThreads) void k_count(const uint64_t *__restr
 {
     __shared__ int8_t sd[kBuildTile + 2 * kMaxLeafCap + 2];
     __shared__ uint32_t lc;
+    const int W = WAVE_ROWS ? 64 : B;   // window margin either side of the tile
     const int64_t t0 = (int64_t)blockIdx.x * kBuildTile;
-    const int64_t w0 = t0 - B;   // window covers positions [t0 - B, t0 + tile + B]
-    const int wlen = kBuildTile + 2 * B + 1;
+    const int64_t w0 = t0 - W;   // window covers positions [t0 - W, t0 + tile + W]
+    const int wlen = kBuildTile + 2 * W + 1;
     for (int k = threadIdx.x; k < wlen; k += kBuildThreads)
         sd[k] = (int8_t)d_at(keys, w0 + k, n, bits);
     if (threadIdx.x == 0) lc = 0;
     __syncthreads();
 
+    uint32_t my_nodes = 0;
     for (int k = 0; k < kBuildTile / kBuildThreads; ++k) {
         const int off = k * kBuildThreads + threadIdx.x;
         const int64_t a = t0 + off;
-        if (a >= (int64_t)n) break;
-        const int ia = off + B;  // index of a in the window
+        if (WAVE_ROWS) {
+            if (t0 + k * kBuildThreads + (threadIdx.x & ~63) >= (int64_t)n) break;   // whole row past n
+        } else if (a >= (int64_t)n) {
+            break;
+        }
+        const bool valid = a < (int64_t)n;
+        const int ia = off + W;  // index of a in the window
         const int da = sd[ia];
-        int c = 0;
-        bool leaf_start;
-        if (a == 0) {
-            leaf_start = true;
-        } else if (da >= bits) {
-            leaf_start = false;
+        bool leaf_start = false;
+        int ell = bits;
+        if (WAVE_ROWS) {
+            const int l = (int)(threadIdx.x & 63);
+            const int dp = sd[ia - 64], dn = sd[ia + 64];
+            // leaf start: the level-d(a) cell around a holds more than B
+            const bool need = valid && a > 0 && da < bits;
+            leaf_start = valid && a == 0;
+            uint64_t pending = __ballot(need);
+            while (pending) {
+                const int v = __builtin_amdgcn_readlane(da, __builtin_ctzll(pending));
+                const uint64_t mp = __ballot(dp < v), mc = __ballot(da < v), mn = __ballot(dn < v);
+                if (need && da == v) {
+                    const uint64_t below = mc & ((1ull << l) - 1ull);
+                    const int g = below ? l - (63 - __builtin_clzll(below))
+                                        : (mp ? l + 1 + __builtin_clzll(mp) : 1000);
+                    const int f = 1 + first_from(mc, mn, l + 1);
+                    leaf_start = f + g > B;
+                }
+                pending &= ~__ballot(da == v);
+            }
+            // level of the leaf starting at a: the smallest level above d(a)
+            // whose cell starting at a ends within (a, a + B], else bits
+            uint64_t open = __ballot(leaf_start);
+            if (open) {
+                int lmin = leaf_start ? da + 1 : 1000;
+                for (int o = 32; o > 0; o >>= 1) lmin = min(lmin, __shfl_xor(lmin, o, 64));
+                const uint64_t wmask = B >= 64 ? ~0ull : ((1ull << B) - 1ull);
+                for (int lv = lmin; lv < bits && open; ++lv) {
+                    const uint64_t mc = __ballot(da < lv), mn = __ballot(dn < lv);
+                    bool hit = false;
+                    if (leaf_start && ell == bits && lv >= da + 1) {
+                        const int s = l + 1;
+                        const uint64_t win = s < 64 ? ((mc >> s) | (s > 0 ? mn << (64 - s) : 0ull))
+                                                    : mn;
+                        hit = (win & wmask) != 0;
+                        if (hit) ell = lv;
+                    }
+                    open &= ~__ballot(hit);
+                }
+            }
         } else {
-            // size of the level-d(a) cell around a, capped above B
-            int cnt = 1;
-            for (int t = 0; t < B && cnt <= B; ++t) {
-                if (sd[ia - t] >= da) ++cnt; else break;
+            if (a == 0) {
+                leaf_start = true;
+            } else if (da < bits) {
+                // size of the level-d(a) cell around a, capped above B
+                int cnt = 1;
+                for (int t = 0; t < B && cnt <= B; ++t) {
+                    if (sd[ia - t] >= da) ++cnt; else break;
+                }
+                for (int t = 1; t <= B && cnt <= B; ++t) {
+                    if (sd[ia + t] >= da) ++cnt; else break;
+                }
+                leaf_start = cnt > B;
             }
-            for (int t = 1; t <= B && cnt <= B; ++t) {
-                if (sd[ia + t] >= da) ++cnt; else break;
+            if (leaf_start) {
+                int rm = bits;
+                for (int t = 1; t <= B; ++t) rm = min(rm, (int)sd[ia + t]);
+                ell = min(bits, 1 + max(da, rm));
             }
-            leaf_start = cnt > B;
         }
-        if (leaf_start) {
-            int rm = bits;
-            for (int t = 1; t <= B; ++t) rm = min(rm, (int)sd[ia + t]);
-            const int ell = min(bits, 1 + max(da, rm));
-            c = ell - da;
-            atomicAdd(&lc, (uint32_t)c);
-        }
-        dc[a] = (uint16_t)((da + 1) | (c << 8));
+        const int c = leaf_start ? ell - da : 0;
+        my_nodes += (uint32_t)c;
+        if (valid) dc[a] = (uint16_t)((da + 1) | (c << 8));
     }
+    for (int o = 32; o > 0; o >>= 1) my_nodes += __shfl_xor(my_nodes, o, 64);
+    if ((threadIdx.x & 63) == 0) atomicAdd(&lc, my_nodes);
+    __syncthreads();
     // the tile's particle sums, each thread over 4 consecutive positions in
     // the order the emit kernel scans them
     {
@@ -279,19 +350,31 @@ __global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restri
         }
     }
 
-    const int64_t a0 = (int64_t)blk * kBuildTile + per * threadIdx.x;
+    // coalesced loads into LDS: per position its (d, c) word and its mass moment
+    __shared__ D4 mom[kBuildTile];          // moments, then the prefix P
+    __shared__ uint32_t fn[kBuildTile];     // first node at each position
+    __shared__ uint16_t sdc[kBuildTile];
+    const int64_t t0 = (int64_t)blk * kBuildTile;
+    for (int k = 0; k < per; ++k) {
+        const int j = k * kBuildThreads + threadIdx.x;
+        const int64_t a = t0 + j;
+        sdc[j] = a < (int64_t)n ? dc[a] : (uint16_t)0;
+        mom[j] = a < (int64_t)n ? mass_moment(spos[a], prm) : D4{0.0, 0.0, 0.0, 0.0};
+    }
+    __syncthreads();
+
+    // each thread: 4 consecutive positions
+    const int j0 = per * threadIdx.x;
+    const int64_t a0 = t0 + j0;
     int dd[per], cc[per];
-    D4 mm[per];
     uint32_t s = 0;
     D4 ms = {0.0, 0.0, 0.0, 0.0};
     for (int k = 0; k < per; ++k) {
-        const int64_t a = a0 + k;
-        uint16_t v = a < (int64_t)n ? dc[a] : (uint16_t)0;
+        const uint16_t v = sdc[j0 + k];
         dd[k] = (int)(v & 0xffu) - 1;
         cc[k] = v >> 8;
         s += cc[k];
-        mm[k] = a < (int64_t)n ? mass_moment(spos[a], prm) : D4{0.0, 0.0, 0.0, 0.0};
-        ms = ms + mm[k];
+        ms = ms + mom[j0 + k];
     }
     const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t incl = wave_incl_scan(s);
@@ -313,9 +396,10 @@ __global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restri
     for (int k = 0; k < per; ++k) {
         const int64_t a = a0 + k;
         if (a >= (int64_t)n) break;
-        first_node[a] = run;
-        P[a] = mrun;
-        mrun = mrun + mm[k];
+        const D4 mk = mom[j0 + k];
+        fn[j0 + k] = run;
+        mom[j0 + k] = mrun;
+        mrun = mrun + mk;
         for (int j = 0; j < cc[k]; ++j) {
             const int l = dd[k] + 1 + j;
             const uint32_t X = run + j;
@@ -325,6 +409,17 @@ __global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restri
             }
         }
         run += cc[k];
+    }
+    __syncthreads();
+    // coalesced stores; nodes start and end only where a leaf starts, so the
+    // prefix and the first-node index are needed only there
+    for (int k = 0; k < per; ++k) {
+        const int j = k * kBuildThreads + threadIdx.x;
+        const int64_t a = t0 + j;
+        if (a < (int64_t)n && (sdc[j] >> 8) != 0) {
+            first_node[a] = fn[j];
+            P[a] = mom[j];
+        }
     }
     if (blk == n_tiles - 1 && threadIdx.x == 0) {
         first_node[n] = total;
@@ -351,6 +446,65 @@ __device__ inline float3 cell_centre(float4 p, int level, int bits, const DevPar
     return make_float3(c[0], c[1], c[2]);
 }
 
+// First sorted position past the level-l cell that holds position a: the
+// first j > a whose key has another level-l prefix (or n).  Keys sharing the
+// prefix are one contiguous run, so the positions inside form a prefix of
+// any increasing set of probes; each round issues eight independent probes:
+// a + step * {1..8} with step growing eightfold while all are inside, then
+// seven evenly spaced probes in the remaining bracket.
+__device__ inline uint32_t cell_end(const uint64_t *__restrict__ keys, uint32_t n, uint32_t a,
+                                    int shift)
+{
+    const uint64_t p = keys[a] >> shift;
+    uint64_t lo = a, hi = n;   // keys[lo] inside; hi outside (or n)
+    for (uint64_t step = 1;; step *= 8) {
+        uint64_t j[8];
+        bool in[8];
+        uint64_t v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            j[k] = (uint64_t)a + (uint64_t)(k + 1) * step;
+            v[k] = keys[min(j[k], (uint64_t)n - 1)];   // unconditional: all eight in flight
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) in[k] = j[k] < n && (v[k] >> shift) == p;
+        int m = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) m += in[k] ? 1 : 0;
+        if (m == 8) {
+            lo = j[7];
+            continue;
+        }
+        if (m > 0) lo = j[m - 1];
+        hi = min((uint64_t)n, j[m]);
+        break;
+    }
+    while (hi - lo > 1) {
+        uint64_t j[7];
+        bool in[7];
+        const uint64_t w = hi - lo;
+        uint64_t v[7];
+#pragma unroll
+        for (int k = 0; k < 7; ++k) {
+            j[k] = lo + 1 + ((w - 1) * (uint64_t)(k + 1)) / 8;   // in (lo, hi)
+            v[k] = keys[j[k]];
+        }
+#pragma unroll
+        for (int k = 0; k < 7; ++k) in[k] = (v[k] >> shift) == p;
+        int m = 0;
+#pragma unroll
+        for (int k = 0; k < 7; ++k) m += in[k] ? 1 : 0;
+        const uint64_t nlo = m > 0 ? j[m - 1] : lo;
+        const uint64_t nhi = m < 7 ? j[m] : hi;
+        lo = nlo;
+        hi = nhi;
+    }
+    return (uint32_t)hi;
+}
+
+// Per node: its particle range, skip, mass and centre of mass, written as one
+// 32-byte record.  A leaf ends where the next node in pre-order starts (its
+// skip is the next node); an internal cell's end is searched in the keys.
 __global__ __launch_bounds__(256) void k_ranges(const uint64_t *__restrict__ keys,
                                                 const float4 *__restrict__ spos,
                                                 const D4 *__restrict__ P, uint32_t n,
@@ -361,27 +515,15 @@ __global__ __launch_bounds__(256) void k_ranges(const uint64_t *__restrict__ key
 {
     const uint32_t nn = (uint32_t)min((uint64_t)prm->n_nodes, cap);
     for (uint32_t X = blockIdx.x * blockDim.x + threadIdx.x; X < nn; X += gridDim.x * blockDim.x) {
-        const uint32_t a = nodes[X].start;
-        const uint32_t meta = nodes[X].meta;
+        const uint4 rec = reinterpret_cast<const uint4 *>(&nodes[X])[1];
+        const uint32_t a = rec.x, meta = rec.w;
         const int l = (int)node_level(meta);
-        const int shift = 3 * (bits - l);
-        const uint64_t p = keys[a] >> shift;
-        // galloping search for the first sorted position past the cell
-        uint32_t lo = a, hi = n;
-        for (uint32_t step = 1;; step <<= 1) {
-            const uint64_t j = (uint64_t)a + step;
-            if (j >= n) break;
-            if ((keys[j] >> shift) != p) { hi = (uint32_t)j; break; }
-            lo = (uint32_t)j;
-        }
-        while (hi - lo > 1) {
-            const uint32_t mid = lo + (hi - lo) / 2;
-            if ((keys[mid] >> shift) == p) lo = mid; else hi = mid;
-        }
-        const uint32_t e = hi;
-        nodes[X].count = e - a;
-        nodes[X].skip = first_node[e];
-        const D4 sum = P[e] - P[a];
+        const bool leaf = (meta & kLeafBit) != 0;
+        const D4 pa = P[a];
+        const uint32_t e = leaf ? (X + 1 < nn ? nodes[X + 1].start : n)
+                                : cell_end(keys, n, a, 3 * (bits - l));
+        const uint32_t skip = leaf ? X + 1 : first_node[e];
+        const D4 sum = P[e] - pa;
         float4 com;
         if (sum.m != 0.0) {
             com = make_float4((float)(prm->lo[0] + sum.x / sum.m),
@@ -391,7 +533,8 @@ __global__ __launch_bounds__(256) void k_ranges(const uint64_t *__restrict__ key
             const float3 c = cell_centre(spos[a], l, bits, prm);
             com = make_float4(c.x, c.y, c.z, 0.f);
         }
-        *reinterpret_cast<float4 *>(&nodes[X]) = com;
+        reinterpret_cast<float4 *>(&nodes[X])[0] = com;
+        reinterpret_cast<uint4 *>(&nodes[X])[1] = make_uint4(a, e - a, skip, meta);
     }
 }
 
@@ -423,8 +566,14 @@ void build_tree(const uint64_t *keys_sorted, const float4 *spos, uint32_t n, int
                 DevParams *prm, hipStream_t s)
 {
     const uint32_t tiles = build_blocks(n);
-    hipLaunchKernelGGL(k_count, dim3(tiles), dim3(kBuildThreads), 0, s, keys_sorted, spos, n, bits,
-                       leaf_cap, w.dc, w.tile_counts, w.tile_sums, (const DevParams *)prm);
+    if (leaf_cap <= 64)
+        hipLaunchKernelGGL(k_count<true>, dim3(tiles), dim3(kBuildThreads), 0, s, keys_sorted,
+                           spos, n, bits, leaf_cap, w.dc, w.tile_counts, w.tile_sums,
+                           (const DevParams *)prm);
+    else
+        hipLaunchKernelGGL(k_count<false>, dim3(tiles), dim3(kBuildThreads), 0, s, keys_sorted,
+                           spos, n, bits, leaf_cap, w.dc, w.tile_counts, w.tile_sums,
+                           (const DevParams *)prm);
     const uint32_t chunk = chunk_tiles(tiles);
     const uint32_t n_chunks = (tiles + chunk - 1) / chunk;
     hipLaunchKernelGGL(k_chunk_totals, dim3(n_chunks), dim3(64), 0, s,

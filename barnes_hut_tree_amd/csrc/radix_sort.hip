@@ -170,18 +170,46 @@ __global__ __launch_bounds__(kSortThreads) void k_scatter(
 
     const uint32_t tile_base = tile * kTile;
     const uint32_t tile_n = min(kTile, n - tile_base);
+    if (!GATHER) {
 #pragma unroll 4
-    for (int k = 0; k < ITEMS; ++k) {
-        const uint32_t j = k * kSortThreads + threadIdx.x;
-        if (j < tile_n) {
-            const uint64_t kk = skey[j];
-            const uint32_t vv = sval[j];
-            const uint32_t digit = (uint32_t)(kk >> shift) & 0xffu;
-            const uint32_t g = wcnt[0][digit] + j;
-            kout[g] = kk;
-            vout[g] = vv;
-            if (GATHER) gdst[g] = gsrc[vv];
+        for (int k = 0; k < ITEMS; ++k) {
+            const uint32_t j = k * kSortThreads + threadIdx.x;
+            if (j < tile_n) {
+                const uint64_t kk = skey[j];
+                const uint32_t vv = sval[j];
+                const uint32_t digit = (uint32_t)(kk >> shift) & 0xffu;
+                const uint32_t g = wcnt[0][digit] + j;
+                kout[g] = kk;
+                vout[g] = vv;
+            }
         }
+    } else {
+        // the last pass also gathers the source rows: all of a thread's
+        // random reads are issued before any of their stores
+        uint32_t gi[ITEMS], vi[ITEMS];
+#pragma unroll
+        for (int k = 0; k < ITEMS; ++k) {
+            const uint32_t j = k * kSortThreads + threadIdx.x;
+            gi[k] = 0xffffffffu;
+            vi[k] = 0;
+            if (j < tile_n) {
+                const uint64_t kk = skey[j];
+                const uint32_t vv = sval[j];
+                const uint32_t digit = (uint32_t)(kk >> shift) & 0xffu;
+                const uint32_t g = wcnt[0][digit] + j;
+                kout[g] = kk;
+                vout[g] = vv;
+                gi[k] = g;
+                vi[k] = vv;
+            }
+        }
+        float4 row[ITEMS];
+#pragma unroll
+        for (int k = 0; k < ITEMS; ++k)
+            row[k] = gi[k] != 0xffffffffu ? gsrc[vi[k]] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int k = 0; k < ITEMS; ++k)
+            if (gi[k] != 0xffffffffu) gdst[gi[k]] = row[k];
     }
 }
 
