@@ -332,6 +332,7 @@ __global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restri
                                                         DevParams *__restrict__ prm)
 {
     constexpr int per = kBuildTile / kBuildThreads;  // consecutive positions per thread
+    static_assert(per == 4, "the LDS layout below assumes 4 positions per thread");
     __shared__ uint32_t wtot[kBuildThreads / 64];
     __shared__ D4 wsum[kBuildThreads / 64];
     __shared__ uint32_t tile_nodes;
@@ -350,16 +351,22 @@ __global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restri
         }
     }
 
-    // coalesced loads into LDS: per position its (d, c) word and its mass moment
-    __shared__ D4 mom[kBuildTile];          // moments, then the prefix P
-    __shared__ uint32_t fn[kBuildTile];     // first node at each position
+    // Coalesced loads into LDS: per position its (d, c) word and its mass
+    // moment.  Each thread then works on 4 consecutive positions; their four
+    // moments are stored at a stride of 9 16-byte units per thread (one unit
+    // of padding), so the threads' 16-byte LDS accesses fall in distinct banks.
+    __shared__ double2 mom[kBuildThreads * 9];   // moments, then the prefix P
+    __shared__ uint32_t fn[kBuildTile];           // first node at each position
     __shared__ uint16_t sdc[kBuildTile];
+    auto unit = [](int j) { return (j >> 2) * 9 + (j & 3) * 2; };
     const int64_t t0 = (int64_t)blk * kBuildTile;
     for (int k = 0; k < per; ++k) {
         const int j = k * kBuildThreads + threadIdx.x;
         const int64_t a = t0 + j;
         sdc[j] = a < (int64_t)n ? dc[a] : (uint16_t)0;
-        mom[j] = a < (int64_t)n ? mass_moment(spos[a], prm) : D4{0.0, 0.0, 0.0, 0.0};
+        const D4 m = a < (int64_t)n ? mass_moment(spos[a], prm) : D4{0.0, 0.0, 0.0, 0.0};
+        mom[unit(j)] = make_double2(m.m, m.x);
+        mom[unit(j) + 1] = make_double2(m.y, m.z);
     }
     __syncthreads();
 
@@ -367,14 +374,20 @@ __global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restri
     const int j0 = per * threadIdx.x;
     const int64_t a0 = t0 + j0;
     int dd[per], cc[per];
+    D4 mk[per];
     uint32_t s = 0;
     D4 ms = {0.0, 0.0, 0.0, 0.0};
-    for (int k = 0; k < per; ++k) {
-        const uint16_t v = sdc[j0 + k];
-        dd[k] = (int)(v & 0xffu) - 1;
-        cc[k] = v >> 8;
-        s += cc[k];
-        ms = ms + mom[j0 + k];
+    {
+        const uint2 w = reinterpret_cast<const uint2 *>(sdc)[threadIdx.x];
+        const uint32_t v4[per] = {w.x & 0xffffu, w.x >> 16, w.y & 0xffffu, w.y >> 16};
+        for (int k = 0; k < per; ++k) {
+            dd[k] = (int)(v4[k] & 0xffu) - 1;
+            cc[k] = (int)(v4[k] >> 8);
+            s += cc[k];
+            const double2 u0 = mom[unit(j0 + k)], u1 = mom[unit(j0 + k) + 1];
+            mk[k] = D4{u0.x, u0.y, u1.x, u1.y};
+            ms = ms + mk[k];
+        }
     }
     const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t incl = wave_incl_scan(s);
@@ -393,23 +406,26 @@ __global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restri
     run += incl - s;
     mrun = mrun + (mincl - ms);
 
+    uint32_t fn4[per];
     for (int k = 0; k < per; ++k) {
         const int64_t a = a0 + k;
-        if (a >= (int64_t)n) break;
-        const D4 mk = mom[j0 + k];
-        fn[j0 + k] = run;
-        mom[j0 + k] = mrun;
-        mrun = mrun + mk;
-        for (int j = 0; j < cc[k]; ++j) {
-            const int l = dd[k] + 1 + j;
-            const uint32_t X = run + j;
-            if (X < cap) {
-                nodes[X].start = (uint32_t)a;
-                nodes[X].meta = (uint32_t)l | (j == cc[k] - 1 ? kLeafBit : 0u);
+        fn4[k] = run;
+        mom[unit(j0 + k)] = make_double2(mrun.m, mrun.x);
+        mom[unit(j0 + k) + 1] = make_double2(mrun.y, mrun.z);
+        mrun = mrun + mk[k];
+        if (a < (int64_t)n) {
+            for (int j = 0; j < cc[k]; ++j) {
+                const int l = dd[k] + 1 + j;
+                const uint32_t X = run + j;
+                if (X < cap) {
+                    nodes[X].start = (uint32_t)a;
+                    nodes[X].meta = (uint32_t)l | (j == cc[k] - 1 ? kLeafBit : 0u);
+                }
             }
         }
         run += cc[k];
     }
+    reinterpret_cast<uint4 *>(fn)[threadIdx.x] = make_uint4(fn4[0], fn4[1], fn4[2], fn4[3]);
     __syncthreads();
     // coalesced stores; nodes start and end only where a leaf starts, so the
     // prefix and the first-node index are needed only there
@@ -418,7 +434,8 @@ __global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restri
         const int64_t a = t0 + j;
         if (a < (int64_t)n && (sdc[j] >> 8) != 0) {
             first_node[a] = fn[j];
-            P[a] = mom[j];
+            const double2 u0 = mom[unit(j)], u1 = mom[unit(j) + 1];
+            P[a] = D4{u0.x, u0.y, u1.x, u1.y};
         }
     }
     if (blk == n_tiles - 1 && threadIdx.x == 0) {
@@ -585,7 +602,9 @@ void build_tree(const uint64_t *keys_sorted, const float4 *spos, uint32_t n, int
                        n, (const uint32_t *)w.tile_counts, (const D4 *)w.tile_sums,
                        (const TileScan *)w.tile_scan, tiles, chunk, node_capacity, w.first_node,
                        w.P, nodes, prm);
-    hipLaunchKernelGGL(k_ranges, dim3(grid_for(n, 2048)), dim3(256), 0, s, keys_sorted, spos,
+    // about one node per thread: n / 2 threads (a tree of leaf capacity 16
+    // has about n / 3 nodes; the grid-stride loop covers any excess)
+    hipLaunchKernelGGL(k_ranges, dim3(grid_for(n / 2 + 1, 65535)), dim3(256), 0, s, keys_sorted, spos,
                        (const D4 *)w.P, n, bits, node_capacity, (const uint32_t *)w.first_node,
                        nodes, (const DevParams *)prm);
 }
