@@ -375,6 +375,41 @@ def sbh_compare(args):
                     "max_abs_err": [float(mx.mean()), float(mx.std())]}), flush=True)
 
 
+def build_only(args):
+    """bh_build alone (bounding box, keys, sort with the sorted-source gather,
+    tree, centres of mass), timed with HIP events on the launch stream; the
+    per-kernel split comes from rocprofv3 on this mode."""
+    import torch
+
+    import barnes_hut_tree_amd as bh
+    p, _, wname = make_workload(args.workload)
+    n = p.shape[0]
+    src = torch.from_numpy(p).cuda()
+    tree = bh.BarnesHut(n, 0, args.key_bits, args.leaf_cap, curve=args.curve)
+    for _ in range(args.warmup):
+        tree.build(src)
+    tree.sync()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        tree.build(src)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    tree.sync()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    nodes = tree.nodes()
+    n_nodes = int(nodes.shape[0])
+    n_leaves = int(((nodes[:, 7] & (1 << 8)) != 0).sum().item())
+    tree.close()
+    print(json.dumps({"mode": "build_only", "workload": wname, "n": n,
+                      "n_nodes": n_nodes, "n_leaves": n_leaves,
+                      "leaf_cap": args.leaf_cap, "key_bits": args.key_bits,
+                      "key_curve": args.curve, "steps": args.steps,
+                      "build_ms_median": ms[len(ms) // 2], "build_ms_min": ms[0]}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -396,6 +431,9 @@ def main():
                     help="time-step the 5M galaxy pair (kick-drift-kick, rebuild every step)")
     ap.add_argument("--sbh", action="store_true",
                     help="stochastic Barnes-Hut vs the tree walk at separate query points")
+    ap.add_argument("--build-only", action="store_true",
+                    help="time bh_build alone on the workload (keys, sort, tree, centres of "
+                         "mass) and print its JSON line")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB (3 times), "
                          "the reference kernel for scaling HBM byte counters")
@@ -421,6 +459,10 @@ def main():
         return
     if args.sbh:
         sbh_compare(args)
+        return
+
+    if args.build_only:
+        build_only(args)
         return
 
     if args.copy_calibration_mib:
