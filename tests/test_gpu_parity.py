@@ -99,7 +99,12 @@ def _expected_skip(level):
 
 TREE_CASES = [("uniform4096", 63, 16), ("uniform4096", 63, 1), ("plummer65536", 63, 16),
               ("plummer65536", 30, 8), ("duplicates", 63, 4), ("lattice_shuffled", 63, 16),
-              ("ragged65", 63, 3), ("single", 63, 16), ("plummer65536", 63, 256)]
+              ("ragged65", 63, 3), ("single", 63, 16), ("plummer65536", 63, 256),
+              # leaf capacities either side of 64, where the leaf-start search changes
+              # from one wave row either side to a scan of the window
+              ("plummer65536", 63, 33), ("ragged4097", 63, 63), ("plummer65536", 63, 64),
+              ("ragged4097", 63, 64), ("plummer65536", 63, 65), ("duplicates", 30, 64),
+              ("ragged65", 63, 64)]
 
 
 @pytest.mark.parametrize("case,bits,B", TREE_CASES)
@@ -365,7 +370,7 @@ def test_invalid_arguments():
 # ---------------------------------------------------------------------------
 # other build parameters: 30-bit keys, very small and very large leaves
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("key_bits,B", [(30, 16), (63, 2), (63, 256), (30, 256)])
+@pytest.mark.parametrize("key_bits,B", [(30, 16), (63, 2), (63, 64), (63, 65), (63, 256), (30, 256)])
 def test_gravity_other_build_parameters(orc, key_bits, B):
     p = W.plummer(1 << 16, seed=12)
     log("gravity plummer 2^16 key_bits", key_bits, "B", B)
