@@ -355,9 +355,10 @@ __global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restri
     // moment.  Each thread then works on 4 consecutive positions; their four
     // moments are stored at a stride of 9 16-byte units per thread (one unit
     // of padding), so the threads' 16-byte LDS accesses fall in distinct banks.
-    __shared__ double2 mom[kBuildThreads * 9];   // moments, then the prefix P
-    __shared__ uint32_t fn[kBuildTile];           // first node at each position
-    __shared__ uint16_t sdc[kBuildTile];
+    // (fn and sdc are also accessed as 16- and 8-byte words)
+    __shared__ double2 mom[kBuildThreads * 9];                // moments, then the prefix P
+    __shared__ __attribute__((aligned(16))) uint32_t fn[kBuildTile];   // first node per position
+    __shared__ __attribute__((aligned(16))) uint16_t sdc[kBuildTile];
     auto unit = [](int j) { return (j >> 2) * 9 + (j & 3) * 2; };
     const int64_t t0 = (int64_t)blk * kBuildTile;
     for (int k = 0; k < per; ++k) {
