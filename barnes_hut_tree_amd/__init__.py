@@ -31,7 +31,7 @@ EXPORTS = ("bh_create", "bh_build", "bh_gravity", "bh_gravity_counted", "bh_grav
            "bh_get_locked_tree", "bh_direct", "bh_kick_drift",
            "bh_leapfrog_step", "bh_diagnostics", "bh_sync", "bh_destroy",
            "bh_status_string", "bh_get_keys", "bh_get_node_count", "bh_get_nodes", "bh_get_bbox",
-           "bh_set_profiling", "bh_get_profile")
+           "bh_set_profiling", "bh_get_profile", "bh_node_hmax")
 
 NODE_DTYPE_FIELDS = [("com_x", "f4"), ("com_y", "f4"), ("com_z", "f4"), ("mass", "f4"),
                      ("start", "u4"), ("count", "u4"), ("skip", "u4"), ("meta", "u4")]
@@ -86,6 +86,7 @@ def load_library():
         "bh_get_bbox": [P, P, P, P, P],
         "bh_set_profiling": [P, i32],
         "bh_get_profile": [P, P, i32],
+        "bh_node_hmax": [P, P, i64, P, i64, P],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -267,6 +268,22 @@ class BarnesHut:
         _check(load_library().bh_get_nodes(self._h, ctypes.c_void_p(buf.data_ptr()), nn,
                                            _stream()), "bh_get_nodes")
         return buf[:nn]
+
+    def node_hmax(self, h):
+        """Largest h among each node's sources (bh_node_hmax): h is a float32
+        CUDA tensor of the built sources' smoothing lengths in their order;
+        returns a float32 CUDA tensor with one value per node (node order)."""
+        import torch
+        if not isinstance(h, torch.Tensor) or h.device.type != "cuda" or h.dtype != torch.float32:
+            raise TypeError("h must be a float32 CUDA tensor")
+        if h.dim() != 1 or not h.is_contiguous():
+            raise ValueError("h must be a contiguous 1-D tensor")
+        nn = self.node_count() if h.shape[0] > 0 else 0
+        out = torch.empty(max(nn, 1), dtype=torch.float32, device="cuda")
+        _check(load_library().bh_node_hmax(self._h, ctypes.c_void_p(h.data_ptr()), h.shape[0],
+                                           ctypes.c_void_p(out.data_ptr()), nn, _stream()),
+               "bh_node_hmax")
+        return out[:nn]
 
     def bbox(self):
         lo = (ctypes.c_double * 3)()

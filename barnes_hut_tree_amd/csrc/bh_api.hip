@@ -532,6 +532,24 @@ bh_status bh_get_node_count(bh_ctx *c, int64_t *n_nodes, void *stream)
     return BH_OK;
 }
 
+bh_status bh_node_hmax(bh_ctx *c, const float *h, int64_t n, float *node_hmax,
+                       int64_t n_nodes_max, void *stream)
+{
+    if (!c || n < 0 || n_nodes_max < 0) return BH_ERR_INVALID;
+    if (!c->built) return BH_ERR_NOT_BUILT;
+    if ((uint64_t)n != c->n_src || (n > 0 && (!h || !node_hmax))) return BH_ERR_INVALID;
+    if (n == 0) return BH_OK;
+    hipStream_t s = (hipStream_t)stream;
+    c->last_stream = s;
+    bh_status st = read_params(c, s);   // the node count (and the build's status)
+    if (st != BH_OK) return st;
+    if (c->host_prm->status != 0) return BH_ERR_NOT_BUILT;
+    const uint32_t nn = c->host_prm->n_nodes;
+    if ((uint64_t)nn > (uint64_t)n_nodes_max) return BH_ERR_INVALID;
+    launch_node_hmax(c->nodes, c->perm, h, nn, c->prm, c->node_cap, c->bits, node_hmax, s);
+    return launch_status();
+}
+
 bh_status bh_get_nodes(bh_ctx *c, bh_node *nodes, int64_t n_nodes, void *stream)
 {
     if (!c || n_nodes < 0 || (uint64_t)n_nodes > c->node_cap || (n_nodes && !nodes))

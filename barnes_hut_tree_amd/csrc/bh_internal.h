@@ -131,6 +131,10 @@ void build_tree(const uint64_t *keys_sorted, const float4 *spos, uint32_t n, int
                 int leaf_cap, uint64_t node_capacity, BuildScratch &w, Node *nodes,
                 DevParams *prm, hipStream_t s);
 
+// hmax.hip: per-node maximum of h (caller order) over the node's sources
+void launch_node_hmax(const Node *nodes, const uint32_t *perm, const float *h, uint32_t n_nodes,
+                      const DevParams *prm, uint64_t cap, int bits, float *out, hipStream_t s);
+
 // traverse.hip
 struct WalkArgs {
     const Node *nodes;

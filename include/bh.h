@@ -198,6 +198,23 @@ bh_status bh_get_locked_tree(bh_ctx *ctx, int64_t *n_cells, int64_t *cap, int32_
 bh_status bh_sbh(bh_ctx *ctx, const float *targets, int64_t n_targets, int d, int samples,
                  uint64_t seed, float G, float eps, float *out_acc_pot, void *stream);
 
+/* Per-node maximum smoothing length: node_hmax[X] = the largest h among the
+ * sources of node X of the last bh_build, the hmax the pages' tree keeps beside
+ * the centre of mass for its SPH neighbour search ([Tree] 树结构 粒子领域搜索;
+ * the d_node_hmax array of 重置树结构).  Leaves take the maximum over their
+ * sources, internal nodes over their children.
+ *   h            device, n floats in the caller's order of the built sources
+ *                (n must equal the n of bh_build); finite values.
+ *   node_hmax    device, at least as many floats as the tree has nodes, in
+ *                node order (the order of bh_get_nodes).
+ *   n_nodes_max  capacity of node_hmax in floats.
+ * Waits for `stream` to finish the build (it reads the node count), then
+ * runs asynchronously on `stream`.  Errors: BH_ERR_NOT_BUILT (no build, or
+ * the build failed on the device), BH_ERR_INVALID (bad arguments, n other
+ * than the built n, n_nodes_max below the node count). */
+bh_status bh_node_hmax(bh_ctx *ctx, const float *h, int64_t n, float *node_hmax,
+                       int64_t n_nodes_max, void *stream);
+
 /* All-pairs direct sum, no tree and no context: every target against every
  * source with the interaction of bh_gravity.  This is the brute-force
  * reference that [GASPHiA] 精度与加速比验证 measures the walk's speed-up and

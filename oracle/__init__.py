@@ -260,3 +260,17 @@ def diagnostics(x, m, v, phi):
     return dict(mass=m.sum(), kinetic=0.5 * np.sum(m * np.sum(v * v, axis=1)),
                 potential=0.5 * np.sum(m * phi), momentum=(m[:, None] * v).sum(axis=0),
                 angular_momentum=(m[:, None] * np.cross(x, v)).sum(axis=0))
+
+
+def node_hmax(tree, h):
+    """Per cell of `tree` (pre-order, the order of Tree.cells), the largest h
+    among its particles: the hmax the tree of [Tree] (树结构, 粒子领域搜索)
+    keeps for its SPH neighbour search, by its definition.  h is given in the
+    input order of the particles."""
+    h = np.asarray(h, np.float32)
+    c = tree.cells()
+    perm = tree.perm()
+    out = np.empty(len(c["level"]), np.float32)
+    for k, (s, n) in enumerate(zip(c["start"], c["count"])):
+        out[k] = h[perm[s:s + n]].max()
+    return out

@@ -241,6 +241,42 @@ def test_massless_cell_takes_its_centre(orc):
     assert np.allclose(c["com"][lev1[0]], [0.25, 0.25, 0.25])
 
 
+def test_node_hmax_from_key_membership(orc):
+    """Per-cell hmax against cell membership taken from the keys alone (a
+    particle belongs to a level-l cell when its key's top 3l bits are the
+    cell's prefix), so a wrong range, permutation or order fails."""
+    rng = np.random.default_rng(17)
+    base = W.plummer(300, seed=17)
+    p = np.concatenate([base, base[:40]])               # coincident pairs too
+    h = rng.uniform(0.01, 1.0, p.shape[0]).astype(np.float32)
+    for bits, B in ((63, 1), (63, 3), (30, 2)):
+        t = orc.Tree(p, key_bits=bits, leaf_cap=B)
+        c, keys = t.cells(), t.keys()
+        got = orc.node_hmax(t, h)
+        b3 = bits // 3
+        for i in range(len(c["level"])):
+            shift = np.uint64(3 * (b3 - int(c["level"][i])))
+            mem = (keys >> shift) == c["prefix"][i]
+            assert mem.sum() == c["count"][i]
+            assert got[i] == h[mem].max()
+
+
+def test_node_hmax_invariants(orc):
+    rng = np.random.default_rng(18)
+    p = W.plummer(20000, seed=18)
+    h = rng.exponential(0.1, p.shape[0]).astype(np.float32)
+    t = orc.Tree(p, leaf_cap=16)
+    c = t.cells()
+    got = orc.node_hmax(t, h)
+    assert got[0] == h.max()                              # the root holds everything
+    lev = c["level"]
+    for i in range(1, len(lev)):                         # a cell's parent precedes it
+        j = i - 1
+        while lev[j] >= lev[i]:
+            j -= 1
+        assert lev[j] == lev[i] - 1 and got[j] >= got[i]
+
+
 # --------------------------------------------------------------------------
 # forces: direct sum and the walk
 # --------------------------------------------------------------------------
