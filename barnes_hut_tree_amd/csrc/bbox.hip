@@ -15,6 +15,10 @@
 #include "bh_internal.h"
 
 namespace bh {
+constexpr int kHilbertMaxStates = 64;
+}
+
+namespace bh {
 namespace {
 
 constexpr int kBboxThreads = 256;
@@ -122,57 +126,95 @@ __device__ inline uint64_t spread3(uint64_t v)
 
 
 // Hilbert index of BITS-bit integer coordinates, after Skilling,
-// "Programming the Hilbert curve" (AIP Conf. Proc. 707, 2004): the transposed
-// index is formed in place (undo excess work from the top bit down, then Gray
-// encoding) and its bits are interleaved x, y, z from the most significant
-// end, so each 3-bit digit names a child cell in the curve's order.  Every
-// cell is still one contiguous key range: the tree is the same, only the
-// order of siblings changes.
+// "Programming the Hilbert curve" (AIP Conf. Proc. 707, 2004): from the top
+// bit down, each level's bits of (x, y, z) decide operations on all lower
+// bits (invert the low bits of x, or exchange them with those of y or z);
+// Gray encoding and a parity correction then give the transposed index,
+// whose bits interleaved x, y, z from the most significant end are the key,
+// so each 3-bit digit names a child cell in the curve's order.  Every cell is
+// still one contiguous key range: the tree is the same, only the order of
+// siblings changes.
 //
-// The level loop is unrolled for the two key widths, each level's choices
-// are selects rather than branches, and the final correction (bit i of t is
-// the parity of the bits of z above i) is a suffix-parity of z >> 1 in five
-// shift-xor steps.
-template <int BITS>
-__device__ inline uint64_t hilbert3(uint32_t x, uint32_t y, uint32_t z)
+// The lower-bit operations compose into one signed permutation of the three
+// axes, the same at every lower level, and the parity correction of a level
+// is the parity of the Gray-coded z bits above it.  So the transform is a
+// finite automaton over the levels: state = (accumulated permutation, parity),
+// input = the level's raw bits, output = the level's key digit.  The host
+// derives its table once from the operations above (48 states reachable); the
+// kernel runs one table lookup (in LDS) per level instead of the level's
+// selects and exchanges.
+struct HilbertTable {
+    uint16_t e[kHilbertMaxStates * 8];   // digit | next state << 3
+};
+
+HilbertTable build_hilbert_table()
 {
-#pragma unroll
-    for (int q = BITS - 1; q >= 1; --q) {
-        const uint32_t P = (1u << q) - 1u;
-        x ^= ((x >> q) & 1u) ? P : 0u;
-        {
-            const uint32_t t = (x ^ y) & P;
-            const bool set = (y >> q) & 1u;
-            x ^= set ? P : t;
-            y ^= set ? 0u : t;
-        }
-        {
-            const uint32_t t = (x ^ z) & P;
-            const bool set = (z >> q) & 1u;
-            x ^= set ? P : t;
-            z ^= set ? 0u : t;
+    // a state: map of the 3-bit vectors (x << 2 | y << 1 | z) of a lower level
+    // under the operations so far, and the parity of the Gray-coded z bits
+    struct State {
+        uint8_t T[8];
+        int p;
+    };
+    auto same = [](const State &a, const State &b) {
+        for (int v = 0; v < 8; ++v)
+            if (a.T[v] != b.T[v]) return false;
+        return a.p == b.p;
+    };
+    State st[kHilbertMaxStates];
+    int ns = 1;
+    for (int v = 0; v < 8; ++v) st[0].T[v] = (uint8_t)v;
+    st[0].p = 0;
+    HilbertTable tab{};
+    for (int i = 0; i < ns; ++i) {
+        for (int r = 0; r < 8; ++r) {
+            const int tv = st[i].T[r];   // this level's bits after the operations above
+            const int tx = (tv >> 2) & 1, ty = (tv >> 1) & 1, tz = tv & 1;
+            // Gray encoding (y ^= x, z ^= y), then the parity correction
+            const int gx = tx, gy = ty ^ gx, gz = tz ^ gy;
+            const int g = (gx << 2) | (gy << 1) | gz;
+            const int digit = st[i].p ? (g ^ 7) : g;
+            // this level's operations on the lower bits
+            uint8_t U[8];
+            for (int v = 0; v < 8; ++v) {
+                int x = (v >> 2) & 1, y = (v >> 1) & 1, z = v & 1;
+                if (tx) x ^= 1;
+                if (ty) x ^= 1; else { const int t = x; x = y; y = t; }
+                if (tz) x ^= 1; else { const int t = x; x = z; z = t; }
+                U[v] = (uint8_t)((x << 2) | (y << 1) | z);
+            }
+            State nx;
+            for (int v = 0; v < 8; ++v) nx.T[v] = U[st[i].T[v]];
+            nx.p = st[i].p ^ gz;
+            int id = 0;
+            while (id < ns && !same(st[id], nx)) ++id;
+            if (id == ns) {
+                if (ns == kHilbertMaxStates) return HilbertTable{};   // cannot happen (48 states)
+                st[ns++] = nx;
+            }
+            tab.e[i * 8 + r] = (uint16_t)(digit | (id << 3));
         }
     }
-    y ^= x;
-    z ^= y;
-    uint32_t t = z >> 1;
-    t ^= t >> 1;
-    t ^= t >> 2;
-    t ^= t >> 4;
-    t ^= t >> 8;
-    t ^= t >> 16;
-    x ^= t;
-    y ^= t;
-    z ^= t;
-    return spread3(z) | (spread3(y) << 1) | (spread3(x) << 2);
+    return tab;
+}
+
+const HilbertTable &hilbert_table()
+{
+    static const HilbertTable t = build_hilbert_table();
+    return t;
 }
 
 template <bool HILBERT, int BITS>
 __global__ __launch_bounds__(256) void k_morton(const float4 *__restrict__ pts, uint32_t n,
                                                 const DevParams *__restrict__ prm,
+                                                const HilbertTable tab,
                                                 uint64_t *__restrict__ keys,
                                                 uint32_t *__restrict__ idx)
 {
+    __shared__ uint16_t lut[HILBERT ? kHilbertMaxStates * 8 : 1];
+    if (HILBERT) {
+        for (int k = threadIdx.x; k < kHilbertMaxStates * 8; k += 256) lut[k] = tab.e[k];
+        __syncthreads();
+    }
     const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     const float4 p = pts[i];
@@ -181,8 +223,22 @@ __global__ __launch_bounds__(256) void k_morton(const float4 *__restrict__ pts, 
     const uint64_t qx = quantise(p.x, prm->lo[0], s, top);
     const uint64_t qy = quantise(p.y, prm->lo[1], s, top);
     const uint64_t qz = quantise(p.z, prm->lo[2], s, top);
-    keys[i] = HILBERT ? hilbert3<BITS>((uint32_t)qx, (uint32_t)qy, (uint32_t)qz)
-                      : spread3(qx) | (spread3(qy) << 1) | (spread3(qz) << 2);
+    uint64_t key;
+    if (HILBERT) {
+        const uint32_t x = (uint32_t)qx, y = (uint32_t)qy, z = (uint32_t)qz;
+        uint32_t state = 0;
+        key = 0;
+#pragma unroll
+        for (int q = BITS - 1; q >= 0; --q) {
+            const uint32_t r = (((x >> q) & 1u) << 2) | (((y >> q) & 1u) << 1) | ((z >> q) & 1u);
+            const uint32_t e = lut[state * 8 + r];
+            key = (key << 3) | (e & 7u);
+            state = e >> 3;
+        }
+    } else {
+        key = spread3(qx) | (spread3(qy) << 1) | (spread3(qz) << 2);
+    }
+    keys[i] = key;
     idx[i] = i;
 }
 
@@ -191,10 +247,11 @@ void launch_keys(const float4 *pts, uint32_t n, const DevParams *prm, int bits, 
                  uint32_t *idx, hipStream_t s)
 {
     const dim3 grid((n + 255) / 256), block(256);
+    const HilbertTable &tab = hilbert_table();
     if (bits == 21)
-        hipLaunchKernelGGL((k_morton<HILBERT, 21>), grid, block, 0, s, pts, n, prm, keys, idx);
+        hipLaunchKernelGGL((k_morton<HILBERT, 21>), grid, block, 0, s, pts, n, prm, tab, keys, idx);
     else
-        hipLaunchKernelGGL((k_morton<HILBERT, 10>), grid, block, 0, s, pts, n, prm, keys, idx);
+        hipLaunchKernelGGL((k_morton<HILBERT, 10>), grid, block, 0, s, pts, n, prm, tab, keys, idx);
 }
 
 }  // namespace

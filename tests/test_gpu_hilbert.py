@@ -36,12 +36,13 @@ def _massless():
     return p
 
 
-CASES = dict(KEY_CASES, massless=_massless)
+CASES = dict(KEY_CASES, massless=_massless,
+             uniform_2p20=lambda: W.uniform_box(1 << 20, seed=5))
 
 
 @pytest.mark.parametrize("bits", [63, 30])
 @pytest.mark.parametrize("case", ["uniform4096", "plummer65536", "duplicates", "ragged65",
-                                  "single"])
+                                  "single", "uniform_2p20", "large_ragged"])
 def test_hilbert_keys_perm_bitexact(orc, case, bits):
     p = CASES[case]()
     log("hilbert keys", case, bits)
