@@ -240,7 +240,9 @@ static bh_status gravity_impl(bh_ctx *c, const float *targets, int64_t n_targets
 {
     if (!c) return BH_ERR_INVALID;
     if (!c->built) return BH_ERR_NOT_BUILT;
-    if (n_targets < 0 || !(theta >= 0.f) || !(eps >= 0.f) || !__builtin_isfinite(G)) return BH_ERR_INVALID;
+    if (n_targets < 0 || n_targets > kMaxCount || !(theta >= 0.f) || !(eps >= 0.f) ||
+        !__builtin_isfinite(G))
+        return BH_ERR_INVALID;
     if (flags & ~(uint32_t)(BH_WALK_VOTE | BH_WALK_UNSORTED)) return BH_ERR_INVALID;
     if (n_targets > 0 && (!out || !aligned16(out))) return BH_ERR_INVALID;
     if (targets) {

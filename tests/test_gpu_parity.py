@@ -364,6 +364,16 @@ def test_invalid_arguments():
     big = torch.from_numpy(W.uniform_cube(101)).cuda()
     with pytest.raises(bh.BHError):
         t.build(big)
+    # a target count that only matches the source count modulo 2^32, and NaN theta
+    import ctypes
+    L = bh.load_library()
+    out = torch.empty((100, 4), dtype=torch.float32, device="cuda")
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    o = ctypes.c_void_p(out.data_ptr())
+    assert L.bh_gravity(t._h, None, (1 << 32) + 100, 0.5, 1.0, 0.0, o, s) == bh.BH_ERR_INVALID
+    assert L.bh_gravity(t._h, None, 100, float("nan"), 1.0, 0.0, o, s) == bh.BH_ERR_INVALID
+    assert L.bh_gravity(t._h, None, 100, 0.5, float("inf"), 0.0, o, s) == bh.BH_ERR_INVALID
+    assert L.bh_gravity(t._h, None, 100, 0.5, 1.0, 0.0, o, s) == bh.BH_OK
     t.close()
 
 
