@@ -57,16 +57,20 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
 
 // Walk of one wave (see the file comment).  EXACT_T selects ldexp for the
 // level thresholds (w_l / theta)^2 = T0 * 4^-l; otherwise 4^-l is an exponent
-// decrement on the scalar unit (exact whenever T0 * 4^-21 stays normal, and
-// for T0 = 0, inf or NaN with a zero step).
+// decrement on the scalar unit (exact whenever T0 * 4^-21 stays normal), or,
+// with FIXED_T, T0 itself (T0 = 0, inf or NaN is the same at every level).
 //
-// The loop is bound by instruction issue (vector and scalar units both issue
-// about one wave instruction per cycle per CU), so it is written to keep both
-// streams short: node fields stay in scalar registers and feed the vector
-// ops directly, the node address is a 32-bit byte offset, and the lane masks
-// come straight from the comparisons.  The one scalar load per node is not
-// prefetched; the other waves on the SIMD cover its latency.
-template <bool SOFT, bool SELF, bool COUNT, bool EXACT_T, bool ANY_MINE>
+// The loop is bound by instruction issue, and a wave's vector and scalar
+// instructions compete for the same issue slots (register-only FMAs issue at
+// about 1.4 wave instructions per cycle per CU alone and at 0.7 when each is
+// paired with a scalar instruction), so the per-node path is kept short on
+// both units: node fields stay in scalar registers and feed the vector ops
+// directly, the node address is a 32-bit byte offset, the lane masks come
+// straight from the comparisons, the level threshold is two scalar
+// operations, and an opened internal node continues at X + 1 without passing
+// through the leaf code.  The one scalar load per node is not prefetched;
+// the other waves on the SIMD cover its latency.
+template <bool SOFT, bool SELF, bool COUNT, bool EXACT_T, bool ANY_MINE, bool FIXED_T = false>
 __device__ __attribute__((always_inline)) inline void walk_wave(
     const Node *__restrict__ nodes, const float4 *__restrict__ src, uint32_t nn, float4 p,
     uint32_t i, uint32_t wave_base, bool valid, float T0, uint32_t T0_bits, uint32_t T_step,
@@ -88,8 +92,11 @@ __device__ __attribute__((always_inline)) inline void walk_wave(
         const float cz = __uint_as_float(lo.z), m = __uint_as_float(mbits);
         const uint32_t skip = hi.z, meta = hi.w;
         const uint32_t level = node_level(meta);
+        // 4^-level as an exponent decrement: level << 24 is the low byte of
+        // meta shifted up (the leaf bit drops out); FIXED_T: T0 is zero,
+        // infinite or NaN, the same at every level
         const float T = EXACT_T ? ldexpf(T0, -2 * (int)level)
-                                : __uint_as_float(sgpr(T0_bits - level * T_step));
+                                : (FIXED_T ? T0 : __uint_as_float(sgpr(T0_bits - (meta << 24))));
         const float dx = cx - p.x, dy = cy - p.y, dz = cz - p.z;
         const float r2 = fmaf(dz, dz, fmaf(dy, dy, dx * dx));
         // lane masks straight from the two compares
@@ -112,8 +119,11 @@ __device__ __attribute__((always_inline)) inline void walk_wave(
             X = skip;
             continue;
         }
-        const bool leaf = (meta & kLeafBit) != 0;
-        if (leaf && rejoin_before <= X && !(T < r2)) {
+        if ((meta & kLeafBit) == 0) {   // descend into an opened internal node
+            X = X + 1;
+            continue;
+        }
+        if (rejoin_before <= X && !(T < r2)) {
             // lanes that opened a leaf sum its particles; a leaf holding some
             // of this wave's own targets needs the self pair removed
             const uint32_t b = hi.x, e = hi.x + hi.y;
@@ -123,9 +133,7 @@ __device__ __attribute__((always_inline)) inline void walk_wave(
                 leaf_tile<SOFT, false>(src, b, e, i, p, eps2, ax, ay, az, pot);
             if (COUNT) n_int += (e - b) - ((SELF && i >= b && i < e) ? 1u : 0u);
         }
-        // descend into an opened internal node; leave an opened leaf
-        // (for a leaf, skip == X + 1)
-        X = leaf ? skip : X + 1;
+        X = skip;   // leave an opened leaf (skip == X + 1)
     }
 }
 
@@ -226,6 +234,9 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
     const bool exact = !fixed && T0_exp <= 44u;
     const uint32_t T_step = fixed ? 0u : (1u << 24);
 
+    // wait for the target's position here: a first use inside the walk loop
+    // would put the wait on every iteration
+    asm volatile("" ::"v"(p.x), "v"(p.y), "v"(p.z));
     float ax = 0.f, ay = 0.f, az = 0.f, pot = 0.f;
     uint32_t n_int = 0;
     if (VOTE) {
@@ -238,7 +249,11 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
                                                           T0, T0_bits, T_step, eps2, ax, ay, az,
                                                           pot, n_int);
     } else {
-        if (exact)
+        if (fixed)
+            walk_wave<SOFT, SELF, COUNT, false, UNSORTED, true>(nodes, src, nn, p, i, wave_base,
+                                                                valid, T0, T0_bits, T_step, eps2,
+                                                                ax, ay, az, pot, n_int);
+        else if (exact)
             walk_wave<SOFT, SELF, COUNT, true, UNSORTED>(nodes, src, nn, p, i, wave_base, valid, T0,
                                                          T0_bits, T_step, eps2, ax, ay, az, pot,
                                                          n_int);
