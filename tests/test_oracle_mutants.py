@@ -2,9 +2,14 @@
 
 Each case plants one mistake in a copy of oracle.c (a text substitution; the
 oracle itself is untouched), compiles it on the CPU, and runs the pin tests of
-test_oracle.py against it: at least one pin must fail.  CPU only."""
+test_oracle.py against it in a child process: at least one pin must fail.  A
+planted mistake can make the C code write out of bounds (no depth limit,
+unclamped keys), so the mutated library is never loaded into the test process
+itself; a child that dies counts as caught.  CPU only."""
+import json
 import os
 import subprocess
+import sys
 import tempfile
 
 import pytest
@@ -122,17 +127,44 @@ def _run_pins_against(lib_path):
     return failed
 
 
-def test_unmutated_copy_passes_every_pin(orc):
-    """Control: the harness itself makes no pin fail."""
+_CHILD = """
+import json, sys
+sys.path[:0] = [sys.argv[2], sys.argv[3]]
+import test_oracle_mutants as m
+print("FAILED_PINS " + json.dumps(m._run_pins_against(sys.argv[1])), flush=True)
+"""
+
+
+def _pins_in_child(lib_path):
+    """Failed pin names from a child process, or None when the child died."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    env = dict(os.environ, OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-c", _CHILD, lib_path, here, os.path.dirname(here)],
+                       capture_output=True, text=True, timeout=600, env=env)
+    for line in r.stdout.splitlines():
+        if line.startswith("FAILED_PINS "):
+            return json.loads(line[len("FAILED_PINS "):])
+    return None
+
+
+@pytest.fixture(scope="module")
+def mutant_results(orc):
+    """Every mutant (and the unmutated control) built and run, four at a time."""
+    from concurrent.futures import ThreadPoolExecutor
+    cases = [("control", "", "")] + MUTANTS
     with tempfile.TemporaryDirectory() as d:
-        lib = _build_mutant("control", "", "", d)
-        failed = _run_pins_against(lib)
-    assert not failed, failed
+        def one(case):
+            return case[0], _pins_in_child(_build_mutant(case[0], case[1], case[2], d))
+        with ThreadPoolExecutor(max_workers=4) as pool:
+            return dict(pool.map(one, cases))
+
+
+def test_unmutated_copy_passes_every_pin(mutant_results):
+    """Control: the harness itself makes no pin fail, and the child runs to its end."""
+    assert mutant_results["control"] == [], mutant_results["control"]
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_pins_catch_planted_mistake(orc, name, old, new):
-    with tempfile.TemporaryDirectory() as d:
-        lib = _build_mutant(name, old, new, d)
-        failed = _run_pins_against(lib)
-    assert failed, "no pin caught the planted mistake %r" % name
+def test_pins_catch_planted_mistake(mutant_results, name, old, new):
+    failed = mutant_results[name]
+    assert failed is None or failed, "no pin caught the planted mistake %r" % name
