@@ -176,6 +176,35 @@ def test_theta_infinite_is_root_monopole(orc):
     t.close()
 
 
+@pytest.mark.parametrize("case", ["tiny_cube", "huge_theta"])
+def test_thresholds_below_the_exponent_step(orc, case):
+    """(L / theta)^2 below 2^-83, where stepping the exponent by 2 per level
+    would leave the normal range: the walk computes the level thresholds with
+    ldexp instead.  A Plummer sphere scaled to a 7e-14 cube at theta = 0.5
+    (tree levels down to a few 1e-16) with masses scaled by the square of the
+    length scale, so accelerations stay of order one and m r^-3 stays inside the
+    fp32 range, and a unit-scale one at theta = 1e16."""
+    p = W.plummer(1 << 12, seed=12)
+    if case == "tiny_cube":
+        s = 2e-15
+        p = p.copy()
+        p[:, :3] *= np.float32(s)
+        p[:, 3] *= np.float32(s * s)
+        theta, eps = 0.5, 2e-17
+    else:
+        theta, eps = 1e16, 0.01
+    log("exact thresholds", case)
+    t = make_tree(p)
+    got = t.gravity(theta, 1.0, eps).cpu().numpy()
+    ref = orc.Tree(p)
+    modes = [ref.gravity(theta, 1.0, eps, tie_mode=m) for m in (0, 1, 2)]
+    assert_walk_parity(got, [m[0] for m in modes], modes[0][2], case)
+    cnt = t.count_interactions(theta, eps)
+    lo_c, hi_c = modes[2][1].sum(), modes[1][1].sum()
+    assert lo_c <= cnt <= hi_c, (cnt, lo_c, hi_c)
+    t.close()
+
+
 def test_zero_softening_coincident_pairs(orc):
     # eps = 0 with coincident particles: such pairs must add nothing
     base = W.uniform_cube(600, seed=11)
