@@ -14,6 +14,8 @@
 // correctly rounded IEEE operation, so the keys are reproducible bit for bit.
 #include "bh_internal.h"
 
+#include <algorithm>
+
 namespace bh {
 constexpr int kHilbertMaxStates = 64;
 }
@@ -197,61 +199,102 @@ HilbertTable build_hilbert_table()
     return tab;
 }
 
-const HilbertTable &hilbert_table()
+}  // namespace
+
+// The automaton's tables indexed by Morton triples (z << 2 | y << 1 | x, the
+// triples of the interleaved code): [0, 48 * 64) two levels per entry,
+// (digit_hi << 3 | digit_lo) | next state << 6; then [48 * 64, + 48 * 8) one level,
+// digit | next state << 3.  False if the automaton does not have the expected
+// 48 states (it always does).
+bool hilbert_lut_host(uint16_t *out)
 {
-    static const HilbertTable t = build_hilbert_table();
-    return t;
+    const HilbertTable t = build_hilbert_table();
+    auto rev3 = [](uint32_t v) { return ((v & 1u) << 2) | (v & 2u) | ((v >> 2) & 1u); };
+    uint32_t states = 1;
+    for (int k = 0; k < kHilbertMaxStates * 8; ++k) states = std::max(states, (uint32_t)(t.e[k] >> 3) + 1);
+    if (states != (uint32_t)kHilbertStates) return false;
+    for (uint32_t st = 0; st < (uint32_t)kHilbertStates; ++st) {
+        for (uint32_t mt = 0; mt < 8; ++mt)
+            out[kHilbertStates * 64 + st * 8 + mt] = t.e[st * 8 + rev3(mt)];
+        for (uint32_t hi = 0; hi < 8; ++hi)
+            for (uint32_t lo = 0; lo < 8; ++lo) {
+                const uint32_t e1 = t.e[st * 8 + rev3(hi)];
+                const uint32_t e2 = t.e[(e1 >> 3) * 8 + rev3(lo)];
+                out[st * 64 + (hi << 3 | lo)] =
+                    (uint16_t)(((e1 & 7u) << 3) | (e2 & 7u) | ((e2 >> 3) << 6));
+            }
+    }
+    return true;
 }
 
+namespace {
+
+// Keys of KPT consecutive points per thread.  Hilbert keys: the quantised
+// coordinates are interleaved into the Morton code first (z y x in each 3-bit
+// triple), and the automaton then reads two levels per lookup, a 6-bit field of
+// that code, from the two-level table (copied into LDS); an odd level count
+// ends with one one-level lookup.
+constexpr int kKeyThreads = 256;
+constexpr int kKeysPerThread = 2;
+
 template <bool HILBERT, int BITS>
-__global__ __launch_bounds__(256) void k_morton(const float4 *__restrict__ pts, uint32_t n,
-                                                const DevParams *__restrict__ prm,
-                                                const HilbertTable tab,
-                                                uint64_t *__restrict__ keys,
-                                                uint32_t *__restrict__ idx)
+__global__ __launch_bounds__(kKeyThreads) void k_morton(const float4 *__restrict__ pts, uint32_t n,
+                                                        const DevParams *__restrict__ prm,
+                                                        const uint16_t *__restrict__ hlut,
+                                                        uint64_t *__restrict__ keys,
+                                                        uint32_t *__restrict__ idx)
 {
-    __shared__ uint16_t lut[HILBERT ? kHilbertMaxStates * 8 : 1];
+    __shared__ __attribute__((aligned(16))) uint16_t lut[HILBERT ? kHilbertLutEntries : 8];
     if (HILBERT) {
-        for (int k = threadIdx.x; k < kHilbertMaxStates * 8; k += 256) lut[k] = tab.e[k];
+        const uint4 *g = reinterpret_cast<const uint4 *>(hlut);
+        uint4 *l = reinterpret_cast<uint4 *>(lut);
+        for (int k = threadIdx.x; k < kHilbertLutEntries / 8; k += kKeyThreads) l[k] = g[k];
         __syncthreads();
     }
-    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    const float4 p = pts[i];
+    const uint16_t *lut2 = lut, *lut1 = lut + kHilbertStates * 64;
     const uint64_t top = (1ull << BITS) - 1;
     const double s = prm->scale;
-    const uint64_t qx = quantise(p.x, prm->lo[0], s, top);
-    const uint64_t qy = quantise(p.y, prm->lo[1], s, top);
-    const uint64_t qz = quantise(p.z, prm->lo[2], s, top);
-    uint64_t key;
-    if (HILBERT) {
-        const uint32_t x = (uint32_t)qx, y = (uint32_t)qy, z = (uint32_t)qz;
-        uint32_t state = 0;
-        key = 0;
+    const uint32_t base = blockIdx.x * (kKeyThreads * kKeysPerThread) + threadIdx.x;
 #pragma unroll
-        for (int q = BITS - 1; q >= 0; --q) {
-            const uint32_t r = (((x >> q) & 1u) << 2) | (((y >> q) & 1u) << 1) | ((z >> q) & 1u);
-            const uint32_t e = lut[state * 8 + r];
-            key = (key << 3) | (e & 7u);
-            state = e >> 3;
+    for (int t = 0; t < kKeysPerThread; ++t) {
+        const uint32_t i = base + t * kKeyThreads;
+        if (i >= n) break;
+        const float4 p = pts[i];
+        const uint64_t qx = quantise(p.x, prm->lo[0], s, top);
+        const uint64_t qy = quantise(p.y, prm->lo[1], s, top);
+        const uint64_t qz = quantise(p.z, prm->lo[2], s, top);
+        const uint64_t m = spread3(qx) | (spread3(qy) << 1) | (spread3(qz) << 2);
+        uint64_t key = m;
+        if (HILBERT) {
+            uint32_t state = 0;
+            key = 0;
+#pragma unroll
+            for (int q = BITS - 1; q >= 1; q -= 2) {
+                const uint32_t f = (uint32_t)(m >> (3 * (q - 1))) & 63u;
+                const uint32_t e = lut2[state * 64 + f];
+                key = (key << 6) | (e & 63u);
+                state = e >> 6;
+            }
+            if (BITS & 1) {
+                const uint32_t e = lut1[state * 8 + ((uint32_t)m & 7u)];
+                key = (key << 3) | (e & 7u);
+            }
         }
-    } else {
-        key = spread3(qx) | (spread3(qy) << 1) | (spread3(qz) << 2);
+        keys[i] = key;
+        idx[i] = i;
     }
-    keys[i] = key;
-    idx[i] = i;
 }
 
 template <bool HILBERT>
-void launch_keys(const float4 *pts, uint32_t n, const DevParams *prm, int bits, uint64_t *keys,
-                 uint32_t *idx, hipStream_t s)
+void launch_keys(const float4 *pts, uint32_t n, const DevParams *prm, int bits,
+                 const uint16_t *hlut, uint64_t *keys, uint32_t *idx, hipStream_t s)
 {
-    const dim3 grid((n + 255) / 256), block(256);
-    const HilbertTable &tab = hilbert_table();
+    const dim3 grid((n + kKeyThreads * kKeysPerThread - 1) / (kKeyThreads * kKeysPerThread));
+    const dim3 block(kKeyThreads);
     if (bits == 21)
-        hipLaunchKernelGGL((k_morton<HILBERT, 21>), grid, block, 0, s, pts, n, prm, tab, keys, idx);
+        hipLaunchKernelGGL((k_morton<HILBERT, 21>), grid, block, 0, s, pts, n, prm, hlut, keys, idx);
     else
-        hipLaunchKernelGGL((k_morton<HILBERT, 10>), grid, block, 0, s, pts, n, prm, tab, keys, idx);
+        hipLaunchKernelGGL((k_morton<HILBERT, 10>), grid, block, 0, s, pts, n, prm, hlut, keys, idx);
 }
 
 }  // namespace
@@ -274,12 +317,12 @@ void launch_bbox(const float4 *src, uint32_t n, float *partials, uint32_t n_part
 }
 
 void launch_morton(const float4 *pts, uint32_t n, const DevParams *prm, int bits, int curve,
-                   uint64_t *keys, uint32_t *idx, hipStream_t s)
+                   const uint16_t *hilbert_lut, uint64_t *keys, uint32_t *idx, hipStream_t s)
 {
     if (n == 0) return;
     // bits is 21 (63-bit keys) or 10 (30-bit keys); bh_create admits no other
-    if (curve == 1) launch_keys<true>(pts, n, prm, bits, keys, idx, s);
-    else launch_keys<false>(pts, n, prm, bits, keys, idx, s);
+    if (curve == 1) launch_keys<true>(pts, n, prm, bits, hilbert_lut, keys, idx, s);
+    else launch_keys<false>(pts, n, prm, bits, hilbert_lut, keys, idx, s);
 }
 
 }  // namespace bh

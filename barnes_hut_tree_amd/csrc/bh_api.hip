@@ -25,6 +25,7 @@ struct bh_ctx {
     float *bbox_part = nullptr;
     uint64_t *keys = nullptr, *keys_alt = nullptr;
     uint32_t *vals = nullptr, *vals_alt = nullptr;
+    uint16_t *hlut = nullptr;         // Hilbert key tables (kHilbertLutEntries)
     uint32_t *spine = nullptr;
     float4 *spos = nullptr;
     uint64_t *keys_sorted = nullptr;  // aliases keys or keys_alt after a build
@@ -68,7 +69,7 @@ hipError_t dalloc(T **p, size_t count)
 
 void free_all(bh_ctx *c)
 {
-    void *ptrs[] = {c->prm, c->bbox_part, c->keys, c->keys_alt, c->vals, c->vals_alt, c->spine,
+    void *ptrs[] = {c->prm, c->hlut, c->bbox_part, c->keys, c->keys_alt, c->vals, c->vals_alt, c->spine,
                     c->spos, c->bw.dc, c->bw.tile_counts, c->bw.tile_sums, c->bw.chunk_tot, c->bw.tile_scan,
                     c->bw.first_node, c->bw.P, c->nodes, c->tkeys, c->tkeys_alt, c->tvals,
                     c->tvals_alt, c->tspine, c->tpos, c->inv, c->diag, c->lk_child,
@@ -143,6 +144,14 @@ bh_status bh_create(bh_ctx **out, int64_t max_sources, int64_t max_targets,
     const size_t tiles = build_blocks((uint32_t)ns);
     bool ok = true;
     ok &= dalloc(&c->prm, 1) == hipSuccess;
+    {
+        uint16_t host_lut[kHilbertLutEntries];
+        ok &= hilbert_lut_host(host_lut);
+        ok &= dalloc(&c->hlut, (size_t)kHilbertLutEntries) == hipSuccess;
+        if (ok)
+            ok &= hipMemcpy(c->hlut, host_lut, sizeof(host_lut), hipMemcpyHostToDevice) ==
+                  hipSuccess;
+    }
     ok &= hipHostMalloc((void **)&c->host_prm, sizeof(DevParams), hipHostMallocDefault) == hipSuccess;
     ok &= dalloc(&c->bbox_part, 8 * 1024) == hipSuccess;
     ok &= dalloc(&c->keys, ns) == hipSuccess;
@@ -203,7 +212,7 @@ bh_status bh_build(bh_ctx *c, const float *src_pos_mass, int64_t n, void *stream
     record(c, 0, s);
     launch_bbox(src, un, c->bbox_part, bbox_partials(un), c->prm, c->bits, s);
     if (un > 0) {
-        launch_morton(src, un, c->prm, c->bits, c->curve, c->keys, c->vals, s);
+        launch_morton(src, un, c->prm, c->bits, c->curve, c->hlut, c->keys, c->vals, s);
         record(c, 1, s);
         radix_sort(c->keys, c->vals, c->keys_alt, c->vals_alt, &c->keys_sorted, &c->perm, un,
                    c->key_bits, c->spine, src, c->spos, s);
@@ -228,7 +237,8 @@ static const uint32_t *sort_targets(bh_ctx *c, const float *targets, uint32_t nt
 {
     uint64_t *ko;
     uint32_t *vo;
-    launch_morton((const float4 *)targets, nt, c->prm, c->bits, c->curve, c->tkeys, c->tvals, s);
+    launch_morton((const float4 *)targets, nt, c->prm, c->bits, c->curve, c->hlut, c->tkeys,
+                  c->tvals, s);
     radix_sort(c->tkeys, c->tvals, c->tkeys_alt, c->tvals_alt, &ko, &vo, nt, c->key_bits,
                c->tspine, (const float4 *)targets, c->tpos, s);
     return vo;
@@ -398,7 +408,7 @@ bh_status bh_build_locked(bh_ctx *c, const float *src_pos_mass, int64_t n, void 
     const float4 *src = (const float4 *)src_pos_mass;
     launch_bbox(src, un, c->bbox_part, bbox_partials(un), c->prm, c->bits, s);
     // the dense build indexes slots by octant: Morton keys whatever the curve
-    if (un > 0) launch_morton(src, un, c->prm, c->bits, 0, c->keys, c->vals, s);
+    if (un > 0) launch_morton(src, un, c->prm, c->bits, 0, c->hlut, c->keys, c->vals, s);
     launch_lock_build(c->keys, un, c->bits, c->lk_child, c->lk_level, c->lk_next, c->lk_cap,
                       c->lk_counter, c->prm, s);
     c->lk_n = un;

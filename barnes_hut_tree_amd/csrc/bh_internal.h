@@ -97,8 +97,13 @@ __device__ inline uint64_t quantise(float x, double lo, double scale, uint64_t t
 void launch_bbox(const float4 *src, uint32_t n, float *partials, uint32_t n_partials,
                  DevParams *prm, int bits, hipStream_t s);
 uint32_t bbox_partials(uint32_t n);
-// curve 0: Morton keys, 1: Hilbert keys
+// curve 0: Morton keys, 1: Hilbert keys (hilbert_lut: the device copy of the
+// tables hilbert_lut_host fills, kHilbertLutEntries entries; unused for Morton)
+constexpr int kHilbertStates = 48;
+constexpr int kHilbertLutEntries = kHilbertStates * 64 + kHilbertStates * 8;
+bool hilbert_lut_host(uint16_t *out);
 void launch_morton(const float4 *pts, uint32_t n, const DevParams *prm, int bits, int curve,
+                   const uint16_t *hilbert_lut,
                    uint64_t *keys, uint32_t *idx, hipStream_t s);
 
 // radix_sort.hip
