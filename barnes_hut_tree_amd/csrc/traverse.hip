@@ -20,6 +20,12 @@
 // all lanes descend when any lane must; here the ballot only decides where
 // the wave goes, and the per-lane rejoin index keeps each lane's result its
 // own).
+//
+// The common step (every active lane uses the node whole, or some lane opens
+// an internal node) is a short loop written in assembly: the build writes an
+// end record after the last node, which every lane still walking opens, so the
+// loop needs no bound check and leaves only at a leaf some lane opens.  The
+// leaf sums are C++.
 #include "bh_internal.h"
 #include "interaction.h"
 
@@ -27,6 +33,30 @@ namespace bh {
 namespace {
 
 constexpr int kWalkThreads = 64;
+
+// One source of an opened leaf: the interaction of pair() (interaction.h),
+// with eps2 taken from a vector register and the potential term subtracted
+// after rounding instead of fused.  A vector op with a scalar-register
+// operand issues at about 0.9 wave instructions per cycle per CU, one with
+// register operands only at 1.3-1.9, and this keeps two of the thirteen ops
+// register-only.
+template <bool SOFT>
+__device__ __attribute__((always_inline)) inline void leaf_pair(float4 s, float px, float py,
+                                                                float pz, float eps2v, float &ax,
+                                                                float &ay, float &az, float &pot)
+{
+#pragma clang fp contract(off)
+    const float dx = s.x - px, dy = s.y - py, dz = s.z - pz;
+    const float r2 = fmaf(dz, dz, fmaf(dy, dy, fmaf(dx, dx, eps2v)));
+    float inv = __builtin_amdgcn_rsqf(r2);
+    if (!SOFT) inv = r2 > 0.f ? inv : 0.f;
+    const float mi = s.w * inv;
+    const float f = mi * inv * inv;
+    ax = fmaf(f, dx, ax);
+    ay = fmaf(f, dy, ay);
+    az = fmaf(f, dz, az);
+    pot = pot - mi;
+}
 
 // Direct sum over the sources [b, e) of an opened leaf, eight at a time (one
 // batch of scalar loads per eight).  MINE: the leaf may hold this lane's own
@@ -47,7 +77,7 @@ __device__ __attribute__((always_inline)) inline void leaf_tile(
         for (int k = 0; k < 8; ++k) {
             if ((uint32_t)k < left) {
                 if (MINE) s[k].w = (j + k == i) ? 0.f : s[k].w;
-                pair<SOFT>(s[k], p.x, p.y, p.z, eps2, ax, ay, az, pot);
+                leaf_pair<SOFT>(s[k], p.x, p.y, p.z, eps2, ax, ay, az, pot);
             }
         }
     }
@@ -55,21 +85,118 @@ __device__ __attribute__((always_inline)) inline void leaf_tile(
 
 __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// The assembly loop of the walk.  Register use: the node records of two
+// consecutive visits land in s[72:79] and s[80:87] (x, y, z, m, start, count,
+// skip, meta), so the next visit's node index is the previous record's skip
+// field where it lies.  One visit of node XR (record slot R0..R7, loaded
+// through RT):
+//   act  = rejoin <= X                         (vcc)
+//   T    = T0 * 4^-level, the exponent of T0 stepped down by 2 * level
+//   far  = T < r^2                              (per lane)
+//   lanes in act & far add the monopole and set rejoin = skip
+//   open = act & ~far                           (SCC: some lane opens X)
+// The monopole is inv = rsq(r^2 + eps^2), f = m inv^3, a += f d, pot -= m inv,
+// with eps^2 in a vector register and the potential term unfused, so that all
+// but the node-field operands are register-only.  One independent instruction
+// (the rejoin move) sits between the reciprocal square root and the first use
+// of its result, which the hardware requires.  A wave in which no lane
+// accepts skips the monopole.  CNT: the interaction count update, if any.
+#define BH_VISIT(R0, R1, R2, R3, R6, R7, RT, XR, CNT, SKIP_LABEL)                       \
+    "s_lshl_b32 %[off], " XR ", 5\n"                                                   \
+    "s_load_dwordx8 " RT ", %[nb], %[off]\n"                                           \
+    "v_cmp_ge_u32_e32 vcc, " XR ", %[rej]\n"                                           \
+    "s_waitcnt lgkmcnt(0)\n"                                                           \
+    "v_sub_f32_e32 %[dx], " R0 ", %[px]\n"                                             \
+    "v_sub_f32_e32 %[dy], " R1 ", %[py]\n"                                             \
+    "v_mul_f32_e32 %[r2], %[dx], %[dx]\n"                                              \
+    "s_lshl_b32 %[t], " R7 ", 24\n"                                                    \
+    "v_sub_f32_e32 %[dz], " R2 ", %[pz]\n"                                             \
+    "v_fmac_f32_e32 %[r2], %[dy], %[dy]\n"                                             \
+    "s_sub_u32 %[t], %[T0], %[t]\n"                                                    \
+    "v_fmac_f32_e32 %[r2], %[dz], %[dz]\n"                                             \
+    "v_cmp_lt_f32_e64 %[far], %[t], %[r2]\n"                                           \
+    "s_and_b64 %[use], vcc, %[far]\n"                                                  \
+    "s_and_saveexec_b64 %[save], %[use]\n"                                             \
+    "s_cbranch_execz " SKIP_LABEL "\n"                                                 \
+    "v_add_f32_e32 %[w], %[eps2], %[r2]\n"                                             \
+    "v_rsq_f32_e32 %[w], %[w]\n"                                                       \
+    "v_mov_b32_e32 %[rej], " R6 "\n"                                                   \
+    "v_mul_f32_e32 %[f], " R3 ", %[w]\n"                                               \
+    "v_sub_f32_e32 %[pot], %[pot], %[f]\n"                                             \
+    "v_mul_f32_e32 %[f], %[w], %[f]\n"                                                 \
+    "v_mul_f32_e32 %[f], %[w], %[f]\n"                                                 \
+    "v_fmac_f32_e32 %[ax], %[f], %[dx]\n"                                              \
+    "v_fmac_f32_e32 %[ay], %[f], %[dy]\n"                                              \
+    "v_fmac_f32_e32 %[az], %[f], %[dz]\n"                                              \
+    CNT                                                                                \
+    SKIP_LABEL ":\n"                                                                   \
+    "s_mov_b64 exec, %[save]\n"                                                        \
+    "s_andn2_b64 %[open], vcc, %[far]\n"
+
+// Visits from node X on, two per loop turn (slots A and B).  A node no lane
+// opens moves the wave to its skip; an opened internal node (meta without the
+// leaf bit) to X + 1.  The loop returns at the first opened leaf, which may be
+// the end record, with its index in X and its start, count and skip.  Every
+// step moves X forward, and the end record ends the loop at the latest.
+#define BH_RUN(CNT)                                                                    \
+    "s_mov_b32 s86, %[X]\n"                                                            \
+    "BH_A%=:\n"                                                                        \
+    BH_VISIT("s72", "s73", "s74", "s75", "s78", "s79", "s[72:79]", "s86", CNT,         \
+             "BH_NA%=")                                                                \
+    "s_cbranch_scc1 BH_OA%=\n"                                                         \
+    "BH_B%=:\n"                                                                        \
+    BH_VISIT("s80", "s81", "s82", "s83", "s86", "s87", "s[80:87]", "s78", CNT,         \
+             "BH_NB%=")                                                                \
+    "s_cbranch_scc0 BH_A%=\n"                                                          \
+    "s_bitcmp1_b32 s87, 8\n"                                                           \
+    "s_cbranch_scc1 BH_XB%=\n"                                                         \
+    "s_add_u32 s86, s78, 1\n"                                                          \
+    "s_branch BH_A%=\n"                                                                \
+    "BH_OA%=:\n"                                                                       \
+    "s_bitcmp1_b32 s79, 8\n"                                                           \
+    "s_cbranch_scc1 BH_XA%=\n"                                                         \
+    "s_add_u32 s78, s86, 1\n"                                                          \
+    "s_branch BH_B%=\n"                                                                \
+    "BH_XB%=:\n"                                                                       \
+    "s_mov_b32 %[X], s78\n"                                                            \
+    "s_mov_b32 %[first], s84\n"                                                        \
+    "s_mov_b32 %[cnt], s85\n"                                                          \
+    "s_mov_b32 %[skip], s86\n"                                                         \
+    "s_branch BH_E%=\n"                                                                \
+    "BH_XA%=:\n"                                                                       \
+    "s_mov_b32 %[X], s86\n"                                                            \
+    "s_mov_b32 %[first], s76\n"                                                        \
+    "s_mov_b32 %[cnt], s77\n"                                                          \
+    "s_mov_b32 %[skip], s78\n"                                                         \
+    "BH_E%=:\n"
+
+#define BH_RUN_OUTS                                                                    \
+    [X] "+s"(X), [ax] "+v"(ax), [ay] "+v"(ay), [az] "+v"(az), [pot] "+v"(pot),        \
+        [rej] "+v"(rejoin), [first] "=&s"(first), [cnt] "=&s"(cnt), [skip] "=&s"(skip), \
+        [dx] "=&v"(dx), [dy] "=&v"(dy), [dz] "=&v"(dz), [r2] "=&v"(r2), [w] "=&v"(w),    \
+        [f] "=&v"(f), [off] "=&s"(off), [t] "=&s"(t), [far] "=&s"(far), [use] "=&s"(use), \
+        [save] "=&s"(save), [open] "=&s"(open)
+#define BH_RUN_INS                                                                     \
+    [nb] "s"(nb), [T0] "s"(T0_bits), [eps2] "v"(eps2v), [px] "v"(p.x), [py] "v"(p.y),  \
+        [pz] "v"(p.z)
+#define BH_RUN_CLOBBERS                                                                \
+    "s72", "s73", "s74", "s75", "s76", "s77", "s78", "s79", "s80", "s81", "s82", "s83", \
+        "s84", "s85", "s86", "s87", "vcc", "scc", "memory"
+
 // Walk of one wave (see the file comment).  EXACT_T selects ldexp for the
 // level thresholds (w_l / theta)^2 = T0 * 4^-l; otherwise 4^-l is an exponent
 // decrement on the scalar unit (exact whenever T0 * 4^-21 stays normal), or,
 // with FIXED_T, T0 itself (T0 = 0, inf or NaN is the same at every level).
 //
-// The loop is bound by instruction issue, and a wave's vector and scalar
-// instructions compete for the same issue slots (register-only FMAs issue at
-// about 1.4 wave instructions per cycle per CU alone and at 0.7 when each is
-// paired with a scalar instruction), so the per-node path is kept short on
-// both units: node fields stay in scalar registers and feed the vector ops
-// directly, the node address is a 32-bit byte offset, the lane masks come
-// straight from the comparisons, the level threshold is two scalar
-// operations, and an opened internal node continues at X + 1 without passing
-// through the leaf code.  The one scalar load per node is not prefetched;
-// the other waves on the SIMD cover its latency.
+// The walk is bound by instruction issue.  A wave's vector and scalar
+// instructions share its issue slots, and a vector op with a scalar-register
+// operand issues at about two thirds the rate of one with register operands
+// only.  The assembly loop (above) keeps the per-node path to 18 vector ops,
+// 7 of them with a scalar operand, 9 scalar instructions and 2 branches; the
+// compiled form of the same loop had 18 vector ops with 9 scalar operands, 13
+// scalar instructions and 3 branches, because the compiler re-derives the
+// lane masks and the loop exit on every node.  The two rarer thresholds keep
+// the compiled loop.
 template <bool SOFT, bool SELF, bool COUNT, bool EXACT_T, bool ANY_MINE, bool FIXED_T = false>
 __device__ __attribute__((always_inline)) inline void walk_wave(
     const Node *__restrict__ nodes, const float4 *__restrict__ src, uint32_t nn, float4 p,
@@ -80,9 +207,53 @@ __device__ __attribute__((always_inline)) inline void walk_wave(
     // Lane state: a lane takes part at node X when rejoin <= X.  A lane that
     // uses a node whole sets rejoin = skip(node) and so sits out the node's
     // subtree; lanes that open a node keep theirs.  (The wave lands on every
-    // such skip on its way out, so `<=` and `==` select the same lanes.)
+    // such skip on its way out, so `<=` and `==` select the same lanes.)  After
+    // the visit of X, the lanes with rejoin <= X are exactly those that opened
+    // it.
     uint32_t rejoin = valid ? 0u : 0xffffffffu;
     uint32_t X = 0;
+    // a leaf opened by some lane: its openers sum its particles; a leaf
+    // holding some of this wave's own targets needs the self pair removed
+    auto open_leaf = [&](uint32_t b, uint32_t e, float e2) {
+        if (rejoin <= X) {
+            if (SELF && (ANY_MINE || (b < wave_base + 64 && e > wave_base)))
+                leaf_tile<SOFT, true>(src, b, e, i, p, e2, ax, ay, az, pot);
+            else
+                leaf_tile<SOFT, false>(src, b, e, i, p, e2, ax, ay, az, pot);
+            if (COUNT) n_int += (e - b) - ((SELF && i >= b && i < e) ? 1u : 0u);
+        }
+    };
+    if constexpr (!EXACT_T && !FIXED_T) {
+        const uint64_t nb = (uint64_t)node_bytes;
+        float eps2v = eps2;
+        asm volatile("" : "+v"(eps2v));   // held in a vector register
+        for (;;) {
+            X = sgpr(X);
+            uint32_t first, cnt, skip, off, t;
+            float dx, dy, dz, r2, w, f;
+            uint64_t far, use, save, open;
+            if constexpr (COUNT) {
+                uint32_t ni = n_int;
+                asm volatile(BH_RUN("v_add_u32_e32 %[ni], 1, %[ni]\n")
+                             : BH_RUN_OUTS, [ni] "+v"(ni)
+                             : BH_RUN_INS
+                             : BH_RUN_CLOBBERS);
+                n_int = ni;
+            } else {
+                asm volatile(BH_RUN("") : BH_RUN_OUTS : BH_RUN_INS : BH_RUN_CLOBBERS);
+            }
+            // the outputs are scalar registers; the compiler takes asm
+            // outputs for per-lane values unless told
+            X = sgpr(X);
+            first = sgpr(first);
+            cnt = sgpr(cnt);
+            skip = sgpr(skip);
+            if (X >= nn) break;   // the end record
+            open_leaf(first, first + cnt, eps2v);
+            X = skip;   // leave the leaf (skip == X + 1)
+        }
+        return;
+    }
     while (X < nn) {
         const uint4 *rec = reinterpret_cast<const uint4 *>(node_bytes + X * (uint32_t)sizeof(Node));
         const uint4 lo = rec[0], hi = rec[1];
@@ -92,18 +263,12 @@ __device__ __attribute__((always_inline)) inline void walk_wave(
         const float cz = __uint_as_float(lo.z), m = __uint_as_float(mbits);
         const uint32_t skip = hi.z, meta = hi.w;
         const uint32_t level = node_level(meta);
-        // 4^-level as an exponent decrement: level << 24 is the low byte of
-        // meta shifted up (the leaf bit drops out); FIXED_T: T0 is zero,
-        // infinite or NaN, the same at every level
-        const float T = EXACT_T ? ldexpf(T0, -2 * (int)level)
-                                : (FIXED_T ? T0 : __uint_as_float(sgpr(T0_bits - (meta << 24))));
+        const float T = EXACT_T ? ldexpf(T0, -2 * (int)level) : T0;
         const float dx = cx - p.x, dy = cy - p.y, dz = cz - p.z;
         const float r2 = fmaf(dz, dz, fmaf(dy, dy, dx * dx));
-        // lane masks straight from the two compares
         const uint64_t act_m = __ballot(rejoin <= X);
         const uint64_t far_m = __ballot(T < r2);
         const uint64_t open_m = act_m & ~far_m;
-        const uint32_t rejoin_before = rejoin;
         if (rejoin <= X && T < r2) {
             const float inv = __builtin_amdgcn_rsqf(r2 + eps2);
             const float mi = m * inv;
@@ -123,16 +288,7 @@ __device__ __attribute__((always_inline)) inline void walk_wave(
             X = X + 1;
             continue;
         }
-        if (rejoin_before <= X && !(T < r2)) {
-            // lanes that opened a leaf sum its particles; a leaf holding some
-            // of this wave's own targets needs the self pair removed
-            const uint32_t b = hi.x, e = hi.x + hi.y;
-            if (SELF && (ANY_MINE || (b < wave_base + 64 && e > wave_base)))
-                leaf_tile<SOFT, true>(src, b, e, i, p, eps2, ax, ay, az, pot);
-            else
-                leaf_tile<SOFT, false>(src, b, e, i, p, eps2, ax, ay, az, pot);
-            if (COUNT) n_int += (e - b) - ((SELF && i >= b && i < e) ? 1u : 0u);
-        }
+        open_leaf(hi.x, hi.x + hi.y, eps2);
         X = skip;   // leave an opened leaf (skip == X + 1)
     }
 }
@@ -207,7 +363,7 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
 {
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t blk = xcd_block(blockIdx.x, gridDim.x);
-    const uint32_t wave_base = blk * kWalkThreads + (threadIdx.x & ~63u);
+    const uint32_t wave_base = sgpr(blk * kWalkThreads + (threadIdx.x & ~63u));
     const uint32_t c = wave_base + lane;
     const bool valid = c < n;
     if (wave_base >= n) return;
