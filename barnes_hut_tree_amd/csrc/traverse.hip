@@ -21,11 +21,11 @@
 // the wave goes, and the per-lane rejoin index keeps each lane's result its
 // own).
 //
-// The common step (every active lane uses the node whole, or some lane opens
-// an internal node) is a short loop written in assembly: the build writes an
-// end record after the last node, which every lane still walking opens, so the
-// loop needs no bound check and leaves only at a leaf some lane opens.  The
-// leaf sums are C++.
+// The walk is a loop written in assembly: node visits, descents and the sums
+// of opened leaves.  The build writes an end record after the last node,
+// which every lane still walking opens, so the loop needs no bound check; it
+// returns to C++ at that record and at leaves that may hold the wave's own
+// targets, where the self pair is masked.
 #include "bh_internal.h"
 #include "interaction.h"
 
@@ -133,12 +133,46 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     "s_mov_b64 exec, %[save]\n"                                                        \
     "s_andn2_b64 %[open], vcc, %[far]\n"
 
+// One source of a leaf opened in the assembly loop, in the order of
+// leaf_pair(): X, Y, Z, M name the source's scalar registers.  GUARD is the
+// r^2 > 0 test of the unsoftened interaction (with softening, a nop keeps
+// the reciprocal square root one instruction from its first use).
+#define BH_PAIR(X, Y, Z, M, GUARD)                                                     \
+    "v_sub_f32_e32 %[dx], " X ", %[px]\n"                                              \
+    "v_sub_f32_e32 %[dy], " Y ", %[py]\n"                                              \
+    "v_fma_f32 %[r2], %[dx], %[dx], %[eps2]\n"                                         \
+    "v_sub_f32_e32 %[dz], " Z ", %[pz]\n"                                              \
+    "v_fmac_f32_e32 %[r2], %[dy], %[dy]\n"                                             \
+    "v_fmac_f32_e32 %[r2], %[dz], %[dz]\n"                                             \
+    "v_rsq_f32_e32 %[w], %[r2]\n"                                                      \
+    GUARD                                                                              \
+    "v_mul_f32_e32 %[f], " M ", %[w]\n"                                                \
+    "v_sub_f32_e32 %[pot], %[pot], %[f]\n"                                             \
+    "v_mul_f32_e32 %[f], %[w], %[f]\n"                                                 \
+    "v_mul_f32_e32 %[f], %[w], %[f]\n"                                                 \
+    "v_fmac_f32_e32 %[ax], %[f], %[dx]\n"                                              \
+    "v_fmac_f32_e32 %[ay], %[f], %[dy]\n"                                              \
+    "v_fmac_f32_e32 %[az], %[f], %[dz]\n"
+#define BH_GUARD_SOFT "s_nop 0\n"
+#define BH_GUARD_HARD                                                                  \
+    "v_cmp_lt_f32_e32 vcc, 0, %[r2]\n"                                                 \
+    "v_cndmask_b32_e32 %[w], 0, %[w], vcc\n"
+// source K (1-based) of the batch, skipped past the leaf's end
+#define BH_PAIR_K(K, X, Y, Z, M, G)                                                    \
+    "s_cmp_lt_u32 %[left], " #K "\n"                                                   \
+    "s_cbranch_scc1 BH_LD%=\n" BH_PAIR(X, Y, Z, M, G)
+
 // Visits from node X on, two per loop turn (slots A and B).  A node no lane
 // opens moves the wave to its skip; an opened internal node (meta without the
-// leaf bit) to X + 1.  The loop returns at the first opened leaf, which may be
-// the end record, with its index in X and its start, count and skip.  Every
-// step moves X forward, and the end record ends the loop at the latest.
-#define BH_RUN(CNT)                                                                    \
+// leaf bit) to X + 1; an opened leaf is summed by its openers, eight sources
+// per batch of two scalar loads into s[56:87] (the record slots are free
+// then; the next node index waits in %[skip]), and the wave moves on to its
+// skip.  The loop returns to the caller at the end record (count 0) and at a
+// leaf that may hold the wave's own targets ([first, first + count) meets
+// [wb, wbe)), whose self pairs the caller masks; X and the leaf's start,
+// count and skip are then the outputs.  Every step moves X forward, and the
+// end record ends the loop at the latest.
+#define BH_RUN(CNT, LEAF_CNT, G)                                                       \
     "s_mov_b32 s86, %[X]\n"                                                            \
     "BH_A%=:\n"                                                                        \
     BH_VISIT("s72", "s73", "s74", "s75", "s78", "s79", "s[72:79]", "s86", CNT,         \
@@ -149,25 +183,58 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
              "BH_NB%=")                                                                \
     "s_cbranch_scc0 BH_A%=\n"                                                          \
     "s_bitcmp1_b32 s87, 8\n"                                                           \
-    "s_cbranch_scc1 BH_XB%=\n"                                                         \
+    "s_cbranch_scc1 BH_LB%=\n"                                                         \
     "s_add_u32 s86, s78, 1\n"                                                          \
     "s_branch BH_A%=\n"                                                                \
     "BH_OA%=:\n"                                                                       \
     "s_bitcmp1_b32 s79, 8\n"                                                           \
-    "s_cbranch_scc1 BH_XA%=\n"                                                         \
+    "s_cbranch_scc1 BH_LA%=\n"                                                         \
     "s_add_u32 s78, s86, 1\n"                                                          \
     "s_branch BH_B%=\n"                                                                \
-    "BH_XB%=:\n"                                                                       \
+    "BH_LB%=:\n"                                                                       \
     "s_mov_b32 %[X], s78\n"                                                            \
     "s_mov_b32 %[first], s84\n"                                                        \
     "s_mov_b32 %[cnt], s85\n"                                                          \
     "s_mov_b32 %[skip], s86\n"                                                         \
-    "s_branch BH_E%=\n"                                                                \
-    "BH_XA%=:\n"                                                                       \
+    "s_branch BH_L%=\n"                                                                \
+    "BH_LA%=:\n"                                                                       \
     "s_mov_b32 %[X], s86\n"                                                            \
     "s_mov_b32 %[first], s76\n"                                                        \
     "s_mov_b32 %[cnt], s77\n"                                                          \
     "s_mov_b32 %[skip], s78\n"                                                         \
+    "BH_L%=:\n"                                                                        \
+    "s_cmp_eq_u32 %[cnt], 0\n"                                                         \
+    "s_cbranch_scc1 BH_E%=\n"                                                          \
+    "s_add_u32 %[le], %[first], %[cnt]\n"                                              \
+    "s_cmp_lt_u32 %[first], %[wbe]\n"                                                  \
+    "s_cbranch_scc0 BH_LN%=\n"                                                         \
+    "s_cmp_gt_u32 %[le], %[wb]\n"                                                      \
+    "s_cbranch_scc1 BH_E%=\n"                                                          \
+    "BH_LN%=:\n"                                                                       \
+    "s_and_saveexec_b64 %[save], %[open]\n"                                            \
+    "s_mov_b32 %[j], %[first]\n"                                                       \
+    "BH_LT%=:\n"                                                                       \
+    "s_lshl_b32 %[off], %[j], 4\n"                                                     \
+    "s_load_dwordx16 s[56:71], %[src], %[off]\n"                                       \
+    "s_load_dwordx16 s[72:87], %[src], %[off] offset:0x40\n"                           \
+    "s_sub_u32 %[left], %[le], %[j]\n"                                                 \
+    "s_waitcnt lgkmcnt(0)\n"                                                           \
+    BH_PAIR("s56", "s57", "s58", "s59", G)                                             \
+    BH_PAIR_K(2, "s60", "s61", "s62", "s63", G)                                        \
+    BH_PAIR_K(3, "s64", "s65", "s66", "s67", G)                                        \
+    BH_PAIR_K(4, "s68", "s69", "s70", "s71", G)                                        \
+    BH_PAIR_K(5, "s72", "s73", "s74", "s75", G)                                        \
+    BH_PAIR_K(6, "s76", "s77", "s78", "s79", G)                                        \
+    BH_PAIR_K(7, "s80", "s81", "s82", "s83", G)                                        \
+    BH_PAIR_K(8, "s84", "s85", "s86", "s87", G)                                        \
+    "s_add_u32 %[j], %[j], 8\n"                                                        \
+    "s_cmp_lt_u32 %[j], %[le]\n"                                                       \
+    "s_cbranch_scc1 BH_LT%=\n"                                                         \
+    "BH_LD%=:\n"                                                                       \
+    LEAF_CNT                                                                           \
+    "s_mov_b64 exec, %[save]\n"                                                        \
+    "s_mov_b32 s86, %[skip]\n"                                                         \
+    "s_branch BH_A%=\n"                                                                \
     "BH_E%=:\n"
 
 #define BH_RUN_OUTS                                                                    \
@@ -175,13 +242,16 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
         [rej] "+v"(rejoin), [first] "=&s"(first), [cnt] "=&s"(cnt), [skip] "=&s"(skip), \
         [dx] "=&v"(dx), [dy] "=&v"(dy), [dz] "=&v"(dz), [r2] "=&v"(r2), [w] "=&v"(w),    \
         [f] "=&v"(f), [off] "=&s"(off), [t] "=&s"(t), [far] "=&s"(far), [use] "=&s"(use), \
-        [save] "=&s"(save), [open] "=&s"(open)
+        [save] "=&s"(save), [open] "=&s"(open), [le] "=&s"(le), [j] "=&s"(jj),          \
+        [left] "=&s"(left)
 #define BH_RUN_INS                                                                     \
-    [nb] "s"(nb), [T0] "s"(T0_bits), [eps2] "v"(eps2v), [px] "v"(p.x), [py] "v"(p.y),  \
-        [pz] "v"(p.z)
+    [nb] "s"(nb), [src] "s"(sb), [T0] "s"(T0_bits), [eps2] "v"(eps2v), [px] "v"(p.x),  \
+        [py] "v"(p.y), [pz] "v"(p.z), [wb] "s"(wb), [wbe] "s"(wbe)
 #define BH_RUN_CLOBBERS                                                                \
-    "s72", "s73", "s74", "s75", "s76", "s77", "s78", "s79", "s80", "s81", "s82", "s83", \
-        "s84", "s85", "s86", "s87", "vcc", "scc", "memory"
+    "s56", "s57", "s58", "s59", "s60", "s61", "s62", "s63", "s64", "s65", "s66", "s67", \
+        "s68", "s69", "s70", "s71", "s72", "s73", "s74", "s75", "s76", "s77", "s78",    \
+        "s79", "s80", "s81", "s82", "s83", "s84", "s85", "s86", "s87", "vcc", "scc",    \
+        "memory"
 
 // Walk of one wave (see the file comment).  EXACT_T selects ldexp for the
 // level thresholds (w_l / theta)^2 = T0 * 4^-l; otherwise 4^-l is an exponent
@@ -195,8 +265,9 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
 // 7 of them with a scalar operand, 9 scalar instructions and 2 branches; the
 // compiled form of the same loop had 18 vector ops with 9 scalar operands, 13
 // scalar instructions and 3 branches, because the compiler re-derives the
-// lane masks and the loop exit on every node.  The two rarer thresholds keep
-// the compiled loop.
+// lane masks and the loop exit on every node, and it copied the accumulators
+// several times around every opened leaf.  The two rarer thresholds keep the
+// compiled loop.
 template <bool SOFT, bool SELF, bool COUNT, bool EXACT_T, bool ANY_MINE, bool FIXED_T = false>
 __device__ __attribute__((always_inline)) inline void walk_wave(
     const Node *__restrict__ nodes, const float4 *__restrict__ src, uint32_t nn, float4 p,
@@ -225,22 +296,45 @@ __device__ __attribute__((always_inline)) inline void walk_wave(
     };
     if constexpr (!EXACT_T && !FIXED_T) {
         const uint64_t nb = (uint64_t)node_bytes;
+        const uint64_t sb = (uint64_t)src;
+        // the loop sums a leaf unless it may hold this wave's own targets
+        // (self-gravity in key order: [wave_base, wave_base + 64)); with
+        // unsorted self-gravity every leaf may, with separate targets none
+        const uint32_t wb = SELF ? (ANY_MINE ? 0u : wave_base) : 0xffffffffu;
+        const uint32_t wbe = SELF ? (ANY_MINE ? 0xffffffffu : wave_base + 64) : 0u;
         float eps2v = eps2;
         asm volatile("" : "+v"(eps2v));   // held in a vector register
         for (;;) {
             X = sgpr(X);
-            uint32_t first, cnt, skip, off, t;
+            uint32_t first, cnt, skip, off, t, le, jj, left;
             float dx, dy, dz, r2, w, f;
             uint64_t far, use, save, open;
             if constexpr (COUNT) {
                 uint32_t ni = n_int;
-                asm volatile(BH_RUN("v_add_u32_e32 %[ni], 1, %[ni]\n")
-                             : BH_RUN_OUTS, [ni] "+v"(ni)
-                             : BH_RUN_INS
-                             : BH_RUN_CLOBBERS);
+                if constexpr (SOFT)
+                    asm volatile(BH_RUN("v_add_u32_e32 %[ni], 1, %[ni]\n",
+                                        "v_add_u32_e32 %[ni], %[cnt], %[ni]\n", BH_GUARD_SOFT)
+                                 : BH_RUN_OUTS, [ni] "+v"(ni)
+                                 : BH_RUN_INS
+                                 : BH_RUN_CLOBBERS);
+                else
+                    asm volatile(BH_RUN("v_add_u32_e32 %[ni], 1, %[ni]\n",
+                                        "v_add_u32_e32 %[ni], %[cnt], %[ni]\n", BH_GUARD_HARD)
+                                 : BH_RUN_OUTS, [ni] "+v"(ni)
+                                 : BH_RUN_INS
+                                 : BH_RUN_CLOBBERS);
                 n_int = ni;
             } else {
-                asm volatile(BH_RUN("") : BH_RUN_OUTS : BH_RUN_INS : BH_RUN_CLOBBERS);
+                if constexpr (SOFT)
+                    asm volatile(BH_RUN("", "", BH_GUARD_SOFT)
+                                 : BH_RUN_OUTS
+                                 : BH_RUN_INS
+                                 : BH_RUN_CLOBBERS);
+                else
+                    asm volatile(BH_RUN("", "", BH_GUARD_HARD)
+                                 : BH_RUN_OUTS
+                                 : BH_RUN_INS
+                                 : BH_RUN_CLOBBERS);
             }
             // the outputs are scalar registers; the compiler takes asm
             // outputs for per-lane values unless told
