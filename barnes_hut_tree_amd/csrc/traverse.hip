@@ -33,6 +33,9 @@ namespace bh {
 namespace {
 
 constexpr int kWalkThreads = 64;
+// node count up to which the assembly loop's 32-bit node byte offsets
+// (X * 32 for X <= the end record's index) cannot wrap
+constexpr uint32_t kAsmMaxNodes = (1u << 27) - 1;
 
 // One source of an opened leaf: the interaction of pair() (interaction.h),
 // with eps2 taken from a vector register and the potential term subtracted
@@ -166,7 +169,8 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
 // opens moves the wave to its skip; an opened internal node (meta without the
 // leaf bit) to X + 1; an opened leaf is summed by its openers, eight sources
 // per batch of two scalar loads into s[56:87] (the record slots are free
-// then; the next node index waits in %[skip]), and the wave moves on to its
+// then; the next node index waits in %[skip]; the batch address, in
+// s[88:89], is formed in 64 bits), and the wave moves on to its
 // skip.  The loop returns to the caller at the end record (count 0) and at a
 // leaf that may hold the wave's own targets ([first, first + count) meets
 // [wb, wbe)), whose self pairs the caller masks; X and the leaf's start,
@@ -214,9 +218,12 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     "s_and_saveexec_b64 %[save], %[open]\n"                                            \
     "s_mov_b32 %[j], %[first]\n"                                                       \
     "BH_LT%=:\n"                                                                       \
-    "s_lshl_b32 %[off], %[j], 4\n"                                                     \
-    "s_load_dwordx16 s[56:71], %[src], %[off]\n"                                       \
-    "s_load_dwordx16 s[72:87], %[src], %[off] offset:0x40\n"                           \
+    "s_lshl_b32 s88, %[j], 4\n"                                                        \
+    "s_lshr_b32 s89, %[j], 28\n"                                                       \
+    "s_add_u32 s88, s88, %[srclo]\n"                                                   \
+    "s_addc_u32 s89, s89, %[srchi]\n"                                                  \
+    "s_load_dwordx16 s[56:71], s[88:89], 0x0\n"                                        \
+    "s_load_dwordx16 s[72:87], s[88:89], 0x40\n"                                       \
     "s_sub_u32 %[left], %[le], %[j]\n"                                                 \
     "s_waitcnt lgkmcnt(0)\n"                                                           \
     BH_PAIR("s56", "s57", "s58", "s59", G)                                             \
@@ -245,13 +252,13 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
         [save] "=&s"(save), [open] "=&s"(open), [le] "=&s"(le), [j] "=&s"(jj),          \
         [left] "=&s"(left)
 #define BH_RUN_INS                                                                     \
-    [nb] "s"(nb), [src] "s"(sb), [T0] "s"(T0_bits), [eps2] "v"(eps2v), [px] "v"(p.x),  \
+    [nb] "s"(nb), [srclo] "s"(sb_lo), [srchi] "s"(sb_hi), [T0] "s"(T0_bits), [eps2] "v"(eps2v), [px] "v"(p.x),  \
         [py] "v"(p.y), [pz] "v"(p.z), [wb] "s"(wb), [wbe] "s"(wbe)
 #define BH_RUN_CLOBBERS                                                                \
     "s56", "s57", "s58", "s59", "s60", "s61", "s62", "s63", "s64", "s65", "s66", "s67", \
         "s68", "s69", "s70", "s71", "s72", "s73", "s74", "s75", "s76", "s77", "s78",    \
-        "s79", "s80", "s81", "s82", "s83", "s84", "s85", "s86", "s87", "vcc", "scc",    \
-        "memory"
+        "s79", "s80", "s81", "s82", "s83", "s84", "s85", "s86", "s87", "s88", "s89",    \
+        "vcc", "scc", "memory"
 
 // Walk of one wave (see the file comment).  EXACT_T selects ldexp for the
 // level thresholds (w_l / theta)^2 = T0 * 4^-l; otherwise 4^-l is an exponent
@@ -296,7 +303,8 @@ __device__ __attribute__((always_inline)) inline void walk_wave(
     };
     if constexpr (!EXACT_T && !FIXED_T) {
         const uint64_t nb = (uint64_t)node_bytes;
-        const uint64_t sb = (uint64_t)src;
+        const uint32_t sb_lo = sgpr((uint32_t)(uint64_t)src);
+        const uint32_t sb_hi = sgpr((uint32_t)((uint64_t)src >> 32));
         // the loop sums a leaf unless it may hold this wave's own targets
         // (self-gravity in key order: [wave_base, wave_base + 64)); with
         // unsorted self-gravity every leaf may, with separate targets none
@@ -349,7 +357,7 @@ __device__ __attribute__((always_inline)) inline void walk_wave(
         return;
     }
     while (X < nn) {
-        const uint4 *rec = reinterpret_cast<const uint4 *>(node_bytes + X * (uint32_t)sizeof(Node));
+        const uint4 *rec = reinterpret_cast<const uint4 *>(node_bytes + (size_t)X * sizeof(Node));
         const uint4 lo = rec[0], hi = rec[1];
         uint32_t mbits = lo.w;
         asm volatile("" : "+s"(mbits));   // keep the mass in a register, not reloaded
@@ -401,7 +409,7 @@ __device__ __attribute__((always_inline)) inline void walk_vote(
     const char *node_bytes = reinterpret_cast<const char *>(nodes);
     uint32_t X = 0;
     while (X < nn) {
-        const uint4 *rec = reinterpret_cast<const uint4 *>(node_bytes + X * (uint32_t)sizeof(Node));
+        const uint4 *rec = reinterpret_cast<const uint4 *>(node_bytes + (size_t)X * sizeof(Node));
         const uint4 lo = rec[0], hi = rec[1];
         const float cx = __uint_as_float(lo.x), cy = __uint_as_float(lo.y);
         const float cz = __uint_as_float(lo.z), m = __uint_as_float(lo.w);
@@ -478,10 +486,12 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
     const uint32_t T0_bits = sgpr(__float_as_uint(T0));
     const uint32_t T0_exp = (T0_bits >> 23) & 0xffu;
     // zero, inf and NaN thresholds are the same at every level (step 0); a
-    // normal T0 with T0 * 4^-21 normal steps the exponent by 2 per level;
-    // anything else takes ldexp
+    // normal T0 with T0 * 4^-21 normal steps the exponent by 2 per level (the
+    // assembly loop); anything else takes ldexp (the compiled loop), and so
+    // does a tree whose byte offsets (32 B per node, the end record included)
+    // would not fit the assembly loop's 32-bit offsets
     const bool fixed = (T0_bits & 0x7fffffffu) == 0u || T0_exp == 255u;
-    const bool exact = !fixed && T0_exp <= 44u;
+    const bool exact = !fixed && (T0_exp <= 44u || nn >= kAsmMaxNodes);
     const uint32_t T_step = fixed ? 0u : (1u << 24);
 
     // wait for the target's position here: a first use inside the walk loop
