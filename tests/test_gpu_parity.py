@@ -339,6 +339,35 @@ def test_all_coincident(orc):
         t.close()
 
 
+def test_end_record_after_the_last_node(orc):
+    """Every build writes an end record right after its last node (NaN centre,
+    zero mass, an empty leaf starting at n, leaf bit set, level 0): every lane
+    still walking opens it, which ends the walk's loop.  A second, smaller build
+    in the same context writes its own at the lower index, and the walk then
+    matches the oracle on that tree."""
+    import ctypes
+    import barnes_hut_tree_amd as bh
+    t = bh.BarnesHut(5000, 0, 63, 16)
+    for n in (5000, 300):
+        p = W.uniform_cube(n, seed=7)
+        t.build(torch.from_numpy(p).cuda())
+        nn = t.node_count()
+        buf = torch.empty((nn + 1, 8), dtype=torch.int32, device="cuda")
+        st = bh.load_library().bh_get_nodes(t._h, ctypes.c_void_p(buf.data_ptr()), nn + 1,
+                                            bh._stream())
+        assert st == 0
+        f = bh.nodes_numpy(buf)
+        assert np.all(np.isnan(f["com"][nn])) and f["mass"][nn] == 0.0
+        assert f["start"][nn] == n and f["count"][nn] == 0 and f["skip"][nn] == nn + 1
+        assert f["is_leaf"][nn] == 1 and f["level"][nn] == 0
+        assert np.all(np.isfinite(f["com"][:nn]))
+        got = t.gravity(0.5, 1.0, 1e-3).cpu().numpy()
+        ref = orc.Tree(p, leaf_cap=16)
+        modes = [ref.gravity(0.5, 1.0, 1e-3, tie_mode=m) for m in (0, 1, 2)]
+        assert_walk_parity(got, [m[0] for m in modes], modes[0][2], "end record n=%d" % n)
+    t.close()
+
+
 def test_nonfinite_input_is_reported():
     import barnes_hut_tree_amd as bh
     p = W.uniform_cube(1000, seed=2)
