@@ -89,9 +89,14 @@ __device__ __attribute__((always_inline)) inline void leaf_tile(
 __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // The assembly loop of the walk.  Register use: the node records of two
-// consecutive visits land in s[72:79] and s[80:87] (x, y, z, m, start, count,
+// consecutive visits land in s[32:39] and s[40:47] (x, y, z, m, start, count,
 // skip, meta), so the next visit's node index is the previous record's skip
-// field where it lies.  One visit of node XR (record slot R0..R7, loaded
+// field where it lies; a leaf's sources are loaded into s[16:47] and their
+// address formed in s[48:49].  These fixed registers sit low: a kernel's
+// scalar register count is its highest register used, and the walk keeps
+// eight waves per SIMD only up to about 76 (measured: 70 registers gave 8
+// resident waves, 90 gave 7, 96 gave 6, and the walk ran 7% faster at 68 than
+// at 90 with the same code).  One visit of node XR (record slot R0..R7, loaded
 // through RT):
 //   act  = rejoin <= X                         (vcc)
 //   T    = T0 * 4^-level, the exponent of T0 stepped down by 2 * level
@@ -168,44 +173,44 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
 // Visits from node X on, two per loop turn (slots A and B).  A node no lane
 // opens moves the wave to its skip; an opened internal node (meta without the
 // leaf bit) to X + 1; an opened leaf is summed by its openers, eight sources
-// per batch of two scalar loads into s[56:87] (the record slots are free
+// per batch of two scalar loads into s[16:47] (the record slots are free
 // then; the next node index waits in %[skip]; the batch address, in
-// s[88:89], is formed in 64 bits), and the wave moves on to its
+// s[48:49], is formed in 64 bits), and the wave moves on to its
 // skip.  The loop returns to the caller at the end record (count 0) and at a
 // leaf that may hold the wave's own targets ([first, first + count) meets
 // [wb, wbe)), whose self pairs the caller masks; X and the leaf's start,
 // count and skip are then the outputs.  Every step moves X forward, and the
 // end record ends the loop at the latest.
 #define BH_RUN(CNT, LEAF_CNT, G)                                                       \
-    "s_mov_b32 s86, %[X]\n"                                                            \
+    "s_mov_b32 s46, %[X]\n"                                                            \
     "BH_A%=:\n"                                                                        \
-    BH_VISIT("s72", "s73", "s74", "s75", "s78", "s79", "s[72:79]", "s86", CNT,         \
+    BH_VISIT("s32", "s33", "s34", "s35", "s38", "s39", "s[32:39]", "s46", CNT,         \
              "BH_NA%=")                                                                \
     "s_cbranch_scc1 BH_OA%=\n"                                                         \
     "BH_B%=:\n"                                                                        \
-    BH_VISIT("s80", "s81", "s82", "s83", "s86", "s87", "s[80:87]", "s78", CNT,         \
+    BH_VISIT("s40", "s41", "s42", "s43", "s46", "s47", "s[40:47]", "s38", CNT,         \
              "BH_NB%=")                                                                \
     "s_cbranch_scc0 BH_A%=\n"                                                          \
-    "s_bitcmp1_b32 s87, 8\n"                                                           \
+    "s_bitcmp1_b32 s47, 8\n"                                                           \
     "s_cbranch_scc1 BH_LB%=\n"                                                         \
-    "s_add_u32 s86, s78, 1\n"                                                          \
+    "s_add_u32 s46, s38, 1\n"                                                          \
     "s_branch BH_A%=\n"                                                                \
     "BH_OA%=:\n"                                                                       \
-    "s_bitcmp1_b32 s79, 8\n"                                                           \
+    "s_bitcmp1_b32 s39, 8\n"                                                           \
     "s_cbranch_scc1 BH_LA%=\n"                                                         \
-    "s_add_u32 s78, s86, 1\n"                                                          \
+    "s_add_u32 s38, s46, 1\n"                                                          \
     "s_branch BH_B%=\n"                                                                \
     "BH_LB%=:\n"                                                                       \
-    "s_mov_b32 %[X], s78\n"                                                            \
-    "s_mov_b32 %[first], s84\n"                                                        \
-    "s_mov_b32 %[cnt], s85\n"                                                          \
-    "s_mov_b32 %[skip], s86\n"                                                         \
+    "s_mov_b32 %[X], s38\n"                                                            \
+    "s_mov_b32 %[first], s44\n"                                                        \
+    "s_mov_b32 %[cnt], s45\n"                                                          \
+    "s_mov_b32 %[skip], s46\n"                                                         \
     "s_branch BH_L%=\n"                                                                \
     "BH_LA%=:\n"                                                                       \
-    "s_mov_b32 %[X], s86\n"                                                            \
-    "s_mov_b32 %[first], s76\n"                                                        \
-    "s_mov_b32 %[cnt], s77\n"                                                          \
-    "s_mov_b32 %[skip], s78\n"                                                         \
+    "s_mov_b32 %[X], s46\n"                                                            \
+    "s_mov_b32 %[first], s36\n"                                                        \
+    "s_mov_b32 %[cnt], s37\n"                                                          \
+    "s_mov_b32 %[skip], s38\n"                                                         \
     "BH_L%=:\n"                                                                        \
     "s_cmp_eq_u32 %[cnt], 0\n"                                                         \
     "s_cbranch_scc1 BH_E%=\n"                                                          \
@@ -218,29 +223,29 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     "s_and_saveexec_b64 %[save], %[open]\n"                                            \
     "s_mov_b32 %[j], %[first]\n"                                                       \
     "BH_LT%=:\n"                                                                       \
-    "s_lshl_b32 s88, %[j], 4\n"                                                        \
-    "s_lshr_b32 s89, %[j], 28\n"                                                       \
-    "s_add_u32 s88, s88, %[srclo]\n"                                                   \
-    "s_addc_u32 s89, s89, %[srchi]\n"                                                  \
-    "s_load_dwordx16 s[56:71], s[88:89], 0x0\n"                                        \
-    "s_load_dwordx16 s[72:87], s[88:89], 0x40\n"                                       \
+    "s_lshl_b32 s48, %[j], 4\n"                                                        \
+    "s_lshr_b32 s49, %[j], 28\n"                                                       \
+    "s_add_u32 s48, s48, %[srclo]\n"                                                   \
+    "s_addc_u32 s49, s49, %[srchi]\n"                                                  \
+    "s_load_dwordx16 s[16:31], s[48:49], 0x0\n"                                        \
+    "s_load_dwordx16 s[32:47], s[48:49], 0x40\n"                                       \
     "s_sub_u32 %[left], %[le], %[j]\n"                                                 \
     "s_waitcnt lgkmcnt(0)\n"                                                           \
-    BH_PAIR("s56", "s57", "s58", "s59", G)                                             \
-    BH_PAIR_K(2, "s60", "s61", "s62", "s63", G)                                        \
-    BH_PAIR_K(3, "s64", "s65", "s66", "s67", G)                                        \
-    BH_PAIR_K(4, "s68", "s69", "s70", "s71", G)                                        \
-    BH_PAIR_K(5, "s72", "s73", "s74", "s75", G)                                        \
-    BH_PAIR_K(6, "s76", "s77", "s78", "s79", G)                                        \
-    BH_PAIR_K(7, "s80", "s81", "s82", "s83", G)                                        \
-    BH_PAIR_K(8, "s84", "s85", "s86", "s87", G)                                        \
+    BH_PAIR("s16", "s17", "s18", "s19", G)                                             \
+    BH_PAIR_K(2, "s20", "s21", "s22", "s23", G)                                        \
+    BH_PAIR_K(3, "s24", "s25", "s26", "s27", G)                                        \
+    BH_PAIR_K(4, "s28", "s29", "s30", "s31", G)                                        \
+    BH_PAIR_K(5, "s32", "s33", "s34", "s35", G)                                        \
+    BH_PAIR_K(6, "s36", "s37", "s38", "s39", G)                                        \
+    BH_PAIR_K(7, "s40", "s41", "s42", "s43", G)                                        \
+    BH_PAIR_K(8, "s44", "s45", "s46", "s47", G)                                        \
     "s_add_u32 %[j], %[j], 8\n"                                                        \
     "s_cmp_lt_u32 %[j], %[le]\n"                                                       \
     "s_cbranch_scc1 BH_LT%=\n"                                                         \
     "BH_LD%=:\n"                                                                       \
     LEAF_CNT                                                                           \
     "s_mov_b64 exec, %[save]\n"                                                        \
-    "s_mov_b32 s86, %[skip]\n"                                                         \
+    "s_mov_b32 s46, %[skip]\n"                                                         \
     "s_branch BH_A%=\n"                                                                \
     "BH_E%=:\n"
 
@@ -255,9 +260,9 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     [nb] "s"(nb), [srclo] "s"(sb_lo), [srchi] "s"(sb_hi), [T0] "s"(T0_bits), [eps2] "v"(eps2v), [px] "v"(p.x),  \
         [py] "v"(p.y), [pz] "v"(p.z), [wb] "s"(wb), [wbe] "s"(wbe)
 #define BH_RUN_CLOBBERS                                                                \
-    "s56", "s57", "s58", "s59", "s60", "s61", "s62", "s63", "s64", "s65", "s66", "s67", \
-        "s68", "s69", "s70", "s71", "s72", "s73", "s74", "s75", "s76", "s77", "s78",    \
-        "s79", "s80", "s81", "s82", "s83", "s84", "s85", "s86", "s87", "s88", "s89",    \
+    "s16", "s17", "s18", "s19", "s20", "s21", "s22", "s23", "s24", "s25", "s26", "s27", \
+        "s28", "s29", "s30", "s31", "s32", "s33", "s34", "s35", "s36", "s37", "s38",    \
+        "s39", "s40", "s41", "s42", "s43", "s44", "s45", "s46", "s47", "s48", "s49",    \
         "vcc", "scc", "memory"
 
 // Walk of one wave (see the file comment).  EXACT_T selects ldexp for the
