@@ -494,12 +494,16 @@ def main():
     tree.sync()
     interactions = tree.count_interactions(prm["theta"], prm["eps"])
 
-    # per-phase device times, from one profiled step outside the timed region
+    # per-phase device times: the median of five profiled steps outside the
+    # timed region
     tree.set_profiling(True)
-    step()
-    phases = tree.profile()
+    runs = []
+    for _ in range(5):
+        step()
+        runs.append(tree.profile())
     tree.set_profiling(False)
     tree.sync()
+    phases = [sorted(r[k] for r in runs)[len(runs) // 2] for k in range(len(runs[0]))]
 
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
