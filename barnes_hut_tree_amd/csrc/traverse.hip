@@ -98,11 +98,11 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
 // resident waves, 90 gave 7, 96 gave 6, and the walk ran 7% faster at 68 than
 // at 90 with the same code).  One visit of node XR (record slot R0..R7, loaded
 // through RT):
-//   act  = rejoin <= X                         (vcc)
+//   act  = rejoin <= X                         (vcc, then exec)
 //   T    = T0 * 4^-level, the exponent of T0 stepped down by 2 * level
-//   far  = T < r^2                              (per lane)
+//   far  = T < r^2, by a compare that also narrows exec to act & far
 //   lanes in act & far add the monopole and set rejoin = skip
-//   open = act & ~far                           (SCC: some lane opens X)
+//   open = act & ~exec                          (SCC: some lane opens X)
 // The monopole is inv = rsq(r^2 + eps^2), f = m inv^3, a += f d, pot -= m inv,
 // with eps^2 in a vector register and the potential term unfused, so that all
 // but the node-field operands are register-only.  One independent instruction
@@ -122,9 +122,8 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     "v_fmac_f32_e32 %[r2], %[dy], %[dy]\n"                                             \
     "s_sub_u32 %[t], %[T0], %[t]\n"                                                    \
     "v_fmac_f32_e32 %[r2], %[dz], %[dz]\n"                                             \
-    "v_cmp_lt_f32_e64 %[far], %[t], %[r2]\n"                                           \
-    "s_and_b64 %[use], vcc, %[far]\n"                                                  \
-    "s_and_saveexec_b64 %[save], %[use]\n"                                             \
+    "s_and_saveexec_b64 %[save], vcc\n"                                                \
+    "v_cmpx_lt_f32_e64 %[far], %[t], %[r2]\n"                                          \
     "s_cbranch_execz " SKIP_LABEL "\n"                                                 \
     "v_add_f32_e32 %[w], %[eps2], %[r2]\n"                                             \
     "v_rsq_f32_e32 %[w], %[w]\n"                                                       \
@@ -138,8 +137,8 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     "v_fmac_f32_e32 %[az], %[f], %[dz]\n"                                              \
     CNT                                                                                \
     SKIP_LABEL ":\n"                                                                   \
-    "s_mov_b64 exec, %[save]\n"                                                        \
-    "s_andn2_b64 %[open], vcc, %[far]\n"
+    "s_andn2_b64 %[open], vcc, exec\n"                                                 \
+    "s_mov_b64 exec, %[save]\n"
 
 // One source of a leaf opened in the assembly loop, in the order of
 // leaf_pair(): X, Y, Z, M name the source's scalar registers.  GUARD is the
@@ -253,7 +252,7 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     [X] "+s"(X), [ax] "+v"(ax), [ay] "+v"(ay), [az] "+v"(az), [pot] "+v"(pot),        \
         [rej] "+v"(rejoin), [first] "=&s"(first), [cnt] "=&s"(cnt), [skip] "=&s"(skip), \
         [dx] "=&v"(dx), [dy] "=&v"(dy), [dz] "=&v"(dz), [r2] "=&v"(r2), [w] "=&v"(w),    \
-        [f] "=&v"(f), [off] "=&s"(off), [t] "=&s"(t), [far] "=&s"(far), [use] "=&s"(use), \
+        [f] "=&v"(f), [off] "=&s"(off), [t] "=&s"(t), [far] "=&s"(far),                   \
         [save] "=&s"(save), [open] "=&s"(open), [le] "=&s"(le), [j] "=&s"(jj),          \
         [left] "=&s"(left)
 #define BH_RUN_INS                                                                     \
@@ -274,7 +273,7 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
 // instructions share its issue slots, and a vector op with a scalar-register
 // operand issues at about two thirds the rate of one with register operands
 // only.  The assembly loop (above) keeps the per-node path to 18 vector ops,
-// 7 of them with a scalar operand, 9 scalar instructions and 2 branches; the
+// 7 of them with a scalar operand, 8 scalar instructions and 2 branches; the
 // compiled form of the same loop had 18 vector ops with 9 scalar operands, 13
 // scalar instructions and 3 branches, because the compiler re-derives the
 // lane masks and the loop exit on every node, and it copied the accumulators
@@ -321,7 +320,7 @@ __device__ __attribute__((always_inline)) inline void walk_wave(
             X = sgpr(X);
             uint32_t first, cnt, skip, off, t, le, jj, left;
             float dx, dy, dz, r2, w, f;
-            uint64_t far, use, save, open;
+            uint64_t far, save, open;
             if constexpr (COUNT) {
                 uint32_t ni = n_int;
                 if constexpr (SOFT)
