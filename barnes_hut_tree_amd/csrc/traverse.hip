@@ -144,7 +144,7 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
 // leaf_pair(): X, Y, Z, M name the source's scalar registers.  GUARD is the
 // r^2 > 0 test of the unsoftened interaction (with softening, a nop keeps
 // the reciprocal square root one instruction from its first use).
-#define BH_PAIR(X, Y, Z, M, GUARD)                                                     \
+#define BH_PAIR(X, Y, Z, M, GUARD, NEXT)                                               \
     "v_sub_f32_e32 %[dx], " X ", %[px]\n"                                              \
     "v_sub_f32_e32 %[dy], " Y ", %[py]\n"                                              \
     "v_fma_f32 %[r2], %[dx], %[dx], %[eps2]\n"                                         \
@@ -152,7 +152,7 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     "v_fmac_f32_e32 %[r2], %[dy], %[dy]\n"                                             \
     "v_fmac_f32_e32 %[r2], %[dz], %[dz]\n"                                             \
     "v_rsq_f32_e32 %[w], %[r2]\n"                                                      \
-    GUARD                                                                              \
+    GUARD(NEXT)                                                                        \
     "v_mul_f32_e32 %[f], " M ", %[w]\n"                                                \
     "v_sub_f32_e32 %[pot], %[pot], %[f]\n"                                             \
     "v_mul_f32_e32 %[f], %[w], %[f]\n"                                                 \
@@ -160,14 +160,17 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     "v_fmac_f32_e32 %[ax], %[f], %[dx]\n"                                              \
     "v_fmac_f32_e32 %[ay], %[f], %[dy]\n"                                              \
     "v_fmac_f32_e32 %[az], %[f], %[dz]\n"
-#define BH_GUARD_SOFT "s_nop 0\n"
-#define BH_GUARD_HARD                                                                  \
+#define BH_GUARD_SOFT(NEXT) NEXT
+#define BH_GUARD_HARD(NEXT)                                                            \
+    NEXT                                                                               \
     "v_cmp_lt_f32_e32 vcc, 0, %[r2]\n"                                                 \
     "v_cndmask_b32_e32 %[w], 0, %[w], vcc\n"
-// source K (1-based) of the batch, skipped past the leaf's end
-#define BH_PAIR_K(K, X, Y, Z, M, G)                                                    \
-    "s_cmp_lt_u32 %[left], " #K "\n"                                                   \
-    "s_cbranch_scc1 BH_LD%=\n" BH_PAIR(X, Y, Z, M, G)
+// NEXT, the instruction that fills the slot after the reciprocal square root,
+// is the bounds compare of the batch's next source (a scalar instruction;
+// the vector ops between it and its branch leave SCC alone), or a nop after
+// the last source
+#define BH_NEXT(K) "s_cmp_lt_u32 %[left], " #K "\n"
+#define BH_LAST "s_nop 0\n"
 
 // Visits from node X on, two per loop turn (slots A and B).  A node no lane
 // opens moves the wave to its skip; an opened internal node (meta without the
@@ -230,14 +233,14 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     "s_load_dwordx16 s[32:47], s[48:49], 0x40\n"                                       \
     "s_sub_u32 %[left], %[le], %[j]\n"                                                 \
     "s_waitcnt lgkmcnt(0)\n"                                                           \
-    BH_PAIR("s16", "s17", "s18", "s19", G)                                             \
-    BH_PAIR_K(2, "s20", "s21", "s22", "s23", G)                                        \
-    BH_PAIR_K(3, "s24", "s25", "s26", "s27", G)                                        \
-    BH_PAIR_K(4, "s28", "s29", "s30", "s31", G)                                        \
-    BH_PAIR_K(5, "s32", "s33", "s34", "s35", G)                                        \
-    BH_PAIR_K(6, "s36", "s37", "s38", "s39", G)                                        \
-    BH_PAIR_K(7, "s40", "s41", "s42", "s43", G)                                        \
-    BH_PAIR_K(8, "s44", "s45", "s46", "s47", G)                                        \
+    BH_PAIR("s16", "s17", "s18", "s19", G, BH_NEXT(2)) "s_cbranch_scc1 BH_LD%=\n"      \
+    BH_PAIR("s20", "s21", "s22", "s23", G, BH_NEXT(3)) "s_cbranch_scc1 BH_LD%=\n"      \
+    BH_PAIR("s24", "s25", "s26", "s27", G, BH_NEXT(4)) "s_cbranch_scc1 BH_LD%=\n"      \
+    BH_PAIR("s28", "s29", "s30", "s31", G, BH_NEXT(5)) "s_cbranch_scc1 BH_LD%=\n"      \
+    BH_PAIR("s32", "s33", "s34", "s35", G, BH_NEXT(6)) "s_cbranch_scc1 BH_LD%=\n"      \
+    BH_PAIR("s36", "s37", "s38", "s39", G, BH_NEXT(7)) "s_cbranch_scc1 BH_LD%=\n"      \
+    BH_PAIR("s40", "s41", "s42", "s43", G, BH_NEXT(8)) "s_cbranch_scc1 BH_LD%=\n"      \
+    BH_PAIR("s44", "s45", "s46", "s47", G, BH_LAST)                                    \
     "s_add_u32 %[j], %[j], 8\n"                                                        \
     "s_cmp_lt_u32 %[j], %[le]\n"                                                       \
     "s_cbranch_scc1 BH_LT%=\n"                                                         \
