@@ -101,14 +101,15 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
 //   act  = rejoin <= X                         (vcc, then exec)
 //   T    = T0 * 4^-level, the exponent of T0 stepped down by 2 * level
 //   far  = T < r^2, by a compare that also narrows exec to act & far
-//   lanes in act & far add the monopole and set rejoin = skip
+//   lanes in act & far add the monopole (their rejoin moves to the node's
+//   skip only where the wave descends into the node or returns, below)
 //   open = act & ~exec                          (SCC: some lane opens X)
 // The monopole is inv = rsq(r^2 + eps^2), f = m inv^3, a += f d, pot -= m inv,
 // with eps^2 in a vector register and the potential term unfused, so that all
-// but the node-field operands are register-only.  One independent instruction
-// (the rejoin move) sits between the reciprocal square root and the first use
-// of its result, which the hardware requires.  A wave in which no lane
-// accepts skips the monopole.  CNT: the interaction count update, if any.
+// but the node-field operands are register-only.  One instruction (the branch
+// past the monopole, taken when no lane accepts) sits between the reciprocal
+// square root and the first use of its result, which the hardware requires.
+// CNT: the interaction count update, if any.
 #define BH_VISIT(R0, R1, R2, R3, R6, R7, RT, XR, CNT, SKIP_LABEL)                       \
     "s_lshl_b32 %[off], " XR ", 5\n"                                                   \
     "s_load_dwordx8 " RT ", %[nb], %[off]\n"                                           \
@@ -124,10 +125,9 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     "v_fmac_f32_e32 %[r2], %[dz], %[dz]\n"                                             \
     "s_and_saveexec_b64 %[save], vcc\n"                                                \
     "v_cmpx_lt_f32_e64 %[far], %[t], %[r2]\n"                                          \
-    "s_cbranch_execz " SKIP_LABEL "\n"                                                 \
     "v_add_f32_e32 %[w], %[eps2], %[r2]\n"                                             \
     "v_rsq_f32_e32 %[w], %[w]\n"                                                       \
-    "v_mov_b32_e32 %[rej], " R6 "\n"                                                   \
+    "s_cbranch_execz " SKIP_LABEL "\n"                                                 \
     "v_mul_f32_e32 %[f], " R3 ", %[w]\n"                                               \
     "v_sub_f32_e32 %[pot], %[pot], %[f]\n"                                             \
     "v_mul_f32_e32 %[f], %[w], %[f]\n"                                                 \
@@ -183,6 +183,15 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
 // [wb, wbe)), whose self pairs the caller masks; X and the leaf's start,
 // count and skip are then the outputs.  Every step moves X forward, and the
 // end record ends the loop at the latest.
+// The lanes that used the node just visited (act & ~open, with act still in
+// vcc) sit out its subtree: rejoin = its skip.  Needed only when the wave
+// descends into that subtree or returns to the caller; when it moves to the
+// skip itself, or past an opened leaf (skip = X + 1), they are active there.
+#define BH_SIT_OUT(SKIP)                                                               \
+    "s_andn2_b64 exec, vcc, %[open]\n"                                                 \
+    "v_mov_b32_e32 %[rej], " SKIP "\n"                                                 \
+    "s_mov_b64 exec, %[save]\n"
+
 #define BH_RUN(CNT, LEAF_CNT, G)                                                       \
     "s_mov_b32 s46, %[X]\n"                                                            \
     "BH_A%=:\n"                                                                        \
@@ -195,11 +204,13 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     "s_cbranch_scc0 BH_A%=\n"                                                          \
     "s_bitcmp1_b32 s47, 8\n"                                                           \
     "s_cbranch_scc1 BH_LB%=\n"                                                         \
+    BH_SIT_OUT("s46")                                                                  \
     "s_add_u32 s46, s38, 1\n"                                                          \
     "s_branch BH_A%=\n"                                                                \
     "BH_OA%=:\n"                                                                       \
     "s_bitcmp1_b32 s39, 8\n"                                                           \
     "s_cbranch_scc1 BH_LA%=\n"                                                         \
+    BH_SIT_OUT("s38")                                                                  \
     "s_add_u32 s38, s46, 1\n"                                                          \
     "s_branch BH_B%=\n"                                                                \
     "BH_LB%=:\n"                                                                       \
@@ -249,7 +260,7 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     "s_mov_b64 exec, %[save]\n"                                                        \
     "s_mov_b32 s46, %[skip]\n"                                                         \
     "s_branch BH_A%=\n"                                                                \
-    "BH_E%=:\n"
+    "BH_E%=:\n" BH_SIT_OUT("%[skip]")
 
 #define BH_RUN_OUTS                                                                    \
     [X] "+s"(X), [ax] "+v"(ax), [ay] "+v"(ay), [az] "+v"(az), [pot] "+v"(pot),        \
@@ -275,8 +286,8 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
 // The walk is bound by instruction issue.  A wave's vector and scalar
 // instructions share its issue slots, and a vector op with a scalar-register
 // operand issues at about two thirds the rate of one with register operands
-// only.  The assembly loop (above) keeps the per-node path to 18 vector ops,
-// 7 of them with a scalar operand, 8 scalar instructions and 2 branches; the
+// only.  The assembly loop (above) keeps the per-node path to 17 vector ops,
+// 6 of them with a scalar operand, 8 scalar instructions and 2 branches; the
 // compiled form of the same loop had 18 vector ops with 9 scalar operands, 13
 // scalar instructions and 3 branches, because the compiler re-derives the
 // lane masks and the loop exit on every node, and it copied the accumulators
