@@ -31,7 +31,8 @@ EXPORTS = ("bh_create", "bh_build", "bh_gravity", "bh_gravity_counted", "bh_grav
            "bh_get_locked_tree", "bh_direct", "bh_kick_drift",
            "bh_leapfrog_step", "bh_diagnostics", "bh_sync", "bh_destroy",
            "bh_status_string", "bh_get_keys", "bh_get_node_count", "bh_get_nodes", "bh_get_bbox",
-           "bh_set_profiling", "bh_get_profile", "bh_node_hmax")
+           "bh_set_profiling", "bh_get_profile", "bh_node_hmax", "bh_get_cells",
+           "bh_set_counting", "bh_get_interactions")
 
 NODE_DTYPE_FIELDS = [("com_x", "f4"), ("com_y", "f4"), ("com_z", "f4"), ("mass", "f4"),
                      ("start", "u4"), ("count", "u4"), ("skip", "u4"), ("meta", "u4")]
@@ -87,6 +88,9 @@ def load_library():
         "bh_set_profiling": [P, i32],
         "bh_get_profile": [P, P, i32],
         "bh_node_hmax": [P, P, i64, P, i64, P],
+        "bh_get_cells": [P, ctypes.POINTER(i64), P, P, P, P],
+        "bh_set_counting": [P, i32],
+        "bh_get_interactions": [P, ctypes.POINTER(ctypes.c_uint64)],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -118,6 +122,19 @@ def _rows(t, name):
         raise TypeError("%s must be a float32 CUDA tensor" % name)
     if t.dim() != 2 or t.shape[1] != 4 or not t.is_contiguous():
         raise ValueError("%s must be a contiguous (n, 4) tensor" % name)
+    return t
+
+
+def _counter(t):
+    """An interaction counter must be one int64 element of device memory on
+    the current device (the walk adds to it with a device atomic)."""
+    import torch
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != torch.int64:
+        raise TypeError("interactions must be an int64 CUDA tensor")
+    if t.numel() != 1 or not t.is_contiguous():
+        raise ValueError("interactions must be a contiguous 1-element tensor")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError("interactions must be on the current device")
     return t
 
 
@@ -174,6 +191,13 @@ class BarnesHut:
             out = torch.empty((nt, 4), dtype=torch.float32, device="cuda")
         else:
             _rows(out, "out")
+            if out.shape[0] != nt:
+                raise ValueError("out must have %d rows" % nt)
+        if interactions is not None:
+            _counter(interactions)
+        if targets is not None and nt == 0:
+            # an empty tensor's data pointer is NULL, which would mean "self"
+            return out
         L = load_library()
         if flags:
             cp = ctypes.c_void_p() if interactions is None else ctypes.c_void_p(
@@ -238,6 +262,37 @@ class BarnesHut:
         cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
         self.gravity(theta, 1.0, eps, targets=targets, interactions=cnt, flags=flags)
         return int(cnt.item())
+
+    def set_counting(self, on=True):
+        """Count interactions of every following gravity() call that has no
+        counter of its own (bh_set_counting); read with interactions()."""
+        _check(load_library().bh_set_counting(self._h, int(bool(on))), "bh_set_counting")
+
+    def interactions(self):
+        """Interactions of the last counted gravity() call (bh_get_interactions)."""
+        v = ctypes.c_uint64()
+        _check(load_library().bh_get_interactions(self._h, ctypes.byref(v)),
+               "bh_get_interactions")
+        return v.value
+
+    def cells(self):
+        """Per node in pre-order (bh_get_cells): level (uint8), key prefix of
+        the cell's place on its level's grid (int64 view of uint64) and source
+        count (int32 view of uint32), as CUDA tensors."""
+        import torch
+        L = load_library()
+        nn = ctypes.c_int64()
+        _check(L.bh_get_cells(self._h, ctypes.byref(nn), None, None, None, _stream()),
+               "bh_get_cells")
+        k = max(nn.value, 1)
+        level = torch.empty(k, dtype=torch.uint8, device="cuda")
+        prefix = torch.empty(k, dtype=torch.int64, device="cuda")
+        count = torch.empty(k, dtype=torch.int32, device="cuda")
+        _check(L.bh_get_cells(self._h, ctypes.byref(nn), ctypes.c_void_p(level.data_ptr()),
+                              ctypes.c_void_p(prefix.data_ptr()),
+                              ctypes.c_void_p(count.data_ptr()), _stream()), "bh_get_cells")
+        m = nn.value
+        return dict(level=level[:m], prefix=prefix[:m], count=count[:m])
 
     def sync(self):
         _check(load_library().bh_sync(self._h), "bh_sync")

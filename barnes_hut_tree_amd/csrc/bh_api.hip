@@ -32,6 +32,9 @@ struct bh_ctx {
     uint32_t *perm = nullptr;         // aliases vals or vals_alt after a build
     uint32_t *inv = nullptr;          // Morton rank of each caller index (unsorted walks)
     double *diag = nullptr;           // partial sums of bh_diagnostics
+    unsigned long long *icount = nullptr;   // interactions of the last counted walk
+    bool counting = false;            // bh_set_counting: walks count into icount
+    bool last_counted = false;        // the last walk counted into icount
 
     // lock-based dense build (allocated on first use)
     int32_t *lk_child = nullptr, *lk_level = nullptr, *lk_next = nullptr, *lk_counter = nullptr;
@@ -72,7 +75,7 @@ void free_all(bh_ctx *c)
     void *ptrs[] = {c->prm, c->hlut, c->bbox_part, c->keys, c->keys_alt, c->vals, c->vals_alt, c->spine,
                     c->spos, c->bw.dc, c->bw.tile_counts, c->bw.tile_sums, c->bw.chunk_tot, c->bw.tile_scan,
                     c->bw.first_node, c->bw.P, c->nodes, c->tkeys, c->tkeys_alt, c->tvals,
-                    c->tvals_alt, c->tspine, c->tpos, c->inv, c->diag, c->lk_child,
+                    c->tvals_alt, c->tspine, c->tpos, c->inv, c->diag, c->icount, c->lk_child,
                     c->lk_level, c->lk_next, c->lk_counter};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
@@ -171,6 +174,7 @@ bh_status bh_create(bh_ctx **out, int64_t max_sources, int64_t max_targets,
     ok &= dalloc(&c->nodes, (size_t)c->node_cap + 1) == hipSuccess;
     ok &= dalloc(&c->inv, ns) == hipSuccess;
     ok &= dalloc(&c->diag, (size_t)kDiagMaxPartials * kDiagTerms) == hipSuccess;
+    ok &= dalloc(&c->icount, 1) == hipSuccess;
     if (nt) {
         ok &= dalloc(&c->tkeys, nt) == hipSuccess;
         ok &= dalloc(&c->tkeys_alt, nt) == hipSuccess;
@@ -263,7 +267,14 @@ static bh_status gravity_impl(bh_ctx *c, const float *targets, int64_t n_targets
     hipStream_t s = (hipStream_t)stream;
     c->last_stream = s;
     const uint32_t nt = (uint32_t)n_targets;
-    if (nt == 0) return BH_OK;
+    // with counting on, a walk without a caller's counter counts into the
+    // context's own (from zero), for bh_get_interactions
+    c->last_counted = !count && c->counting;
+    if (c->last_counted) {
+        launch_zero_u64(c->icount, s);
+        count = (uint64_t *)c->icount;
+    }
+    if (nt == 0) return launch_status();
     if (c->n_src == 0) {
         launch_fill_zero((float4 *)out, nt, s);
         return launch_status();
@@ -586,6 +597,43 @@ bh_status bh_get_bbox(bh_ctx *c, double *lo, double *hi, double *L, void *stream
     }
     *L = c->host_prm->L;
     return BH_OK;
+}
+
+bh_status bh_set_counting(bh_ctx *c, int enable)
+{
+    if (!c) return BH_ERR_INVALID;
+    c->counting = enable != 0;
+    return BH_OK;
+}
+
+bh_status bh_get_interactions(bh_ctx *c, uint64_t *host_total)
+{
+    if (!c || !host_total) return BH_ERR_INVALID;
+    if (!c->last_counted) return BH_ERR_INVALID;
+    unsigned long long v = 0;
+    if (hipMemcpyAsync(&v, c->icount, sizeof(v), hipMemcpyDeviceToHost, c->last_stream) !=
+            hipSuccess ||
+        hipStreamSynchronize(c->last_stream) != hipSuccess)
+        return BH_ERR_HIP;
+    *host_total = (uint64_t)v;
+    return BH_OK;
+}
+
+bh_status bh_get_cells(bh_ctx *c, int64_t *n_nodes, uint8_t *level, uint64_t *prefix,
+                       uint32_t *count, void *stream)
+{
+    if (!c || !n_nodes) return BH_ERR_INVALID;
+    if (!c->built) return BH_ERR_NOT_BUILT;
+    *n_nodes = 0;
+    if (c->n_src == 0) return BH_OK;
+    hipStream_t s = (hipStream_t)stream;
+    bh_status st = read_params(c, s);   // the node count (and the build's status)
+    if (st != BH_OK) return st;
+    if (c->host_prm->status & (kStatusNonFinite | kStatusCapacity)) return BH_ERR_NOT_BUILT;
+    const uint32_t nn = c->host_prm->n_nodes;
+    *n_nodes = nn;
+    launch_cells(c->nodes, c->spos, nn, c->bits, c->prm, level, prefix, count, s);
+    return launch_status();
 }
 
 bh_status bh_set_profiling(bh_ctx *c, int enable)

@@ -37,10 +37,13 @@ struct alignas(16) D4 {
 __host__ __device__ inline D4 operator+(D4 a, D4 b) { return D4{a.m + b.m, a.x + b.x, a.y + b.y, a.z + b.z}; }
 __host__ __device__ inline D4 operator-(D4 a, D4 b) { return D4{a.m - b.m, a.x - b.x, a.y - b.y, a.z - b.z}; }
 
-// Exclusive per-tile prefix of node counts and particle sums.
+// Exclusive per-tile prefix of node counts and particle sums.  Node counts
+// are 32-bit (a chunk of tiles holds at most 2^21 positions, so fewer than
+// 2^26 nodes); the scan over chunks also sums them in 64 bits and sets
+// `wrapped` in the totals entry when the whole tree has 2^32 nodes or more.
 struct alignas(16) TileScan {
     D4 sums;
-    uint32_t nodes, pad[3];
+    uint32_t nodes, wrapped, pad[2];
 };
 
 // Pre-order node record; the public bh_node has the same layout.
@@ -135,6 +138,15 @@ struct BuildScratch {
 void build_tree(const uint64_t *keys_sorted, const float4 *spos, uint32_t n, int bits,
                 int leaf_cap, uint64_t node_capacity, BuildScratch &w, Node *nodes,
                 DevParams *prm, hipStream_t s);
+
+// per node: level, key prefix of the cell's place on its level's grid, count
+// (any output may be NULL)
+void launch_cells(const Node *nodes, const float4 *spos, uint32_t nn, int bits,
+                  const DevParams *prm, uint8_t *level, uint64_t *prefix, uint32_t *count,
+                  hipStream_t s);
+
+// *p = 0 by a one-thread kernel (no memset node under stream capture)
+void launch_zero_u64(unsigned long long *p, hipStream_t s);
 
 // hmax.hip: per-node maximum of h (caller order) over the node's sources
 void launch_node_hmax(const Node *nodes, const uint32_t *perm, const float *h, uint32_t n_nodes,

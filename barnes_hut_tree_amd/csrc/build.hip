@@ -277,15 +277,20 @@ __global__ __launch_bounds__(kTileScanThreads) void k_scan_chunks(
     constexpr int kWavesScan = kTileScanThreads / 64;
     __shared__ D4 wsum[kWavesScan + 1];
     __shared__ uint32_t wcnt[kWavesScan + 1];
+    __shared__ unsigned long long wide[kWavesScan];
     const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t k = threadIdx.x;
     const uint32_t c = k < n_chunks ? tot[k].nodes : 0u;
     const D4 m = k < n_chunks ? tot[k].sums : D4{0.0, 0.0, 0.0, 0.0};
     const uint32_t ic = wave_incl_scan(c);
     const D4 im = wave_incl_scan_d4(m);
+    // the same node total in 64 bits, to detect a 32-bit wrap
+    unsigned long long c64 = c;
+    for (int o = 32; o > 0; o >>= 1) c64 += __shfl_xor(c64, o, 64);
     if (lane == 63) {
         wcnt[wave] = ic;
         wsum[wave] = im;
+        wide[wave] = c64;
     }
     __syncthreads();
     // the first wave turns the wave totals into exclusive prefixes
@@ -311,7 +316,10 @@ __global__ __launch_bounds__(kTileScanThreads) void k_scan_chunks(
         out[k].sums = rm;
     }
     if (k == 0) {
+        unsigned long long all = 0;
+        for (int w = 0; w < kWavesScan; ++w) all += wide[w];
         out[n_chunks].nodes = tc;
+        out[n_chunks].wrapped = all > 0xffffffffull ? 1u : 0u;
         out[n_chunks].sums = tm;
     }
 }
@@ -445,7 +453,7 @@ __global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restri
     }
     if (blk == 0 && threadIdx.x == 0) {
         prm->n_nodes = total;
-        if (total > cap) prm->status |= kStatusCapacity;
+        if (total > cap || chunk_pref[n_chunks].wrapped) prm->status |= kStatusCapacity;
     }
 }
 
@@ -563,6 +571,40 @@ __global__ __launch_bounds__(256) void k_ranges(const uint64_t *__restrict__ key
     }
 }
 
+// Per node in pre-order, the canonical description of its cell: level,
+// count, and the key prefix naming the cell's place on its level's grid (the
+// top `level` bits of each integer coordinate, interleaved x into bit 3k, y
+// into 3k + 1, z into 3k + 2, the octant numbering of [Tree] 构建树结构).  The
+// place comes from the quantised coordinates of the cell's first sorted
+// source, so it is the same for either key curve.
+__global__ __launch_bounds__(256) void k_cells(const Node *__restrict__ nodes,
+                                               const float4 *__restrict__ spos, uint32_t nn,
+                                               int bits, const DevParams *__restrict__ prm,
+                                               uint8_t *__restrict__ level,
+                                               uint64_t *__restrict__ prefix,
+                                               uint32_t *__restrict__ count)
+{
+    const uint64_t top = (1ull << bits) - 1;
+    for (uint32_t X = blockIdx.x * blockDim.x + threadIdx.x; X < nn; X += gridDim.x * blockDim.x) {
+        const uint4 rec = reinterpret_cast<const uint4 *>(&nodes[X])[1];
+        const int l = (int)node_level(rec.w);
+        if (level) level[X] = (uint8_t)l;
+        if (count) count[X] = rec.y;
+        if (prefix) {
+            const float4 p = spos[rec.x];
+            const float xyz[3] = {p.x, p.y, p.z};
+            uint64_t pre = 0;
+            for (int a = 0; a < 3; ++a) {
+                const uint64_t c = quantise(xyz[a], prm->lo[a], prm->scale, top) >> (bits - l);
+                for (int k = 0; k < l; ++k) pre |= ((c >> k) & 1ull) << (3 * k + a);
+            }
+            prefix[X] = pre;
+        }
+    }
+}
+
+__global__ void k_zero_u64(unsigned long long *p) { *p = 0ull; }
+
 uint32_t grid_for(uint64_t items, uint32_t max_blocks)
 {
     uint64_t b = (items + 255) / 256;
@@ -615,6 +657,20 @@ void build_tree(const uint64_t *keys_sorted, const float4 *spos, uint32_t n, int
     hipLaunchKernelGGL(k_ranges, dim3(grid_for(n / 2 + 1, 65535)), dim3(256), 0, s, keys_sorted, spos,
                        (const D4 *)w.P, n, bits, node_capacity, (const uint32_t *)w.first_node,
                        nodes, (const DevParams *)prm);
+}
+
+void launch_zero_u64(unsigned long long *p, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(1), 0, s, p);
+}
+
+void launch_cells(const Node *nodes, const float4 *spos, uint32_t nn, int bits,
+                  const DevParams *prm, uint8_t *level, uint64_t *prefix, uint32_t *count,
+                  hipStream_t s)
+{
+    if (nn == 0) return;
+    hipLaunchKernelGGL(k_cells, dim3(grid_for(nn, 4096)), dim3(256), 0, s, nodes, spos, nn, bits,
+                       prm, level, prefix, count);
 }
 
 }  // namespace bh

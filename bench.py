@@ -80,16 +80,18 @@ def read_traffic(workload, curve):
         return None
 
 
-def cpu_baseline(p, prm, key_bits, leaf_cap, budget_s=8.0):
+def cpu_baseline(p, prm, key_bits, leaf_cap, curve, budget_s=8.0):
     """The oracle (fp64, OpenMP) on the host: full tree build plus the walk
     for a random sample of targets sized to about budget_s seconds, scaled to
-    the whole step."""
+    the whole step.  Returns the baseline record and the oracle's interaction
+    count for the step: exact when the sample is every target, else scaled
+    from the sample (the label says which)."""
     import numpy as np
 
     import oracle
     n = p.shape[0]
     t0 = time.perf_counter()
-    tree = oracle.Tree(p, key_bits, leaf_cap)
+    tree = oracle.Tree(p, key_bits, leaf_cap, curve=curve)
     t_build = time.perf_counter() - t0
     rng = np.random.default_rng(99)
     m = min(n, 1 << 13)
@@ -106,12 +108,16 @@ def cpu_baseline(p, prm, key_bits, leaf_cap, budget_s=8.0):
     per_target = t_walk / m
     t_step = t_build + per_target * n
     inter = float(ni.sum()) * n / m
-    return {
+    rec = {
         "value": inter / t_step, "unit": "interactions/s", "cores": oracle.threads(),
         "kind": "oracle",
         "sample": "full fp64 tree build (%.2f s) + walk of %d random targets of %d (%.2f s), "
                   "scaled to all targets: %.2f s per step" % (t_build, m, n, t_walk, t_step),
     }
+    count = {"interactions": int(ni.sum()) if m == n else int(round(inter)),
+             "kind": "exact: every target walked" if m == n else
+                     "scaled from %d of %d targets" % (m, n)}
+    return rec, count
 
 
 def theta_sweep(args):
@@ -542,7 +548,13 @@ def main():
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(p, prm, args.key_bits, args.leaf_cap)
+        rec["cpu_baseline"], oc = cpu_baseline(p, prm, args.key_bits, args.leaf_cap, args.curve)
+        # the numerator checked against the oracle's own count (fp64 opening
+        # decisions: near-ties may flip against the GPU's fp32 ones)
+        rec["config"]["interactions_oracle"] = oc["interactions"]
+        rec["config"]["interactions_oracle_kind"] = oc["kind"]
+        rec["config"]["interactions_rel_diff"] = (interactions - oc["interactions"]) / max(
+            oc["interactions"], 1)
     tree.close()
     print(json.dumps(rec), flush=True)
 

@@ -288,6 +288,33 @@ bh_status bh_get_node_count(bh_ctx *ctx, int64_t *n_nodes, void *stream);
 /* Copy the first n_nodes nodes (bh_node records) into a device buffer. */
 bh_status bh_get_nodes(bh_ctx *ctx, bh_node *nodes, int64_t n_nodes, void *stream);
 
+/* The tree of the last bh_build described cell by cell, in pre-order, as the
+ * octree of [Tree] 构建树结构 defines its cells (synchronous for the count,
+ * then asynchronous on `stream` for the arrays):
+ *   *n_nodes  host: the number of nodes (0 for an empty build);
+ *   level     device, n_nodes bytes: the cell's level (root = 0);
+ *   prefix    device, n_nodes uint64: the cell's place on its level's grid,
+ *             the top `level` bits of each quantised coordinate interleaved
+ *             with x in bit 3k, y in 3k + 1, z in 3k + 2 (the octant
+ *             numbering of [Tree] 构建树结构), for either key curve;
+ *   count     device, n_nodes uint32: the number of sources in the cell.
+ * Any of the three arrays may be NULL.  The caller sizes them from a first
+ * call with all three NULL, or from bh_get_node_count.  Errors:
+ * BH_ERR_NOT_BUILT (no build, or the build failed on the device). */
+bh_status bh_get_cells(bh_ctx *ctx, int64_t *n_nodes, uint8_t *level, uint64_t *prefix,
+                       uint32_t *count, void *stream);
+
+/* Interaction counting for measurement ([GASPHiA] 性能瓶颈分析 counts one
+ * interaction per node used whole and one per source of an opened leaf).
+ * With counting enabled, every bh_gravity / bh_gravity_ex call made without a
+ * caller's counter adds its interactions (accepted nodes plus particle pairs,
+ * self excluded) to the context's own counter, cleared at the start of that
+ * call; the walk is then slower.  bh_get_interactions waits for the stream of
+ * the last such call and returns that call's total; BH_ERR_INVALID if the
+ * context's last walk did not count. */
+bh_status bh_set_counting(bh_ctx *ctx, int enable);
+bh_status bh_get_interactions(bh_ctx *ctx, uint64_t *host_total);
+
 /* Root cube of the last build (synchronous): lo[3] = min corner, hi[3] = max
  * corner of the sources, *L = the cube side (largest extent), all fp64. */
 bh_status bh_get_bbox(bh_ctx *ctx, double *lo, double *hi, double *L, void *stream);

@@ -95,10 +95,15 @@ def test_hilbert_gravity_uniform4096(orc, theta):
     tm.close()
 
 
-def test_hilbert_plummer_2p20(orc):
+@pytest.mark.parametrize("theta", [0.3, 0.5, 0.7])
+def test_hilbert_plummer_2p20(orc, theta):
+    """The benchmark's workload and curve at each opening angle of the
+    Plummer configuration, on 2048 sampled targets, with the median error
+    against the direct sum on the same targets."""
     p = W.plummer(1 << 20, seed=3)
-    log("hilbert plummer 2^20")
-    _sampled_parity(orc, p, 0.5, 0.01, 16, 2048, 37, "hilbert plummer2^20", curve="hilbert")
+    log("hilbert plummer 2^20 theta", theta)
+    _sampled_parity(orc, p, theta, 0.01, 16, 2048, 37, "hilbert plummer2^20 theta=%g" % theta,
+                    curve="hilbert")
 
 
 def test_hilbert_sbh_matches_oracle(orc):

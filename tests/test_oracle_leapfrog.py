@@ -104,3 +104,26 @@ def test_tree_forces_track_direct_forces(orc):
     xd, vd, _ = orc.leapfrog(p, v, 0.01, 10, 0.0, 1.0, 0.02)
     disp = np.linalg.norm(xd - p[:, :3], axis=1)
     assert np.percentile(np.linalg.norm(xb - xd, axis=1) / disp, 99) < 1e-2
+
+
+def test_diagnostics_unequal_masses_by_hand(orc):
+    """Each conserved quantity of two bodies of unequal mass, worked out by
+    hand: masses 1 and 3 at (1, 0, 0) and (0, 2, 0), velocities (0, 1, 0) and
+    (2, 0, 1), potentials -3/sqrt(5) and -1/sqrt(5) (each body's potential
+    from the other at separation sqrt(5), G = 1).  A sum that drops or
+    misplaces the mass weight, the factor 1/2 or an operand of the cross
+    product gives another number."""
+    x = np.array([[1.0, 0.0, 0.0], [0.0, 2.0, 0.0]])
+    m = np.array([1.0, 3.0])
+    v = np.array([[0.0, 1.0, 0.0], [2.0, 0.0, 1.0]])
+    r5 = np.sqrt(5.0)
+    d = orc.diagnostics(x, m, v, [-3.0 / r5, -1.0 / r5])
+    assert d["mass"] == 4.0
+    # (1 * 1 + 3 * (4 + 1)) / 2
+    assert d["kinetic"] == 8.0
+    # (1 * (-3 / sqrt 5) + 3 * (-1 / sqrt 5)) / 2
+    assert d["potential"] == pytest.approx(-3.0 / r5, rel=1e-15)
+    # 1 * (0, 1, 0) + 3 * (2, 0, 1)
+    assert list(d["momentum"]) == [6.0, 1.0, 3.0]
+    # 1 * (1,0,0) x (0,1,0) + 3 * (0,2,0) x (2,0,1) = (0, 0, 1) + 3 * (2, 0, -4)
+    assert list(d["angular_momentum"]) == [6.0, 0.0, -11.0]
