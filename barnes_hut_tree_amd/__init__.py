@@ -32,7 +32,7 @@ EXPORTS = ("bh_create", "bh_build", "bh_gravity", "bh_gravity_counted", "bh_grav
            "bh_leapfrog_step", "bh_diagnostics", "bh_sync", "bh_destroy",
            "bh_status_string", "bh_get_keys", "bh_get_node_count", "bh_get_nodes", "bh_get_bbox",
            "bh_set_profiling", "bh_get_profile", "bh_node_hmax", "bh_get_cells",
-           "bh_set_counting", "bh_get_interactions")
+           "bh_set_counting", "bh_get_interactions", "bh_gravity_static")
 
 NODE_DTYPE_FIELDS = [("com_x", "f4"), ("com_y", "f4"), ("com_z", "f4"), ("mass", "f4"),
                      ("start", "u4"), ("count", "u4"), ("skip", "u4"), ("meta", "u4")]
@@ -91,6 +91,7 @@ def load_library():
         "bh_get_cells": [P, ctypes.POINTER(i64), P, P, P, P],
         "bh_set_counting": [P, i32],
         "bh_get_interactions": [P, ctypes.POINTER(ctypes.c_uint64)],
+        "bh_gravity_static": [P, i64, ctypes.POINTER(_Params), f32, f32, f32, P, P],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -407,6 +408,28 @@ def direct(src, G=1.0, eps=0.0, targets=None, out=None):
     _check(load_library().bh_direct(ctypes.c_void_p(src.data_ptr()), src.shape[0], tp, nt,
                                     float(G), float(eps), ctypes.c_void_p(out.data_ptr()),
                                     _stream()), "bh_direct")
+    return out
+
+
+def gravity_static(pos_mass, theta, G=1.0, eps=0.0, key_bits=63, leaf_cap=16, curve="morton",
+                   out=None):
+    """One self-gravity step (build + walk) that allocates no device memory in
+    the library (bh_gravity_static): its scratch is a static device array.
+    Returns (n, 4) float32 ax, ay, az, phi in the caller's order."""
+    import torch
+    pos_mass = _rows(pos_mass, "pos_mass")
+    n = pos_mass.shape[0]
+    if out is None:
+        out = torch.empty((n, 4), dtype=torch.float32, device="cuda")
+    else:
+        _rows(out, "out")
+        if out.shape[0] != n:
+            raise ValueError("out must have %d rows" % n)
+    p = _Params(int(key_bits), int(leaf_cap), 0, CURVES[curve], 0)
+    _check(load_library().bh_gravity_static(ctypes.c_void_p(pos_mass.data_ptr()), n,
+                                            ctypes.byref(p), float(theta), float(G), float(eps),
+                                            ctypes.c_void_p(out.data_ptr()), _stream()),
+           "bh_gravity_static")
     return out
 
 

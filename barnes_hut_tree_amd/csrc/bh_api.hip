@@ -8,7 +8,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
+#include <type_traits>
 
 #include "bh_internal.h"
 
@@ -92,6 +94,98 @@ void record(bh_ctx *c, int k, hipStream_t s)
 bh_status launch_status()
 {
     return hipGetLastError() == hipSuccess ? BH_OK : BH_ERR_HIP;
+}
+
+}  // namespace
+
+// ---- the allocation-free step -------------------------------------------
+//
+// bh_gravity_static runs bh_build + bh_gravity (self-gravity) on a context
+// whose buffers are carved out of one static device array, so the call never
+// allocates.  The array's host-side name is not a device address: the
+// device's copy is located once per device with hipGetSymbolAddress and only
+// that address is used.  Every buffer the kernels read is written by an
+// earlier kernel of the same call (the bounding-box kernel resets the status
+// word), so nothing needs clearing between calls; calls that overlap on one
+// device race for the array.
+
+namespace {
+
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+constexpr int kStaticMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+struct StaticDevice {
+    unsigned char *base = nullptr;   // this device's copy of `scratch`
+    bool ready = false;
+};
+StaticDevice g_static[kStaticMaxDevices];
+std::mutex g_static_mu;
+
+// Nodes a tree over n sources can need: at each of the levels 0 .. bits-1 the
+// cells holding more than B sources are disjoint, so at most n / (B + 1) of
+// them are split (internal), and leaves are disjoint non-empty cells, at most
+// n; plus the end record.
+uint64_t node_bound(uint64_t n, int bits, int leaf_cap)
+{
+    return (uint64_t)bits * (n / (uint64_t)(leaf_cap + 1)) + n + 1;
+}
+
+// Lays the buffers of a static context for n sources out from `base` (256-byte
+// aligned pieces); returns the bytes used.  base == nullptr only measures.
+size_t static_layout(bh_ctx *c, unsigned char *base, uint32_t n)
+{
+    size_t off = 0;
+    auto take = [&](auto **p, size_t count) {
+        using T = typename std::remove_pointer<typename std::remove_pointer<decltype(p)>::type>::type;
+        if (count == 0) count = 1;
+        if (base) *p = reinterpret_cast<T *>(base + off);
+        off += ((count * sizeof(T) + 255) / 256) * 256;
+    };
+    const size_t ns = n, tiles = build_blocks(n);
+    take(&c->prm, 1);
+    take(&c->hlut, (size_t)kHilbertLutEntries);
+    take(&c->bbox_part, 8 * 1024);
+    take(&c->keys, ns);
+    take(&c->keys_alt, ns);
+    take(&c->vals, ns);
+    take(&c->vals_alt, ns);
+    take(&c->spine, sort_spine_entries(n));
+    take(&c->spos, ns + kSourcePad);
+    take(&c->bw.dc, ns);
+    take(&c->bw.tile_counts, tiles);
+    take(&c->bw.tile_sums, tiles);
+    take(&c->bw.chunk_tot, tiles + 1);
+    take(&c->bw.tile_scan, tiles + 1);
+    take(&c->bw.first_node, ns + 1);
+    take(&c->bw.P, ns + 1);
+    take(&c->nodes, (size_t)c->node_cap + 1);
+    return off;
+}
+
+// The device's copy of `scratch`, located (and the Hilbert key tables copied
+// into it) on the first call on that device.
+bh_status static_base(int dev, unsigned char **out)
+{
+    if (dev < 0 || dev >= kStaticMaxDevices) return BH_ERR_INVALID;
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    StaticDevice &d = g_static[dev];
+    if (!d.ready) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BH_ERR_HIP;
+        bh_ctx probe;
+        static_layout(&probe, (unsigned char *)p, 0);
+        uint16_t host_lut[kHilbertLutEntries];
+        if (!hilbert_lut_host(host_lut)) return BH_ERR_HIP;
+        if (hipMemcpy(probe.hlut, host_lut, sizeof(host_lut), hipMemcpyHostToDevice) !=
+            hipSuccess)
+            return BH_ERR_HIP;
+        d.base = (unsigned char *)p;
+        d.ready = true;
+    }
+    *out = d.base;
+    return BH_OK;
 }
 
 }  // namespace
@@ -656,6 +750,40 @@ bh_status bh_get_profile(bh_ctx *c, float *ms, int n)
         ms[k] = t;
     }
     return BH_OK;
+}
+
+
+bh_status bh_gravity_static(const float *src_pos_mass, int64_t n, const bh_build_params *params,
+                            float theta, float G, float eps, float *out_acc_pot, void *stream)
+{
+    bh_build_params p = {63, 16, 0, 0, 0};
+    if (params) p = *params;
+    if ((p.key_bits != 63 && p.key_bits != 30) || p.leaf_cap < 1 || p.leaf_cap > kMaxLeafCap ||
+        p.node_capacity != 0 || (p.key_curve != BH_CURVE_MORTON && p.key_curve != BH_CURVE_HILBERT) ||
+        p.reserved != 0)
+        return BH_ERR_INVALID;
+    if (n < 0 || n > kMaxCount || !(theta >= 0.f) || !(eps >= 0.f) || !__builtin_isfinite(G))
+        return BH_ERR_INVALID;
+    if (n > 0 && (!src_pos_mass || !out_acc_pot || !aligned16(src_pos_mass) ||
+                  !aligned16(out_acc_pot)))
+        return BH_ERR_INVALID;
+    bh_ctx c;   // host-side description only: no allocation, no events
+    c.max_src = n;
+    c.key_bits = p.key_bits;
+    c.bits = p.key_bits / 3;
+    c.leaf_cap = p.leaf_cap;
+    c.curve = p.key_curve;
+    c.node_cap = node_bound((uint64_t)n, c.bits, c.leaf_cap);
+    if (static_layout(&c, nullptr, (uint32_t)n) > kStaticScratchBytes) return BH_ERR_CAPACITY;
+    if (n == 0) return BH_OK;
+    if (hipGetDevice(&c.device) != hipSuccess) return BH_ERR_HIP;
+    unsigned char *base = nullptr;
+    bh_status st = static_base(c.device, &base);
+    if (st != BH_OK) return st;
+    static_layout(&c, base, (uint32_t)n);
+    st = bh_build(&c, src_pos_mass, n, stream);
+    if (st != BH_OK) return st;
+    return gravity_impl(&c, nullptr, n, theta, G, eps, 0u, out_acc_pot, nullptr, stream);
 }
 
 }  // extern "C"

@@ -265,6 +265,35 @@ bh_status bh_leapfrog_step(bh_ctx *ctx, float *pos_mass, float *vel, float *acc_
 bh_status bh_diagnostics(bh_ctx *ctx, const float *pos_mass, const float *vel,
                          const float *acc_pot, int64_t n, double *out, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP stream
+ * capture, tight serving loops, harnesses that forbid hipMalloc): one
+ * self-gravity step, bh_build followed by bh_gravity with targets == NULL,
+ * with no context.  Every scratch buffer (keys, sort buffers, the sorted
+ * sources, the tree) lives in one static device array of the library, 32 MiB
+ * on each GPU the library runs on, held until the process ends.  The tree's
+ * node capacity is the bound bits * floor(n / (leaf_cap + 1)) + n + 1, which
+ * no input can exceed, so a step fits when about 150 bytes per source (63-bit
+ * keys, leaf_cap 16; about 450 with leaf_cap 1) fit the array: up to roughly
+ * 220000 sources at leaf_cap 16, 75000 at leaf_cap 1.
+ *   src_pos_mass  device, n float4 rows (x, y, z, m), 16-byte aligned.
+ *   params        key_bits, leaf_cap and key_curve as for bh_create
+ *                 (node_capacity and reserved must be 0); NULL = 63-bit
+ *                 Morton keys, leaf_cap 16.
+ *   out_acc_pot   device, n float4 rows (ax, ay, az, phi), caller order.
+ *   theta, G, eps as for bh_gravity.
+ * Results are bit-identical to bh_build + bh_gravity on a context with the
+ * same parameters.  Errors: BH_ERR_INVALID (bad argument), BH_ERR_CAPACITY
+ * (the step needs more than the static array holds: use a context), both
+ * before anything is launched; BH_ERR_HIP.  Non-finite sources give NaN
+ * outputs (there is no status word to read back).  The first call on a
+ * device locates that device's array and copies 7 KB of key-curve tables
+ * into it (synchronous; make it outside stream capture); later calls only
+ * launch kernels on `stream`.  Calls on one device share its array, which
+ * keeps the last call's contents: calls that overlap on one device race
+ * (serialise them, e.g. on one stream).  Calls no hipMalloc or hipFree. */
+bh_status bh_gravity_static(const float *src_pos_mass, int64_t n, const bh_build_params *params,
+                            float theta, float G, float eps, float *out_acc_pot, void *stream);
+
 /* Wait for the context's last stream and return the device status word
  * (BH_OK, BH_ERR_NONFINITE or BH_ERR_CAPACITY).  Synchronous. */
 bh_status bh_sync(bh_ctx *ctx);
