@@ -545,7 +545,7 @@ __global__ __launch_bounds__(256) void k_ranges(const uint64_t *__restrict__ key
         // leaf at an undefined (NaN) centre, which every target still walking
         // opens, so the walk needs no bound check on its common path
         reinterpret_cast<float4 *>(&nodes[nn])[0] = make_float4(NAN, NAN, NAN, 0.f);
-        reinterpret_cast<uint4 *>(&nodes[nn])[1] = make_uint4(n, 0u, nn + 1, kLeafBit);
+        reinterpret_cast<uint4 *>(&nodes[nn])[1] = make_uint4(n, 0u, nn, kLeafBit);
     }
     for (uint32_t X = blockIdx.x * blockDim.x + threadIdx.x; X < nn; X += gridDim.x * blockDim.x) {
         const uint4 rec = reinterpret_cast<const uint4 *>(&nodes[X])[1];

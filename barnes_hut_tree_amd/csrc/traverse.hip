@@ -22,7 +22,8 @@
 // own).
 //
 // The walk is a loop written in assembly: node visits, descents and the sums
-// of opened leaves.  The build writes an end record after the last node,
+// of opened leaves, with each next node record requested before the current
+// visit's arithmetic.  The build writes an end record after the last node,
 // which every lane still walking opens, so the loop needs no bound check; it
 // returns to C++ at that record and at leaves that may hold the wave's own
 // targets, where the self pair is masked.
@@ -91,30 +92,44 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
 // The assembly loop of the walk.  Register use: the node records of two
 // consecutive visits land in s[32:39] and s[40:47] (x, y, z, m, start, count,
 // skip, meta), so the next visit's node index is the previous record's skip
-// field where it lies; a leaf's sources are loaded into s[16:47] and their
-// address formed in s[48:49].  These fixed registers sit low: a kernel's
-// scalar register count is its highest register used, and the walk keeps
-// eight waves per SIMD only up to about 76 (measured: 70 registers gave 8
-// resident waves, 90 gave 7, 96 gave 6, and the walk ran 7% faster at 68 than
-// at 90 with the same code).  One visit of node XR (record slot R0..R7, loaded
-// through RT):
+// field where it lies; a leaf's sources are loaded six at a time into
+// s[16:31] and the leaf's own record slot, their address formed in
+// s[48:49].  These fixed registers sit low: a kernel's scalar register count
+// is its highest register used, and the walk keeps eight waves per SIMD only
+// up to about 76 (measured: 70 registers gave 8 resident waves, 90 gave 7, 96
+// gave 6, and the walk ran 7% faster at 68 than at 90 with the same code).
+//
+// The loop is bound by the latency of each visit's scalar load of its node
+// record (waves spend about half their cycles waiting on it), so the record
+// of the next visit is requested as early as its index is known.  Moves to
+// the skip are the common case (a wave descends into about one node in five
+// it visits), so when a record arrives the loop at once requests the record
+// at its skip into the other slot, before any arithmetic; the wave moves
+// there when no lane opens the node, a descent waits for that request and
+// then requests X + 1 instead, and an opened leaf (whose skip is X + 1) keeps
+// it while its sources pass through the leaf's own slot.  Only in-bounds
+// records are requested: skips point at most at the end record, whose own
+// skip is itself.
+//
+// One visit of node XR (record slot R0..R7, the other slot OTHER):
 //   act  = rejoin <= X                         (vcc, then exec)
 //   T    = T0 * 4^-level, the exponent of T0 stepped down by 2 * level
 //   far  = T < r^2, by a compare that also narrows exec to act & far
+//   open = act & ~exec                          (SCC: some lane opens X)
 //   lanes in act & far add the monopole (their rejoin moves to the node's
 //   skip only where the wave descends into the node or returns, below)
-//   open = act & ~exec                          (SCC: some lane opens X)
 // The monopole is inv = rsq(r^2 + eps^2), f = m inv^3, a += f d, pot -= m inv,
 // with eps^2 in a vector register and the potential term unfused, so that all
-// but the node-field operands are register-only.  One instruction (the branch
-// past the monopole, taken when no lane accepts) sits between the reciprocal
-// square root and the first use of its result, which the hardware requires.
+// but the node-field operands are register-only.  At least one instruction
+// sits between the reciprocal square root and the first use of its result,
+// which the hardware requires.  %[off] holds X + 1 from the head on.
 // CNT: the interaction count update, if any.
-#define BH_VISIT(R0, R1, R2, R3, R6, R7, RT, XR, CNT, SKIP_LABEL)                       \
-    "s_lshl_b32 %[off], " XR ", 5\n"                                                   \
-    "s_load_dwordx8 " RT ", %[nb], %[off]\n"                                           \
+#define BH_HEAD(R0, R1, R2, R6, R7, XR, OTHER)                                         \
     "v_cmp_ge_u32_e32 vcc, " XR ", %[rej]\n"                                           \
+    "s_add_u32 %[off], " XR ", 1\n"                                                    \
     "s_waitcnt lgkmcnt(0)\n"                                                           \
+    "s_lshl_b32 %[le], " R6 ", 5\n"                                                    \
+    "s_load_dwordx8 " OTHER ", %[nb], %[le]\n"                                         \
     "v_sub_f32_e32 %[dx], " R0 ", %[px]\n"                                             \
     "v_sub_f32_e32 %[dy], " R1 ", %[py]\n"                                             \
     "v_mul_f32_e32 %[r2], %[dx], %[dx]\n"                                              \
@@ -127,7 +142,8 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     "v_cmpx_lt_f32_e64 %[far], %[t], %[r2]\n"                                          \
     "v_add_f32_e32 %[w], %[eps2], %[r2]\n"                                             \
     "v_rsq_f32_e32 %[w], %[w]\n"                                                       \
-    "s_cbranch_execz " SKIP_LABEL "\n"                                                 \
+    "s_andn2_b64 %[open], vcc, exec\n"
+#define BH_MONO(R3, CNT)                                                               \
     "v_mul_f32_e32 %[f], " R3 ", %[w]\n"                                               \
     "v_sub_f32_e32 %[pot], %[pot], %[f]\n"                                             \
     "v_mul_f32_e32 %[f], %[w], %[f]\n"                                                 \
@@ -135,10 +151,10 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     "v_fmac_f32_e32 %[ax], %[f], %[dx]\n"                                              \
     "v_fmac_f32_e32 %[ay], %[f], %[dy]\n"                                              \
     "v_fmac_f32_e32 %[az], %[f], %[dz]\n"                                              \
-    CNT                                                                                \
-    SKIP_LABEL ":\n"                                                                   \
-    "s_andn2_b64 %[open], vcc, exec\n"                                                 \
-    "s_mov_b64 exec, %[save]\n"
+    CNT
+#define BH_FETCH(NX, OTHER)                                                            \
+    "s_lshl_b32 %[t], " NX ", 5\n"                                                     \
+    "s_load_dwordx8 " OTHER ", %[nb], %[t]\n"
 
 // One source of a leaf opened in the assembly loop, in the order of
 // leaf_pair(): X, Y, Z, M name the source's scalar registers.  GUARD is the
@@ -173,16 +189,17 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
 #define BH_LAST "s_nop 0\n"
 
 // Visits from node X on, two per loop turn (slots A and B).  A node no lane
-// opens moves the wave to its skip; an opened internal node (meta without the
-// leaf bit) to X + 1; an opened leaf is summed by its openers, eight sources
-// per batch of two scalar loads into s[16:47] (the record slots are free
-// then; the next node index waits in %[skip]; the batch address, in
-// s[48:49], is formed in 64 bits), and the wave moves on to its
-// skip.  The loop returns to the caller at the end record (count 0) and at a
-// leaf that may hold the wave's own targets ([first, first + count) meets
-// [wb, wbe)), whose self pairs the caller masks; X and the leaf's start,
-// count and skip are then the outputs.  Every step moves X forward, and the
-// end record ends the loop at the latest.
+// opens moves the wave to its skip, whose record is already on its way into
+// the other slot; an opened internal node (meta without the leaf bit) to
+// X + 1; an opened leaf is summed by its openers, six sources per batch (one
+// 64-byte and one 32-byte scalar load; the batch address, in s[48:49], is
+// formed in 64 bits), and the wave moves on to its skip, the record already
+// in the other slot.  The loop returns to the caller at the end record (count
+// 0) and at a leaf that may hold the wave's own targets ([first, first +
+// count) meets [wb, wbe)), whose self pairs the caller masks; X and the
+// leaf's start, count and skip are then the outputs, and nothing is left in
+// flight into the fixed registers.  Every step moves X forward, and the end
+// record ends the loop at the latest.
 // The lanes that used the node just visited (act & ~open, with act still in
 // vcc) sit out its subtree: rejoin = its skip.  Needed only when the wave
 // descends into that subtree or returns to the caller; when it moves to the
@@ -194,73 +211,131 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
 
 #define BH_RUN(CNT, LEAF_CNT, G)                                                       \
     "s_mov_b32 s46, %[X]\n"                                                            \
+    BH_FETCH("s46", "s[32:39]")                                                        \
     "BH_A%=:\n"                                                                        \
-    BH_VISIT("s32", "s33", "s34", "s35", "s38", "s39", "s[32:39]", "s46", CNT,         \
-             "BH_NA%=")                                                                \
+    BH_HEAD("s32", "s33", "s34", "s38", "s39", "s46", "s[40:47]")                      \
     "s_cbranch_scc1 BH_OA%=\n"                                                         \
+    BH_MONO("s35", CNT)                                                                \
+    "s_mov_b64 exec, %[save]\n"                                                        \
     "BH_B%=:\n"                                                                        \
-    BH_VISIT("s40", "s41", "s42", "s43", "s46", "s47", "s[40:47]", "s38", CNT,         \
-             "BH_NB%=")                                                                \
-    "s_cbranch_scc0 BH_A%=\n"                                                          \
-    "s_bitcmp1_b32 s47, 8\n"                                                           \
-    "s_cbranch_scc1 BH_LB%=\n"                                                         \
-    BH_SIT_OUT("s46")                                                                  \
-    "s_add_u32 s46, s38, 1\n"                                                          \
+    BH_HEAD("s40", "s41", "s42", "s46", "s47", "s38", "s[32:39]")                      \
+    "s_cbranch_scc1 BH_OB%=\n"                                                         \
+    BH_MONO("s43", CNT)                                                                \
+    "s_mov_b64 exec, %[save]\n"                                                        \
     "s_branch BH_A%=\n"                                                                \
     "BH_OA%=:\n"                                                                       \
     "s_bitcmp1_b32 s39, 8\n"                                                           \
-    "s_cbranch_scc1 BH_LA%=\n"                                                         \
+    "s_cbranch_scc1 BH_KA%=\n"                                                         \
+    "s_waitcnt lgkmcnt(0)\n"                                                           \
+    BH_FETCH("%[off]", "s[40:47]")                                                     \
+    "s_cbranch_execz BH_NA%=\n"                                                        \
+    BH_MONO("s35", CNT)                                                                \
+    "BH_NA%=:\n"                                                                       \
     BH_SIT_OUT("s38")                                                                  \
-    "s_add_u32 s38, s46, 1\n"                                                          \
+    "s_mov_b32 s38, %[off]\n"                                                          \
     "s_branch BH_B%=\n"                                                                \
-    "BH_LB%=:\n"                                                                       \
-    "s_mov_b32 %[X], s38\n"                                                            \
-    "s_mov_b32 %[first], s44\n"                                                        \
-    "s_mov_b32 %[cnt], s45\n"                                                          \
-    "s_mov_b32 %[skip], s46\n"                                                         \
-    "s_branch BH_L%=\n"                                                                \
-    "BH_LA%=:\n"                                                                       \
-    "s_mov_b32 %[X], s46\n"                                                            \
+    "BH_OB%=:\n"                                                                       \
+    "s_bitcmp1_b32 s47, 8\n"                                                           \
+    "s_cbranch_scc1 BH_KB%=\n"                                                         \
+    "s_waitcnt lgkmcnt(0)\n"                                                           \
+    BH_FETCH("%[off]", "s[32:39]")                                                     \
+    "s_cbranch_execz BH_NB%=\n"                                                        \
+    BH_MONO("s43", CNT)                                                                \
+    "BH_NB%=:\n"                                                                       \
+    BH_SIT_OUT("s46")                                                                  \
+    "s_mov_b32 s46, %[off]\n"                                                          \
+    "s_branch BH_A%=\n"                                                                \
+    "BH_KA%=:\n"                                                                       \
+    "s_cbranch_execz BH_MA%=\n"                                                        \
+    BH_MONO("s35", CNT)                                                                \
+    "BH_MA%=:\n"                                                                       \
+    "s_mov_b64 exec, %[save]\n"                                                        \
+    "s_sub_u32 %[X], %[off], 1\n"                                                      \
     "s_mov_b32 %[first], s36\n"                                                        \
     "s_mov_b32 %[cnt], s37\n"                                                          \
     "s_mov_b32 %[skip], s38\n"                                                         \
-    "BH_L%=:\n"                                                                        \
+    "BH_LA%=:\n"                                                                       \
     "s_cmp_eq_u32 %[cnt], 0\n"                                                         \
     "s_cbranch_scc1 BH_E%=\n"                                                          \
     "s_add_u32 %[le], %[first], %[cnt]\n"                                              \
     "s_cmp_lt_u32 %[first], %[wbe]\n"                                                  \
-    "s_cbranch_scc0 BH_LN%=\n"                                                         \
+    "s_cbranch_scc0 BH_LNA%=\n"                                                        \
     "s_cmp_gt_u32 %[le], %[wb]\n"                                                      \
     "s_cbranch_scc1 BH_E%=\n"                                                          \
-    "BH_LN%=:\n"                                                                       \
+    "BH_LNA%=:\n"                                                                      \
     "s_and_saveexec_b64 %[save], %[open]\n"                                            \
     "s_mov_b32 %[j], %[first]\n"                                                       \
-    "BH_LT%=:\n"                                                                       \
+    "BH_LTA%=:\n"                                                                      \
     "s_lshl_b32 s48, %[j], 4\n"                                                        \
     "s_lshr_b32 s49, %[j], 28\n"                                                       \
     "s_add_u32 s48, s48, %[srclo]\n"                                                   \
     "s_addc_u32 s49, s49, %[srchi]\n"                                                  \
+    "s_waitcnt lgkmcnt(0)\n"                                                           \
     "s_load_dwordx16 s[16:31], s[48:49], 0x0\n"                                        \
-    "s_load_dwordx16 s[32:47], s[48:49], 0x40\n"                                       \
+    "s_load_dwordx8 s[32:39], s[48:49], 0x40\n"                                        \
     "s_sub_u32 %[left], %[le], %[j]\n"                                                 \
     "s_waitcnt lgkmcnt(0)\n"                                                           \
-    BH_PAIR("s16", "s17", "s18", "s19", G, BH_NEXT(2)) "s_cbranch_scc1 BH_LD%=\n"      \
-    BH_PAIR("s20", "s21", "s22", "s23", G, BH_NEXT(3)) "s_cbranch_scc1 BH_LD%=\n"      \
-    BH_PAIR("s24", "s25", "s26", "s27", G, BH_NEXT(4)) "s_cbranch_scc1 BH_LD%=\n"      \
-    BH_PAIR("s28", "s29", "s30", "s31", G, BH_NEXT(5)) "s_cbranch_scc1 BH_LD%=\n"      \
-    BH_PAIR("s32", "s33", "s34", "s35", G, BH_NEXT(6)) "s_cbranch_scc1 BH_LD%=\n"      \
-    BH_PAIR("s36", "s37", "s38", "s39", G, BH_NEXT(7)) "s_cbranch_scc1 BH_LD%=\n"      \
-    BH_PAIR("s40", "s41", "s42", "s43", G, BH_NEXT(8)) "s_cbranch_scc1 BH_LD%=\n"      \
-    BH_PAIR("s44", "s45", "s46", "s47", G, BH_LAST)                                    \
-    "s_add_u32 %[j], %[j], 8\n"                                                        \
+    BH_PAIR("s16", "s17", "s18", "s19", G, BH_NEXT(2)) "s_cbranch_scc1 BH_LDA%=\n"     \
+    BH_PAIR("s20", "s21", "s22", "s23", G, BH_NEXT(3)) "s_cbranch_scc1 BH_LDA%=\n"     \
+    BH_PAIR("s24", "s25", "s26", "s27", G, BH_NEXT(4)) "s_cbranch_scc1 BH_LDA%=\n"     \
+    BH_PAIR("s28", "s29", "s30", "s31", G, BH_NEXT(5)) "s_cbranch_scc1 BH_LDA%=\n"     \
+    BH_PAIR("s32", "s33", "s34", "s35", G, BH_NEXT(6)) "s_cbranch_scc1 BH_LDA%=\n"     \
+    BH_PAIR("s36", "s37", "s38", "s39", G, BH_LAST)                                    \
+    "s_add_u32 %[j], %[j], 6\n"                                                        \
     "s_cmp_lt_u32 %[j], %[le]\n"                                                       \
-    "s_cbranch_scc1 BH_LT%=\n"                                                         \
-    "BH_LD%=:\n"                                                                       \
+    "s_cbranch_scc1 BH_LTA%=\n"                                                        \
+    "BH_LDA%=:\n"                                                                      \
+    LEAF_CNT                                                                           \
+    "s_mov_b64 exec, %[save]\n"                                                        \
+    "s_mov_b32 s38, %[skip]\n"                                                         \
+    "s_branch BH_B%=\n"                                                                \
+    "BH_KB%=:\n"                                                                       \
+    "s_cbranch_execz BH_MB%=\n"                                                        \
+    BH_MONO("s43", CNT)                                                                \
+    "BH_MB%=:\n"                                                                       \
+    "s_mov_b64 exec, %[save]\n"                                                        \
+    "s_sub_u32 %[X], %[off], 1\n"                                                      \
+    "s_mov_b32 %[first], s44\n"                                                        \
+    "s_mov_b32 %[cnt], s45\n"                                                          \
+    "s_mov_b32 %[skip], s46\n"                                                         \
+    "BH_LB%=:\n"                                                                       \
+    "s_cmp_eq_u32 %[cnt], 0\n"                                                         \
+    "s_cbranch_scc1 BH_E%=\n"                                                          \
+    "s_add_u32 %[le], %[first], %[cnt]\n"                                              \
+    "s_cmp_lt_u32 %[first], %[wbe]\n"                                                  \
+    "s_cbranch_scc0 BH_LNB%=\n"                                                        \
+    "s_cmp_gt_u32 %[le], %[wb]\n"                                                      \
+    "s_cbranch_scc1 BH_E%=\n"                                                          \
+    "BH_LNB%=:\n"                                                                      \
+    "s_and_saveexec_b64 %[save], %[open]\n"                                            \
+    "s_mov_b32 %[j], %[first]\n"                                                       \
+    "BH_LTB%=:\n"                                                                      \
+    "s_lshl_b32 s48, %[j], 4\n"                                                        \
+    "s_lshr_b32 s49, %[j], 28\n"                                                       \
+    "s_add_u32 s48, s48, %[srclo]\n"                                                   \
+    "s_addc_u32 s49, s49, %[srchi]\n"                                                  \
+    "s_waitcnt lgkmcnt(0)\n"                                                           \
+    "s_load_dwordx16 s[16:31], s[48:49], 0x0\n"                                        \
+    "s_load_dwordx8 s[40:47], s[48:49], 0x40\n"                                        \
+    "s_sub_u32 %[left], %[le], %[j]\n"                                                 \
+    "s_waitcnt lgkmcnt(0)\n"                                                           \
+    BH_PAIR("s16", "s17", "s18", "s19", G, BH_NEXT(2)) "s_cbranch_scc1 BH_LDB%=\n"     \
+    BH_PAIR("s20", "s21", "s22", "s23", G, BH_NEXT(3)) "s_cbranch_scc1 BH_LDB%=\n"     \
+    BH_PAIR("s24", "s25", "s26", "s27", G, BH_NEXT(4)) "s_cbranch_scc1 BH_LDB%=\n"     \
+    BH_PAIR("s28", "s29", "s30", "s31", G, BH_NEXT(5)) "s_cbranch_scc1 BH_LDB%=\n"     \
+    BH_PAIR("s40", "s41", "s42", "s43", G, BH_NEXT(6)) "s_cbranch_scc1 BH_LDB%=\n"     \
+    BH_PAIR("s44", "s45", "s46", "s47", G, BH_LAST)                                    \
+    "s_add_u32 %[j], %[j], 6\n"                                                        \
+    "s_cmp_lt_u32 %[j], %[le]\n"                                                       \
+    "s_cbranch_scc1 BH_LTB%=\n"                                                        \
+    "BH_LDB%=:\n"                                                                      \
     LEAF_CNT                                                                           \
     "s_mov_b64 exec, %[save]\n"                                                        \
     "s_mov_b32 s46, %[skip]\n"                                                         \
     "s_branch BH_A%=\n"                                                                \
-    "BH_E%=:\n" BH_SIT_OUT("%[skip]")
+    "BH_E%=:\n"                                                                        \
+    "s_waitcnt lgkmcnt(0)\n"                                                           \
+    BH_SIT_OUT("%[skip]")
 
 #define BH_RUN_OUTS                                                                    \
     [X] "+s"(X), [ax] "+v"(ax), [ay] "+v"(ay), [az] "+v"(az), [pot] "+v"(pot),        \
@@ -283,16 +358,18 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
 // decrement on the scalar unit (exact whenever T0 * 4^-21 stays normal), or,
 // with FIXED_T, T0 itself (T0 = 0, inf or NaN is the same at every level).
 //
-// The walk is bound by instruction issue.  A wave's vector and scalar
-// instructions share its issue slots, and a vector op with a scalar-register
-// operand issues at about two thirds the rate of one with register operands
-// only.  The assembly loop (above) keeps the per-node path to 17 vector ops,
-// 6 of them with a scalar operand, 8 scalar instructions and 2 branches; the
-// compiled form of the same loop had 18 vector ops with 9 scalar operands, 13
-// scalar instructions and 3 branches, because the compiler re-derives the
-// lane masks and the loop exit on every node, and it copied the accumulators
-// several times around every opened leaf.  The two rarer thresholds keep the
-// compiled loop.
+// The walk is bound by the latency of its dependent node-record loads, with
+// instruction issue second: a wave's vector and scalar instructions share its
+// issue slots, and a vector op with a scalar-register operand issues at about
+// two thirds the rate of one with register operands only.  The assembly loop
+// (above) keeps the path of a visit that moves to the skip to 17 vector ops,
+// 6 of them with a scalar operand, 9 scalar instructions and 1 branch, with
+// the next record's load issued before the first vector op; the compiled
+// form of the loop had 18 vector ops with 9 scalar operands, 13 scalar
+// instructions and 3 branches, because the compiler re-derives the lane masks
+// and the loop exit on every node, and it copied the accumulators several
+// times around every opened leaf.  The two rarer thresholds keep the compiled
+// loop.
 template <bool SOFT, bool SELF, bool COUNT, bool EXACT_T, bool ANY_MINE, bool FIXED_T = false>
 __device__ __attribute__((always_inline)) inline void walk_wave(
     const Node *__restrict__ nodes, const float4 *__restrict__ src, uint32_t nn, float4 p,

@@ -409,8 +409,9 @@ def test_all_coincident(orc):
 
 def test_end_record_after_the_last_node(orc):
     """Every build writes an end record right after its last node (NaN centre,
-    zero mass, an empty leaf starting at n, leaf bit set, level 0): every lane
-    still walking opens it, which ends the walk's loop.  A second, smaller build
+    zero mass, an empty leaf starting at n, leaf bit set, level 0, skip
+    pointing at itself, so a record fetched at its skip stays inside the
+    array): every lane still walking opens it, which ends the walk's loop.  A second, smaller build
     in the same context writes its own at the lower index, and the walk then
     matches the oracle on that tree."""
     import ctypes
@@ -426,7 +427,7 @@ def test_end_record_after_the_last_node(orc):
         assert st == 0
         f = bh.nodes_numpy(buf)
         assert np.all(np.isnan(f["com"][nn])) and f["mass"][nn] == 0.0
-        assert f["start"][nn] == n and f["count"][nn] == 0 and f["skip"][nn] == nn + 1
+        assert f["start"][nn] == n and f["count"][nn] == 0 and f["skip"][nn] == nn
         assert f["is_leaf"][nn] == 1 and f["level"][nn] == 0
         assert np.all(np.isfinite(f["com"][:nn]))
         got = t.gravity(0.5, 1.0, 1e-3).cpu().numpy()
