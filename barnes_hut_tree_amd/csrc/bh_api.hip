@@ -44,6 +44,8 @@ struct bh_ctx {
     uint32_t lk_n = 0;
     BuildScratch bw = {};
     Node *nodes = nullptr;
+    Node *wnodes = nullptr;           // per-call walk records (see launch_walk)
+    uint32_t wn_cap = 0;              // records wnodes holds
 
     uint64_t *tkeys = nullptr, *tkeys_alt = nullptr;
     uint32_t *tvals = nullptr, *tvals_alt = nullptr;
@@ -76,7 +78,7 @@ void free_all(bh_ctx *c)
 {
     void *ptrs[] = {c->prm, c->hlut, c->bbox_part, c->keys, c->keys_alt, c->vals, c->vals_alt, c->spine,
                     c->spos, c->bw.dc, c->bw.tile_counts, c->bw.tile_sums, c->bw.chunk_tot, c->bw.tile_scan,
-                    c->bw.first_node, c->bw.P, c->nodes, c->tkeys, c->tkeys_alt, c->tvals,
+                    c->bw.first_node, c->bw.P, c->nodes, c->wnodes, c->tkeys, c->tkeys_alt, c->tvals,
                     c->tvals_alt, c->tspine, c->tpos, c->inv, c->diag, c->icount, c->lk_child,
                     c->lk_level, c->lk_next, c->lk_counter};
     for (void *p : ptrs)
@@ -96,6 +98,24 @@ bh_status launch_status()
     return hipGetLastError() == hipSuccess ? BH_OK : BH_ERR_HIP;
 }
 
+// Nodes a tree over n sources can need: at each of the levels 0 .. bits-1 the
+// cells holding more than B sources are disjoint, so at most n / (B + 1) of
+// them are split (internal), and leaves are disjoint non-empty cells, at most
+// n; plus the end record.
+uint64_t node_bound(uint64_t n, int bits, int leaf_cap)
+{
+    return (uint64_t)bits * (n / (uint64_t)(leaf_cap + 1)) + n + 1;
+}
+
+// Walk records a context keeps: one per node of the largest tree it can
+// build, the end record included, up to the assembly loop's limit.
+uint32_t walk_records(uint64_t max_src, int bits, int leaf_cap, uint64_t node_cap)
+{
+    uint64_t k = node_bound(max_src, bits, leaf_cap);
+    k = k < node_cap + 1 ? k : node_cap + 1;
+    return (uint32_t)(k < (uint64_t)kAsmMaxNodes ? k : (uint64_t)kAsmMaxNodes);
+}
+
 }  // namespace
 
 // ---- the allocation-free step -------------------------------------------
@@ -111,7 +131,7 @@ bh_status launch_status()
 
 namespace {
 
-constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
 constexpr int kStaticMaxDevices = 64;
 
 static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
@@ -123,14 +143,6 @@ struct StaticDevice {
 StaticDevice g_static[kStaticMaxDevices];
 std::mutex g_static_mu;
 
-// Nodes a tree over n sources can need: at each of the levels 0 .. bits-1 the
-// cells holding more than B sources are disjoint, so at most n / (B + 1) of
-// them are split (internal), and leaves are disjoint non-empty cells, at most
-// n; plus the end record.
-uint64_t node_bound(uint64_t n, int bits, int leaf_cap)
-{
-    return (uint64_t)bits * (n / (uint64_t)(leaf_cap + 1)) + n + 1;
-}
 
 // Lays the buffers of a static context for n sources out from `base` (256-byte
 // aligned pieces); returns the bytes used.  base == nullptr only measures.
@@ -161,6 +173,8 @@ size_t static_layout(bh_ctx *c, unsigned char *base, uint32_t n)
     take(&c->bw.first_node, ns + 1);
     take(&c->bw.P, ns + 1);
     take(&c->nodes, (size_t)c->node_cap + 1);
+    c->wn_cap = walk_records(n, c->bits, c->leaf_cap, c->node_cap);
+    take(&c->wnodes, (size_t)c->wn_cap);
     return off;
 }
 
@@ -266,6 +280,8 @@ bh_status bh_create(bh_ctx **out, int64_t max_sources, int64_t max_targets,
     ok &= dalloc(&c->bw.first_node, ns + 1) == hipSuccess;
     ok &= dalloc(&c->bw.P, ns + 1) == hipSuccess;
     ok &= dalloc(&c->nodes, (size_t)c->node_cap + 1) == hipSuccess;
+    c->wn_cap = walk_records((uint64_t)ns, c->bits, c->leaf_cap, c->node_cap);
+    ok &= dalloc(&c->wnodes, (size_t)c->wn_cap) == hipSuccess;
     ok &= dalloc(&c->inv, ns) == hipSuccess;
     ok &= dalloc(&c->diag, (size_t)kDiagMaxPartials * kDiagTerms) == hipSuccess;
     ok &= dalloc(&c->icount, 1) == hipSuccess;
@@ -375,6 +391,8 @@ static bh_status gravity_impl(bh_ctx *c, const float *targets, int64_t n_targets
     }
     WalkArgs a;
     a.nodes = c->nodes;
+    a.wnodes = c->wnodes;
+    a.wn_cap = c->wn_cap;
     a.src = c->spos;
     a.prm = c->prm;
     a.n_targets = nt;

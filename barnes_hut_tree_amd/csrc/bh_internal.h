@@ -153,8 +153,13 @@ void launch_node_hmax(const Node *nodes, const uint32_t *perm, const float *h, u
                       const DevParams *prm, uint64_t cap, int bits, float *out, hipStream_t s);
 
 // traverse.hip
+// node count up to which the walk's assembly loop runs: its 32-bit node byte
+// offsets (X * 32 for X <= the end record's index) cannot wrap
+constexpr uint32_t kAsmMaxNodes = (1u << 27) - 1;
 struct WalkArgs {
     const Node *nodes;
+    Node *wnodes;               // per-call walk records (skips in bytes, thresholds in place)
+    uint32_t wn_cap;            // records wnodes holds (0: none; the compiled loop walks)
     const float4 *src;          // sources in Morton order
     const float4 *tpos;         // target positions (Morton order, or as given when unsorted)
     const uint32_t *tmap;       // sorted: caller index of each target; unsorted self: Morton rank

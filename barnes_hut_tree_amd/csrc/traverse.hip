@@ -27,6 +27,8 @@
 // which every lane still walking opens, so the loop needs no bound check; it
 // returns to C++ at that record and at leaves that may hold the wave's own
 // targets, where the self pair is masked.
+#include <algorithm>
+
 #include "bh_internal.h"
 #include "interaction.h"
 
@@ -34,9 +36,6 @@ namespace bh {
 namespace {
 
 constexpr int kWalkThreads = 64;
-// node count up to which the assembly loop's 32-bit node byte offsets
-// (X * 32 for X <= the end record's index) cannot wrap
-constexpr uint32_t kAsmMaxNodes = (1u << 27) - 1;
 
 // One source of an opened leaf: the interaction of pair() (interaction.h),
 // with eps2 taken from a vector register and the potential term subtracted
@@ -126,20 +125,17 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
 // CNT: the interaction count update, if any.
 #define BH_HEAD(R0, R1, R2, R6, R7, XR, OTHER)                                         \
     "v_cmp_ge_u32_e32 vcc, " XR ", %[rej]\n"                                           \
-    "s_add_u32 %[off], " XR ", 1\n"                                                    \
+    "s_add_u32 %[off], " XR ", 32\n"                                                   \
     "s_waitcnt lgkmcnt(0)\n"                                                           \
-    "s_lshl_b32 %[le], " R6 ", 5\n"                                                    \
-    "s_load_dwordx8 " OTHER ", %[nb], %[le]\n"                                         \
+    "s_load_dwordx8 " OTHER ", %[nb], " R6 "\n"                                        \
     "v_sub_f32_e32 %[dx], " R0 ", %[px]\n"                                             \
     "v_sub_f32_e32 %[dy], " R1 ", %[py]\n"                                             \
     "v_mul_f32_e32 %[r2], %[dx], %[dx]\n"                                              \
-    "s_lshl_b32 %[t], " R7 ", 24\n"                                                    \
     "v_sub_f32_e32 %[dz], " R2 ", %[pz]\n"                                             \
     "v_fmac_f32_e32 %[r2], %[dy], %[dy]\n"                                             \
-    "s_sub_u32 %[t], %[T0], %[t]\n"                                                    \
     "v_fmac_f32_e32 %[r2], %[dz], %[dz]\n"                                             \
     "s_and_saveexec_b64 %[save], vcc\n"                                                \
-    "v_cmpx_lt_f32_e64 %[far], %[t], %[r2]\n"                                          \
+    "v_cmpx_lt_f32_e64 %[far], |" R7 "|, %[r2]\n"                                      \
     "v_add_f32_e32 %[w], %[eps2], %[r2]\n"                                             \
     "v_rsq_f32_e32 %[w], %[w]\n"                                                       \
     "s_andn2_b64 %[open], vcc, exec\n"
@@ -153,8 +149,7 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     "v_fmac_f32_e32 %[az], %[f], %[dz]\n"                                              \
     CNT
 #define BH_FETCH(NX, OTHER)                                                            \
-    "s_lshl_b32 %[t], " NX ", 5\n"                                                     \
-    "s_load_dwordx8 " OTHER ", %[nb], %[t]\n"
+    "s_load_dwordx8 " OTHER ", %[nb], " NX "\n"
 
 // One source of a leaf opened in the assembly loop, in the order of
 // leaf_pair(): X, Y, Z, M name the source's scalar registers.  GUARD is the
@@ -224,7 +219,7 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     "s_mov_b64 exec, %[save]\n"                                                        \
     "s_branch BH_A%=\n"                                                                \
     "BH_OA%=:\n"                                                                       \
-    "s_bitcmp1_b32 s39, 8\n"                                                           \
+    "s_bitcmp1_b32 s39, 31\n"                                                           \
     "s_cbranch_scc1 BH_KA%=\n"                                                         \
     "s_waitcnt lgkmcnt(0)\n"                                                           \
     BH_FETCH("%[off]", "s[40:47]")                                                     \
@@ -235,7 +230,7 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     "s_mov_b32 s38, %[off]\n"                                                          \
     "s_branch BH_B%=\n"                                                                \
     "BH_OB%=:\n"                                                                       \
-    "s_bitcmp1_b32 s47, 8\n"                                                           \
+    "s_bitcmp1_b32 s47, 31\n"                                                           \
     "s_cbranch_scc1 BH_KB%=\n"                                                         \
     "s_waitcnt lgkmcnt(0)\n"                                                           \
     BH_FETCH("%[off]", "s[32:39]")                                                     \
@@ -250,7 +245,7 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     BH_MONO("s35", CNT)                                                                \
     "BH_MA%=:\n"                                                                       \
     "s_mov_b64 exec, %[save]\n"                                                        \
-    "s_sub_u32 %[X], %[off], 1\n"                                                      \
+    "s_sub_u32 %[X], %[off], 32\n"                                                      \
     "s_mov_b32 %[first], s36\n"                                                        \
     "s_mov_b32 %[cnt], s37\n"                                                          \
     "s_mov_b32 %[skip], s38\n"                                                         \
@@ -294,7 +289,7 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     BH_MONO("s43", CNT)                                                                \
     "BH_MB%=:\n"                                                                       \
     "s_mov_b64 exec, %[save]\n"                                                        \
-    "s_sub_u32 %[X], %[off], 1\n"                                                      \
+    "s_sub_u32 %[X], %[off], 32\n"                                                      \
     "s_mov_b32 %[first], s44\n"                                                        \
     "s_mov_b32 %[cnt], s45\n"                                                          \
     "s_mov_b32 %[skip], s46\n"                                                         \
@@ -345,7 +340,7 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
         [save] "=&s"(save), [open] "=&s"(open), [le] "=&s"(le), [j] "=&s"(jj),          \
         [left] "=&s"(left)
 #define BH_RUN_INS                                                                     \
-    [nb] "s"(nb), [srclo] "s"(sb_lo), [srchi] "s"(sb_hi), [T0] "s"(T0_bits), [eps2] "v"(eps2v), [px] "v"(p.x),  \
+    [nb] "s"(nb), [srclo] "s"(sb_lo), [srchi] "s"(sb_hi), [eps2] "v"(eps2v), [px] "v"(p.x),  \
         [py] "v"(p.y), [pz] "v"(p.z), [wb] "s"(wb), [wbe] "s"(wbe)
 #define BH_RUN_CLOBBERS                                                                \
     "s16", "s17", "s18", "s19", "s20", "s21", "s22", "s23", "s24", "s25", "s26", "s27", \
@@ -370,14 +365,18 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
 // and the loop exit on every node, and it copied the accumulators several
 // times around every opened leaf.  The two rarer thresholds keep the compiled
 // loop.
-template <bool SOFT, bool SELF, bool COUNT, bool EXACT_T, bool ANY_MINE, bool FIXED_T = false>
+// ASM: the assembly loop over the walk records (wnodes), else the compiled
+// loop over the nodes with thresholds by ldexp.
+template <bool SOFT, bool SELF, bool COUNT, bool ASM, bool ANY_MINE>
 __device__ __attribute__((always_inline)) inline void walk_wave(
-    const Node *__restrict__ nodes, const float4 *__restrict__ src, uint32_t nn, float4 p,
-    uint32_t i, uint32_t wave_base, bool valid, float T0, uint32_t T0_bits, uint32_t T_step,
-    float eps2, float &ax, float &ay, float &az, float &pot, uint32_t &n_int)
+    const Node *__restrict__ nodes, const Node *__restrict__ wnodes,
+    const float4 *__restrict__ src, uint32_t nn, float4 p, uint32_t i, uint32_t wave_base,
+    bool valid, float T0, float eps2, float &ax, float &ay, float &az, float &pot,
+    uint32_t &n_int)
 {
-    const char *node_bytes = reinterpret_cast<const char *>(nodes);
-    // Lane state: a lane takes part at node X when rejoin <= X.  A lane that
+    const char *node_bytes = reinterpret_cast<const char *>(ASM ? wnodes : nodes);
+    // Lane state: a lane takes part at node X when rejoin <= X (both as byte
+    // offsets into the walk records in the assembly loop).  A lane that
     // uses a node whole sets rejoin = skip(node) and so sits out the node's
     // subtree; lanes that open a node keep theirs.  (The wave lands on every
     // such skip on its way out, so `<=` and `==` select the same lanes.)  After
@@ -396,7 +395,7 @@ __device__ __attribute__((always_inline)) inline void walk_wave(
             if (COUNT) n_int += (e - b) - ((SELF && i >= b && i < e) ? 1u : 0u);
         }
     };
-    if constexpr (!EXACT_T && !FIXED_T) {
+    if constexpr (ASM) {
         const uint64_t nb = (uint64_t)node_bytes;
         const uint32_t sb_lo = sgpr((uint32_t)(uint64_t)src);
         const uint32_t sb_hi = sgpr((uint32_t)((uint64_t)src >> 32));
@@ -445,9 +444,9 @@ __device__ __attribute__((always_inline)) inline void walk_wave(
             first = sgpr(first);
             cnt = sgpr(cnt);
             skip = sgpr(skip);
-            if (X >= nn) break;   // the end record
+            if (cnt == 0) break;   // the end record (every other leaf holds a source)
             open_leaf(first, first + cnt, eps2v);
-            X = skip;   // leave the leaf (skip == X + 1)
+            X = skip;   // leave the leaf (skip == X + 1, as a byte offset)
         }
         return;
     }
@@ -460,7 +459,7 @@ __device__ __attribute__((always_inline)) inline void walk_wave(
         const float cz = __uint_as_float(lo.z), m = __uint_as_float(mbits);
         const uint32_t skip = hi.z, meta = hi.w;
         const uint32_t level = node_level(meta);
-        const float T = EXACT_T ? ldexpf(T0, -2 * (int)level) : T0;
+        const float T = ldexpf(T0, -2 * (int)level);
         const float dx = cx - p.x, dy = cy - p.y, dz = cz - p.z;
         const float r2 = fmaf(dz, dz, fmaf(dy, dy, dx * dx));
         const uint64_t act_m = __ballot(rejoin <= X);
@@ -550,6 +549,8 @@ __device__ __attribute__((always_inline)) inline void walk_vote(
 // from tpos[c] as given.
 template <bool SOFT, bool SELF, bool COUNT, bool VOTE, bool UNSORTED>
 __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ nodes,
+                                                       const Node *__restrict__ wnodes,
+                                                       uint32_t wn_cap,
                                                        const float4 *__restrict__ src,
                                                        const float4 *__restrict__ tpos,
                                                        const uint32_t *__restrict__ tmap,
@@ -578,15 +579,17 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
     const float4 p = valid ? tpos[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     const double L = prm->L;
     const float T0 = (float)(L * L / ((double)theta * (double)theta));
+    // the assembly loop walks the per-call records (thresholds in place, any
+    // T0) while they exist and their byte offsets fit 32 bits; otherwise the
+    // compiled loop walks the nodes
+    const bool use_asm = nn < kAsmMaxNodes && nn < wn_cap;
+    // the warp vote: zero, inf and NaN thresholds are the same at every level
+    // (step 0); a normal T0 with T0 * 4^-21 normal steps the exponent by 2 per
+    // level; anything else takes ldexp
     const uint32_t T0_bits = sgpr(__float_as_uint(T0));
     const uint32_t T0_exp = (T0_bits >> 23) & 0xffu;
-    // zero, inf and NaN thresholds are the same at every level (step 0); a
-    // normal T0 with T0 * 4^-21 normal steps the exponent by 2 per level (the
-    // assembly loop); anything else takes ldexp (the compiled loop), and so
-    // does a tree whose byte offsets (32 B per node, the end record included)
-    // would not fit the assembly loop's 32-bit offsets
     const bool fixed = (T0_bits & 0x7fffffffu) == 0u || T0_exp == 255u;
-    const bool exact = !fixed && (T0_exp <= 44u || nn >= kAsmMaxNodes);
+    const bool exact = !fixed && T0_exp <= 44u;
     const uint32_t T_step = fixed ? 0u : (1u << 24);
 
     // wait for the target's position here: a first use inside the walk loop
@@ -604,18 +607,12 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
                                                           T0, T0_bits, T_step, eps2, ax, ay, az,
                                                           pot, n_int);
     } else {
-        if (fixed)
-            walk_wave<SOFT, SELF, COUNT, false, UNSORTED, true>(nodes, src, nn, p, i, wave_base,
-                                                                valid, T0, T0_bits, T_step, eps2,
-                                                                ax, ay, az, pot, n_int);
-        else if (exact)
-            walk_wave<SOFT, SELF, COUNT, true, UNSORTED>(nodes, src, nn, p, i, wave_base, valid, T0,
-                                                         T0_bits, T_step, eps2, ax, ay, az, pot,
-                                                         n_int);
+        if (use_asm)
+            walk_wave<SOFT, SELF, COUNT, true, UNSORTED>(nodes, wnodes, src, nn, p, i, wave_base,
+                                                         valid, T0, eps2, ax, ay, az, pot, n_int);
         else
-            walk_wave<SOFT, SELF, COUNT, false, UNSORTED>(nodes, src, nn, p, i, wave_base, valid,
-                                                          T0, T0_bits, T_step, eps2, ax, ay, az,
-                                                          pot, n_int);
+            walk_wave<SOFT, SELF, COUNT, false, UNSORTED>(nodes, wnodes, src, nn, p, i, wave_base,
+                                                          valid, T0, eps2, ax, ay, az, pot, n_int);
     }
 
     if (valid) out[slot] = make_float4(G * ax, G * ay, G * az, G * pot);
@@ -623,6 +620,32 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
         unsigned long long cnt = valid ? n_int : 0u;
         for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
         if (lane == 0) atomicAdd(count, cnt);
+    }
+}
+
+// The walk records of one call: per node X <= n_nodes (the end record
+// included) {com, mass, start, count, skip * 32, T | leaf << 31}, with the
+// opening threshold T = (L / theta)^2 4^-level by ldexp (exact wherever it is
+// representable, the value every walk form compares with) and the skip as a
+// byte offset, so the assembly loop uses both without arithmetic.  Written
+// only when the loop will use them (see k_walk).
+__global__ __launch_bounds__(256) void k_walk_nodes(const Node *__restrict__ nodes,
+                                                    const DevParams *__restrict__ prm,
+                                                    float theta, uint32_t wn_cap,
+                                                    Node *__restrict__ wnodes)
+{
+    if (prm->status != 0) return;
+    const uint32_t nn = prm->n_nodes;
+    if (!(nn < kAsmMaxNodes && nn < wn_cap)) return;
+    const double L = prm->L;
+    const float T0 = (float)(L * L / ((double)theta * (double)theta));
+    for (uint32_t X = blockIdx.x * blockDim.x + threadIdx.x; X <= nn; X += gridDim.x * blockDim.x) {
+        const uint4 lo = reinterpret_cast<const uint4 *>(&nodes[X])[0];
+        const uint4 hi = reinterpret_cast<const uint4 *>(&nodes[X])[1];
+        const float T = ldexpf(T0, -2 * (int)node_level(hi.w));
+        const uint32_t tb = (__float_as_uint(T) & 0x7fffffffu) | ((hi.w & kLeafBit) ? 0x80000000u : 0u);
+        reinterpret_cast<uint4 *>(&wnodes[X])[0] = lo;
+        reinterpret_cast<uint4 *>(&wnodes[X])[1] = make_uint4(hi.x, hi.y, hi.z << 5, tb);
     }
 }
 
@@ -644,7 +667,7 @@ void launch5(const WalkArgs &a, hipStream_t s)
 {
     const uint32_t grid = (a.n_targets + kWalkThreads - 1) / kWalkThreads;
     hipLaunchKernelGGL((k_walk<SOFT, SELF, COUNT, VOTE, UNSORTED>), dim3(grid), dim3(kWalkThreads),
-                       0, s, a.nodes, a.src, a.tpos, a.tmap, a.prm, a.n_targets, a.theta, a.G,
+                       0, s, a.nodes, a.wnodes, a.wn_cap, a.src, a.tpos, a.tmap, a.prm, a.n_targets, a.theta, a.G,
                        a.eps * a.eps, a.out, a.count);
 }
 
@@ -677,6 +700,11 @@ void launch1(const WalkArgs &a, hipStream_t s)
 void launch_walk(const WalkArgs &a, hipStream_t s)
 {
     if (a.n_targets == 0) return;
+    if (!a.vote && a.wn_cap > 0) {
+        const uint32_t blocks = (uint32_t)std::min<uint64_t>((a.wn_cap + 255) / 256, 2048);
+        hipLaunchKernelGGL(k_walk_nodes, dim3(blocks), dim3(256), 0, s, a.nodes, a.prm, a.theta,
+                           a.wn_cap, a.wnodes);
+    }
     // Plummer softening with eps^2 > 0 never meets r^2 + eps^2 == 0
     if (a.eps * a.eps > 0.f) launch1<true>(a, s); else launch1<false>(a, s);
 }

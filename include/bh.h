@@ -269,12 +269,13 @@ bh_status bh_diagnostics(bh_ctx *ctx, const float *pos_mass, const float *vel,
  * capture, tight serving loops, harnesses that forbid hipMalloc): one
  * self-gravity step, bh_build followed by bh_gravity with targets == NULL,
  * with no context.  Every scratch buffer (keys, sort buffers, the sorted
- * sources, the tree) lives in one static device array of the library, 32 MiB
- * on each GPU the library runs on, held until the process ends.  The tree's
- * node capacity is the bound bits * floor(n / (leaf_cap + 1)) + n + 1, which
- * no input can exceed, so a step fits when about 150 bytes per source (63-bit
- * keys, leaf_cap 16; about 450 with leaf_cap 1) fit the array: up to roughly
- * 220000 sources at leaf_cap 16, 75000 at leaf_cap 1.
+ * sources, the tree and its walk records) lives in one static device array
+ * of the library, 64 MiB on each GPU the library runs on, held until the
+ * process ends.  The tree's node capacity is the bound
+ * bits * floor(n / (leaf_cap + 1)) + n + 1, which no input can exceed, so a
+ * step fits when about 220 bytes per source (63-bit keys, leaf_cap 16; about
+ * 820 with leaf_cap 1) fit the array: up to roughly 300000 sources at
+ * leaf_cap 16, 82000 at leaf_cap 1.
  *   src_pos_mass  device, n float4 rows (x, y, z, m), 16-byte aligned.
  *   params        key_bits, leaf_cap and key_curve as for bh_create
  *                 (node_capacity and reserved must be 0); NULL = 63-bit

@@ -60,13 +60,13 @@ def test_static_step_limits_and_arguments():
     import barnes_hut_tree_amd as bh
     L = bh.load_library()
     s = bh._stream()
-    p = torch.from_numpy(W.uniform_cube(80000, seed=43)).cuda()
+    p = torch.from_numpy(W.uniform_cube(90000, seed=43)).cuda()
     out = torch.empty_like(p)
     P = lambda kb, B, cap=0, curve=0, res=0: ctypes.byref(bh._Params(kb, B, cap, curve, res))  # noqa: E731
     sp, op = ctypes.c_void_p(p.data_ptr()), ctypes.c_void_p(out.data_ptr())
-    # 80000 sources at leaf capacity 1 need more than the static array
-    assert L.bh_gravity_static(sp, 80000, P(63, 1), 0.5, 1.0, 0.0, op, s) == bh.BH_ERR_CAPACITY
-    assert L.bh_gravity_static(sp, 80000, P(63, 16), 0.5, 1.0, 0.0, op, s) == bh.BH_OK
+    # 90000 sources at leaf capacity 1 need more than the static array
+    assert L.bh_gravity_static(sp, 90000, P(63, 1), 0.5, 1.0, 0.0, op, s) == bh.BH_ERR_CAPACITY
+    assert L.bh_gravity_static(sp, 90000, P(63, 16), 0.5, 1.0, 0.0, op, s) == bh.BH_OK
     torch.cuda.synchronize()
     assert torch.all(torch.isfinite(out))
     assert L.bh_gravity_static(sp, 100, P(63, 16, cap=1000), 0.5, 1.0, 0.0, op, s) == \
