@@ -241,6 +241,11 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     "s_mov_b32 s46, %[off]\n"                                                          \
     "s_branch BH_A%=\n"                                                                \
     "BH_KA%=:\n"                                                                       \
+    "s_lshl_b32 s48, s36, 4\n"                                                           \
+    "s_lshr_b32 s49, s36, 28\n"                                                          \
+    "s_add_u32 s48, s48, %[srclo]\n"                                                   \
+    "s_addc_u32 s49, s49, %[srchi]\n"                                                  \
+    "s_load_dwordx16 s[16:31], s[48:49], 0x0\n"                                        \
     "s_cbranch_execz BH_MA%=\n"                                                        \
     BH_MONO("s35", CNT)                                                                \
     "BH_MA%=:\n"                                                                       \
@@ -260,13 +265,14 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     "BH_LNA%=:\n"                                                                      \
     "s_and_saveexec_b64 %[save], %[open]\n"                                            \
     "s_mov_b32 %[j], %[first]\n"                                                       \
+    "s_branch BH_LFA%=\n"                                                               \
     "BH_LTA%=:\n"                                                                      \
     "s_lshl_b32 s48, %[j], 4\n"                                                        \
     "s_lshr_b32 s49, %[j], 28\n"                                                       \
     "s_add_u32 s48, s48, %[srclo]\n"                                                   \
     "s_addc_u32 s49, s49, %[srchi]\n"                                                  \
-    "s_waitcnt lgkmcnt(0)\n"                                                           \
     "s_load_dwordx16 s[16:31], s[48:49], 0x0\n"                                        \
+    "BH_LFA%=:\n"                                                                      \
     "s_load_dwordx8 s[32:39], s[48:49], 0x40\n"                                        \
     "s_sub_u32 %[left], %[le], %[j]\n"                                                 \
     "s_waitcnt lgkmcnt(0)\n"                                                           \
@@ -285,6 +291,11 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     "s_mov_b32 s38, %[skip]\n"                                                         \
     "s_branch BH_B%=\n"                                                                \
     "BH_KB%=:\n"                                                                       \
+    "s_lshl_b32 s48, s44, 4\n"                                                           \
+    "s_lshr_b32 s49, s44, 28\n"                                                          \
+    "s_add_u32 s48, s48, %[srclo]\n"                                                   \
+    "s_addc_u32 s49, s49, %[srchi]\n"                                                  \
+    "s_load_dwordx16 s[16:31], s[48:49], 0x0\n"                                        \
     "s_cbranch_execz BH_MB%=\n"                                                        \
     BH_MONO("s43", CNT)                                                                \
     "BH_MB%=:\n"                                                                       \
@@ -304,13 +315,14 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     "BH_LNB%=:\n"                                                                      \
     "s_and_saveexec_b64 %[save], %[open]\n"                                            \
     "s_mov_b32 %[j], %[first]\n"                                                       \
+    "s_branch BH_LFB%=\n"                                                               \
     "BH_LTB%=:\n"                                                                      \
     "s_lshl_b32 s48, %[j], 4\n"                                                        \
     "s_lshr_b32 s49, %[j], 28\n"                                                       \
     "s_add_u32 s48, s48, %[srclo]\n"                                                   \
     "s_addc_u32 s49, s49, %[srchi]\n"                                                  \
-    "s_waitcnt lgkmcnt(0)\n"                                                           \
     "s_load_dwordx16 s[16:31], s[48:49], 0x0\n"                                        \
+    "BH_LFB%=:\n"                                                                      \
     "s_load_dwordx8 s[40:47], s[48:49], 0x40\n"                                        \
     "s_sub_u32 %[left], %[le], %[j]\n"                                                 \
     "s_waitcnt lgkmcnt(0)\n"                                                           \
