@@ -454,6 +454,18 @@ def main():
     import barnes_hut_tree_amd as bh
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_calibration_mib:
+        nbytes = args.copy_calibration_mib << 20
+        a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": nbytes, "copy_calibration_bytes_written":
+                          nbytes, "copies": 3}), file=sys.stderr, flush=True)
+        del a, b
+
     if args.sweep:
         theta_sweep(args)
         return
@@ -470,18 +482,6 @@ def main():
     if args.build_only:
         build_only(args)
         return
-
-    if args.copy_calibration_mib:
-        nbytes = args.copy_calibration_mib << 20
-        a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
-        b = torch.empty_like(a)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes_read": nbytes, "copy_calibration_bytes_written":
-                          nbytes, "copies": 3}), file=sys.stderr, flush=True)
-        del a, b
 
     p, prm, wname = make_workload(args.workload)
     if args.theta is not None:
