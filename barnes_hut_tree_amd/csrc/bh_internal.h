@@ -43,7 +43,7 @@ __host__ __device__ inline D4 operator-(D4 a, D4 b) { return D4{a.m - b.m, a.x -
 // `wrapped` in the totals entry when the whole tree has 2^32 nodes or more.
 struct alignas(16) TileScan {
     D4 sums;
-    uint32_t nodes, wrapped, pad[2];
+    uint32_t nodes, wrapped, leaves, pad;
 };
 
 // Pre-order node record; the public bh_node has the same layout.
@@ -128,12 +128,14 @@ uint32_t build_blocks(uint32_t n);
 // Device scratch of the tree build (owned by the context).
 struct BuildScratch {
     uint16_t *dc;           // per position: d + 1 (low byte), nodes starting there (high byte)
-    uint32_t *tile_counts;  // per tile: nodes starting in the tile
+    uint2 *tile_counts;     // per tile: nodes and leaves starting in the tile
     D4 *tile_sums;          // per tile: particle sums
     TileScan *chunk_tot;    // per chunk of tiles: node count and particle sums
     TileScan *tile_scan;    // per chunk: exclusive prefix; [n_chunks] = totals
-    uint32_t *first_node;   // per position (and n): pre-order index of the first node there
-    D4 *P;                  // per position (and n): prefix sums of (m, m (x - lo))
+    uint2 *first_node;      // per leaf start (and n): pre-order index of the first node
+                            // there, and the number of leaves before it
+    D4 *P;                  // per leaf in pre-order (and one past the last): prefix sums
+                            // of (m, m (x - lo)) over the sources before the leaf
 };
 void build_tree(const uint64_t *keys_sorted, const float4 *spos, uint32_t n, int bits,
                 int leaf_cap, uint64_t node_capacity, BuildScratch &w, Node *nodes,

@@ -101,22 +101,25 @@ __global__ __launch_bounds__(kBuildThreads) void k_count(const uint64_t *__restr
                                                          const float4 *__restrict__ spos,
                                                          uint32_t n, int bits, int B,
                                                          uint16_t *__restrict__ dc,
-                                                         uint32_t *__restrict__ block_counts,
+                                                         uint2 *__restrict__ block_counts,
                                                          D4 *__restrict__ block_sums,
                                                          const DevParams *__restrict__ prm)
 {
     __shared__ int8_t sd[kBuildTile + 2 * kMaxLeafCap + 2];
-    __shared__ uint32_t lc;
+    __shared__ uint32_t lc, ll;
     const int W = WAVE_ROWS ? 64 : B;   // window margin either side of the tile
     const int64_t t0 = (int64_t)blockIdx.x * kBuildTile;
     const int64_t w0 = t0 - W;   // window covers positions [t0 - W, t0 + tile + W]
     const int wlen = kBuildTile + 2 * W + 1;
     for (int k = threadIdx.x; k < wlen; k += kBuildThreads)
         sd[k] = (int8_t)d_at(keys, w0 + k, n, bits);
-    if (threadIdx.x == 0) lc = 0;
+    if (threadIdx.x == 0) {
+        lc = 0;
+        ll = 0;
+    }
     __syncthreads();
 
-    uint32_t my_nodes = 0;
+    uint32_t my_nodes = 0, my_leaves = 0;
     for (int k = 0; k < kBuildTile / kBuildThreads; ++k) {
         const int off = k * kBuildThreads + threadIdx.x;
         const int64_t a = t0 + off;
@@ -191,10 +194,17 @@ __global__ __launch_bounds__(kBuildThreads) void k_count(const uint64_t *__restr
         }
         const int c = leaf_start ? ell - da : 0;
         my_nodes += (uint32_t)c;
+        my_leaves += c > 0 ? 1u : 0u;
         if (valid) dc[a] = (uint16_t)((da + 1) | (c << 8));
     }
-    for (int o = 32; o > 0; o >>= 1) my_nodes += __shfl_xor(my_nodes, o, 64);
-    if ((threadIdx.x & 63) == 0) atomicAdd(&lc, my_nodes);
+    for (int o = 32; o > 0; o >>= 1) {
+        my_nodes += __shfl_xor(my_nodes, o, 64);
+        my_leaves += __shfl_xor(my_leaves, o, 64);
+    }
+    if ((threadIdx.x & 63) == 0) {
+        atomicAdd(&lc, my_nodes);
+        atomicAdd(&ll, my_leaves);
+    }
     __syncthreads();
     // the tile's particle sums, each thread over 4 consecutive positions in
     // the order the emit kernel scans them
@@ -213,7 +223,7 @@ __global__ __launch_bounds__(kBuildThreads) void k_count(const uint64_t *__restr
             D4 tot = wsum[0];
             for (int w = 1; w < kBuildThreads / 64; ++w) tot = tot + wsum[w];
             block_sums[blockIdx.x] = tot;
-            block_counts[blockIdx.x] = lc;
+            block_counts[blockIdx.x] = make_uint2(lc, ll);
         }
     }
 }
@@ -228,7 +238,15 @@ __device__ inline uint32_t wave_incl_scan(uint32_t v)
     return v;
 }
 
-// The exclusive scan over tiles of (node count, particle sums) is split so
+__device__ inline uint2 wave_incl_scan_u2(uint2 v)
+{
+    return make_uint2(wave_incl_scan(v.x), wave_incl_scan(v.y));
+}
+
+__device__ inline uint2 operator+(uint2 a, uint2 b) { return make_uint2(a.x + b.x, a.y + b.y); }
+__device__ inline uint2 operator-(uint2 a, uint2 b) { return make_uint2(a.x - b.x, a.y - b.y); }
+
+// The exclusive scan over tiles of (node count, leaf count, particle sums) is split so
 // that every access is coalesced and no single workgroup walks all tiles.
 // Tiles are grouped in chunks of chunk_tiles(n_tiles) consecutive tiles (a
 // multiple of 64, at most kTileScanThreads chunks).  k_chunk_totals reduces
@@ -236,12 +254,12 @@ __device__ inline uint32_t wave_incl_scan(uint32_t v)
 // one workgroup, scans the chunk totals: out[c] = the sum of the chunks
 // before c, out[n_chunks] = the totals.  Each emit workgroup then adds the
 // tiles before its own within its chunk.
-__device__ inline void wave_sum_tiles(const uint32_t *__restrict__ counts,
+__device__ inline void wave_sum_tiles(const uint2 *__restrict__ counts,
                                       const D4 *__restrict__ sums, uint32_t b, uint32_t e,
-                                      uint32_t &c, D4 &m)
+                                      uint2 &c, D4 &m)
 {
     const uint32_t lane = threadIdx.x & 63;
-    c = 0;
+    c = make_uint2(0u, 0u);
     m = D4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll 1
     for (uint32_t t = b + lane; t < e; t += 64) {
@@ -249,24 +267,25 @@ __device__ inline void wave_sum_tiles(const uint32_t *__restrict__ counts,
         m = m + sums[t];
     }
     for (int o = 32; o > 0; o >>= 1) {
-        c += __shfl_xor(c, o, 64);
+        c = c + make_uint2(__shfl_xor(c.x, o, 64), __shfl_xor(c.y, o, 64));
         m = m + D4{__shfl_xor(m.m, o, 64), __shfl_xor(m.x, o, 64), __shfl_xor(m.y, o, 64),
                    __shfl_xor(m.z, o, 64)};
     }
 }
 
 // one wave per chunk
-__global__ __launch_bounds__(64) void k_chunk_totals(const uint32_t *__restrict__ counts,
+__global__ __launch_bounds__(64) void k_chunk_totals(const uint2 *__restrict__ counts,
                                                      const D4 *__restrict__ sums,
                                                      uint32_t n_tiles, uint32_t chunk,
                                                      TileScan *__restrict__ tot)
 {
     const uint32_t k = blockIdx.x;
-    uint32_t c;
+    uint2 c;
     D4 m;
     wave_sum_tiles(counts, sums, k * chunk, min(n_tiles, (k + 1) * chunk), c, m);
     if (threadIdx.x == 0) {
-        tot[k].nodes = c;
+        tot[k].nodes = c.x;
+        tot[k].leaves = c.y;
         tot[k].sums = m;
     }
 }
@@ -276,16 +295,16 @@ __global__ __launch_bounds__(kTileScanThreads) void k_scan_chunks(
 {
     constexpr int kWavesScan = kTileScanThreads / 64;
     __shared__ D4 wsum[kWavesScan + 1];
-    __shared__ uint32_t wcnt[kWavesScan + 1];
+    __shared__ uint2 wcnt[kWavesScan + 1];
     __shared__ unsigned long long wide[kWavesScan];
     const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t k = threadIdx.x;
-    const uint32_t c = k < n_chunks ? tot[k].nodes : 0u;
+    const uint2 c = k < n_chunks ? make_uint2(tot[k].nodes, tot[k].leaves) : make_uint2(0u, 0u);
     const D4 m = k < n_chunks ? tot[k].sums : D4{0.0, 0.0, 0.0, 0.0};
-    const uint32_t ic = wave_incl_scan(c);
+    const uint2 ic = wave_incl_scan_u2(c);
     const D4 im = wave_incl_scan_d4(m);
     // the same node total in 64 bits, to detect a 32-bit wrap
-    unsigned long long c64 = c;
+    unsigned long long c64 = c.x;
     for (int o = 32; o > 0; o >>= 1) c64 += __shfl_xor(c64, o, 64);
     if (lane == 63) {
         wcnt[wave] = ic;
@@ -295,9 +314,9 @@ __global__ __launch_bounds__(kTileScanThreads) void k_scan_chunks(
     __syncthreads();
     // the first wave turns the wave totals into exclusive prefixes
     if (wave == 0) {
-        const uint32_t c2 = lane < kWavesScan ? wcnt[lane] : 0u;
+        const uint2 c2 = lane < kWavesScan ? wcnt[lane] : make_uint2(0u, 0u);
         const D4 m2 = lane < kWavesScan ? wsum[lane] : D4{0.0, 0.0, 0.0, 0.0};
-        const uint32_t ic2 = wave_incl_scan(c2);
+        const uint2 ic2 = wave_incl_scan_u2(c2);
         const D4 im2 = wave_incl_scan_d4(m2);
         if (lane < kWavesScan) {
             wcnt[lane] = ic2 - c2;
@@ -309,52 +328,60 @@ __global__ __launch_bounds__(kTileScanThreads) void k_scan_chunks(
         }
     }
     __syncthreads();
-    const uint32_t rc = ic - c + wcnt[wave], tc = wcnt[kWavesScan];
+    const uint2 rc = (ic - c) + wcnt[wave], tc = wcnt[kWavesScan];
     const D4 rm = (im - m) + wsum[wave], tm = wsum[kWavesScan];
     if (k < n_chunks) {
-        out[k].nodes = rc;
+        out[k].nodes = rc.x;
+        out[k].leaves = rc.y;
         out[k].sums = rm;
     }
     if (k == 0) {
         unsigned long long all = 0;
         for (int w = 0; w < kWavesScan; ++w) all += wide[w];
-        out[n_chunks].nodes = tc;
+        out[n_chunks].nodes = tc.x;
+        out[n_chunks].leaves = tc.y;
         out[n_chunks].wrapped = all > 0xffffffffull ? 1u : 0u;
         out[n_chunks].sums = tm;
     }
 }
 
-// chunk_pref: the exclusive scan over chunks of the tiles' node counts and
-// particle sums ([n_chunks] = the totals); the tiles before this one in its
-// chunk are added here.
+// chunk_pref: the exclusive scan over chunks of the tiles' node and leaf
+// counts and particle sums ([n_chunks] = the totals); the tiles before this
+// one in its chunk are added here.  Outputs: per node its start, the number
+// of leaves before it in pre-order and its level/leaf word, in the second
+// half of its record (the ranges kernel completes the record); per leaf the
+// prefix P of the particle sums at its start, stored by leaf number so the
+// ranges kernel reads it in order; per leaf start position the first node
+// there and its leaf number (for the ends of internal cells).
 __global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restrict__ dc,
                                                         const float4 *__restrict__ spos, uint32_t n,
-                                                        const uint32_t *__restrict__ tile_counts,
+                                                        const uint2 *__restrict__ tile_counts,
                                                         const D4 *__restrict__ tile_sums,
                                                         const TileScan *__restrict__ chunk_pref,
                                                         uint32_t n_tiles, uint32_t chunk,
                                                         uint64_t cap,
-                                                        uint32_t *__restrict__ first_node,
+                                                        uint2 *__restrict__ first_node,
                                                         D4 *__restrict__ P,
                                                         Node *__restrict__ nodes,
                                                         DevParams *__restrict__ prm)
 {
     constexpr int per = kBuildTile / kBuildThreads;  // consecutive positions per thread
     static_assert(per == 4, "the LDS layout below assumes 4 positions per thread");
-    __shared__ uint32_t wtot[kBuildThreads / 64];
+    __shared__ uint2 wtot[kBuildThreads / 64];
     __shared__ D4 wsum[kBuildThreads / 64];
-    __shared__ uint32_t tile_nodes;
+    __shared__ uint32_t tile_nodes, tile_leaves;
     __shared__ D4 tile_mass;
     const uint32_t blk = blockIdx.x;
     const uint32_t n_chunks = (n_tiles + chunk - 1) / chunk;
     const uint32_t total = chunk_pref[n_chunks].nodes;   // all nodes
     if (threadIdx.x < 64) {
         const uint32_t c0 = blk / chunk;
-        uint32_t c;
+        uint2 c;
         D4 m;
         wave_sum_tiles(tile_counts, tile_sums, c0 * chunk, blk, c, m);
         if (threadIdx.x == 0) {
-            tile_nodes = chunk_pref[c0].nodes + c;
+            tile_nodes = chunk_pref[c0].nodes + c.x;
+            tile_leaves = chunk_pref[c0].leaves + c.y;
             tile_mass = chunk_pref[c0].sums + m;
         }
     }
@@ -366,6 +393,7 @@ __global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restri
     // (fn and sdc are also accessed as 16- and 8-byte words)
     __shared__ double2 mom[kBuildThreads * 9];                // moments, then the prefix P
     __shared__ __attribute__((aligned(16))) uint32_t fn[kBuildTile];   // first node per position
+    __shared__ __attribute__((aligned(16))) uint32_t flr[kBuildTile];  // leaves before it
     __shared__ __attribute__((aligned(16))) uint16_t sdc[kBuildTile];
     auto unit = [](int j) { return (j >> 2) * 9 + (j & 3) * 2; };
     const int64_t t0 = (int64_t)blk * kBuildTile;
@@ -384,7 +412,7 @@ __global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restri
     const int64_t a0 = t0 + j0;
     int dd[per], cc[per];
     D4 mk[per];
-    uint32_t s = 0;
+    uint32_t s = 0, sl = 0;
     D4 ms = {0.0, 0.0, 0.0, 0.0};
     {
         const uint2 w = reinterpret_cast<const uint2 *>(sdc)[threadIdx.x];
@@ -393,32 +421,36 @@ __global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restri
             dd[k] = (int)(v4[k] & 0xffu) - 1;
             cc[k] = (int)(v4[k] >> 8);
             s += cc[k];
+            sl += cc[k] > 0 ? 1u : 0u;
             const double2 u0 = mom[unit(j0 + k)], u1 = mom[unit(j0 + k) + 1];
             mk[k] = D4{u0.x, u0.y, u1.x, u1.y};
             ms = ms + mk[k];
         }
     }
     const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t incl = wave_incl_scan(s);
+    const uint2 incl = wave_incl_scan_u2(make_uint2(s, sl));
     const D4 mincl = wave_incl_scan_d4(ms);
     if (lane == 63) {
         wtot[wave] = incl;
         wsum[wave] = mincl;
     }
     __syncthreads();
-    uint32_t run = tile_nodes;
+    uint32_t run = tile_nodes, lrun = tile_leaves;
     D4 mrun = tile_mass;
     for (uint32_t w = 0; w < wave; ++w) {
-        run += wtot[w];
+        run += wtot[w].x;
+        lrun += wtot[w].y;
         mrun = mrun + wsum[w];
     }
-    run += incl - s;
+    run += incl.x - s;
+    lrun += incl.y - sl;
     mrun = mrun + (mincl - ms);
 
-    uint32_t fn4[per];
+    uint32_t fn4[per], lr4[per];
     for (int k = 0; k < per; ++k) {
         const int64_t a = a0 + k;
         fn4[k] = run;
+        lr4[k] = lrun;
         mom[unit(j0 + k)] = make_double2(mrun.m, mrun.x);
         mom[unit(j0 + k) + 1] = make_double2(mrun.y, mrun.z);
         mrun = mrun + mk[k];
@@ -426,30 +458,34 @@ __global__ __launch_bounds__(kBuildThreads) void k_emit(const uint16_t *__restri
             for (int j = 0; j < cc[k]; ++j) {
                 const int l = dd[k] + 1 + j;
                 const uint32_t X = run + j;
-                if (X < cap) {
-                    nodes[X].start = (uint32_t)a;
-                    nodes[X].meta = (uint32_t)l | (j == cc[k] - 1 ? kLeafBit : 0u);
-                }
+                if (X < cap)
+                    reinterpret_cast<uint4 *>(&nodes[X])[1] =
+                        make_uint4((uint32_t)a, lrun, 0u,
+                                   (uint32_t)l | (j == cc[k] - 1 ? kLeafBit : 0u));
             }
         }
         run += cc[k];
+        lrun += cc[k] > 0 ? 1u : 0u;
     }
     reinterpret_cast<uint4 *>(fn)[threadIdx.x] = make_uint4(fn4[0], fn4[1], fn4[2], fn4[3]);
+    reinterpret_cast<uint4 *>(flr)[threadIdx.x] = make_uint4(lr4[0], lr4[1], lr4[2], lr4[3]);
     __syncthreads();
     // coalesced stores; nodes start and end only where a leaf starts, so the
-    // prefix and the first-node index are needed only there
+    // prefix and the first node are needed only there (the prefix stored at
+    // the leaf's number, dense in the leaves)
     for (int k = 0; k < per; ++k) {
         const int j = k * kBuildThreads + threadIdx.x;
         const int64_t a = t0 + j;
         if (a < (int64_t)n && (sdc[j] >> 8) != 0) {
-            first_node[a] = fn[j];
+            first_node[a] = make_uint2(fn[j], flr[j]);
             const double2 u0 = mom[unit(j)], u1 = mom[unit(j) + 1];
-            P[a] = D4{u0.x, u0.y, u1.x, u1.y};
+            P[flr[j]] = D4{u0.x, u0.y, u1.x, u1.y};
         }
     }
     if (blk == n_tiles - 1 && threadIdx.x == 0) {
-        first_node[n] = total;
-        P[n] = chunk_pref[n_chunks].sums;
+        const uint32_t leaves = chunk_pref[n_chunks].leaves;
+        first_node[n] = make_uint2(total, leaves);
+        P[leaves] = chunk_pref[n_chunks].sums;
     }
     if (blk == 0 && threadIdx.x == 0) {
         prm->n_nodes = total;
@@ -530,12 +566,14 @@ __device__ inline uint32_t cell_end(const uint64_t *__restrict__ keys, uint32_t 
 
 // Per node: its particle range, skip, mass and centre of mass, written as one
 // 32-byte record.  A leaf ends where the next node in pre-order starts (its
-// skip is the next node); an internal cell's end is searched in the keys.
+// skip is the next node, and the next leaf's prefix closes its sums); an
+// internal cell's end is searched in the keys, and the first node at the end
+// gives its skip and the leaf whose prefix closes its sums.
 __global__ __launch_bounds__(256) void k_ranges(const uint64_t *__restrict__ keys,
                                                 const float4 *__restrict__ spos,
                                                 const D4 *__restrict__ P, uint32_t n,
                                                 int bits, uint64_t cap,
-                                                const uint32_t *__restrict__ first_node,
+                                                const uint2 *__restrict__ first_node,
                                                 Node *__restrict__ nodes,
                                                 const DevParams *__restrict__ prm)
 {
@@ -549,14 +587,23 @@ __global__ __launch_bounds__(256) void k_ranges(const uint64_t *__restrict__ key
     }
     for (uint32_t X = blockIdx.x * blockDim.x + threadIdx.x; X < nn; X += gridDim.x * blockDim.x) {
         const uint4 rec = reinterpret_cast<const uint4 *>(&nodes[X])[1];
-        const uint32_t a = rec.x, meta = rec.w;
+        const uint32_t a = rec.x, lr = rec.y, meta = rec.w;
         const int l = (int)node_level(meta);
         const bool leaf = (meta & kLeafBit) != 0;
-        const D4 pa = P[a];
-        const uint32_t e = leaf ? (X + 1 < nn ? nodes[X + 1].start : n)
-                                : cell_end(keys, n, a, 3 * (bits - l));
-        const uint32_t skip = leaf ? X + 1 : first_node[e];
-        const D4 sum = P[e] - pa;
+        const D4 pa = P[lr];
+        uint32_t e, skip, le;
+        if (leaf) {
+            // the next record's start is rewritten with the same value
+            e = X + 1 < nn ? nodes[X + 1].start : n;
+            skip = X + 1;
+            le = lr + 1;
+        } else {
+            e = cell_end(keys, n, a, 3 * (bits - l));
+            const uint2 f = first_node[e];
+            skip = f.x;
+            le = f.y;
+        }
+        const D4 sum = P[le] - pa;
         float4 com;
         if (sum.m != 0.0) {
             com = make_float4((float)(prm->lo[0] + sum.x / sum.m),
@@ -644,18 +691,18 @@ void build_tree(const uint64_t *keys_sorted, const float4 *spos, uint32_t n, int
     const uint32_t chunk = chunk_tiles(tiles);
     const uint32_t n_chunks = (tiles + chunk - 1) / chunk;
     hipLaunchKernelGGL(k_chunk_totals, dim3(n_chunks), dim3(64), 0, s,
-                       (const uint32_t *)w.tile_counts, (const D4 *)w.tile_sums, tiles, chunk,
+                       (const uint2 *)w.tile_counts, (const D4 *)w.tile_sums, tiles, chunk,
                        w.chunk_tot);
     hipLaunchKernelGGL(k_scan_chunks, dim3(1), dim3(kTileScanThreads), 0, s,
                        (const TileScan *)w.chunk_tot, n_chunks, w.tile_scan);
     hipLaunchKernelGGL(k_emit, dim3(tiles), dim3(kBuildThreads), 0, s, (const uint16_t *)w.dc, spos,
-                       n, (const uint32_t *)w.tile_counts, (const D4 *)w.tile_sums,
+                       n, (const uint2 *)w.tile_counts, (const D4 *)w.tile_sums,
                        (const TileScan *)w.tile_scan, tiles, chunk, node_capacity, w.first_node,
                        w.P, nodes, prm);
     // about one node per thread: n / 2 threads (a tree of leaf capacity 16
     // has about n / 3 nodes; the grid-stride loop covers any excess)
     hipLaunchKernelGGL(k_ranges, dim3(grid_for(n / 2 + 1, 65535)), dim3(256), 0, s, keys_sorted, spos,
-                       (const D4 *)w.P, n, bits, node_capacity, (const uint32_t *)w.first_node,
+                       (const D4 *)w.P, n, bits, node_capacity, (const uint2 *)w.first_node,
                        nodes, (const DevParams *)prm);
 }
 
