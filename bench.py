@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "ms per gravity step + interactions/s at N=2^20, θ=0.5, fp32 (1 GPU)"
 FLOPS_PER_INTERACTION = 20
 FP32_PEAK_TFLOPS = 157.3
+HBM_PEAK_BYTES = 8e12
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -48,6 +49,18 @@ def make_workload(name):
         n = 1 << int(name[len("uniform_2p"):])
         return W.uniform_box(n, seed=5), dict(theta=0.5, G=1.0, eps=1e-3), "uniform_n%d" % n
     raise SystemExit("unknown workload " + name)
+
+
+def build_alg_bytes(n, n_nodes, n_leaves, key_bits):
+    """Algorithmic HBM bytes of one bh_build over n sources giving n_nodes
+    nodes and n_leaves leaves: bounding box 16n read; keys 16n read and 12n
+    written; per sort pass an 8n histogram read and a 12n + 12n scatter, the
+    last pass also gathering the 16-byte rows (16n + 16n); count 26n read and
+    2n written; emit 18n read, 16 bytes per node and 40 per leaf written;
+    ranges 84 bytes read and 32 written per node."""
+    passes = (key_bits + 7) // 8
+    return (16 * n + 28 * n + passes * 32 * n + 32 * n + 28 * n + 18 * n
+            + 16 * n_nodes + 40 * n_leaves + 116 * n_nodes)
 
 
 def walk_source_hash():
@@ -381,6 +394,128 @@ def sbh_compare(args):
                     "max_abs_err": [float(mx.mean()), float(mx.std())]}), flush=True)
 
 
+def cpu_oracle_row(p, q, prm, key_bits, leaf_cap, curve, budget_s=4.0, direct_targets=1 << 14):
+    """CPU baselines of one configuration, both from the oracle (fp64, OpenMP)
+    on the host: its tree build plus its walk for a random sample of the
+    targets sized to about budget_s seconds, scaled to all targets; and its
+    direct sum on direct_targets random targets, scaled to all targets."""
+    import numpy as np
+
+    import oracle
+    n = p.shape[0]
+    nt = n if q is None else q.shape[0]
+    rng = np.random.default_rng(98)
+    t0 = time.perf_counter()
+    tree = oracle.Tree(p, key_bits, leaf_cap, curve=curve)
+    t_build = time.perf_counter() - t0
+    m = min(nt, 1 << 11)
+    for _ in range(2):
+        which = np.sort(rng.choice(nt, m, replace=False))
+        t0 = time.perf_counter()
+        tree.gravity(prm["theta"], prm["G"], prm["eps"], targets=q, which=which)
+        t_walk = time.perf_counter() - t0
+        if t_walk >= budget_s / 4 or m == nt:
+            break
+        m = int(min(nt, m * budget_s / max(t_walk, 1e-3)))
+    del tree
+    md = min(nt, direct_targets)
+    which = np.sort(rng.choice(nt, md, replace=False))
+    t0 = time.perf_counter()
+    oracle.direct(p, prm["G"], prm["eps"], targets=q, which=which)
+    t_direct = time.perf_counter() - t0
+    return {"cpu_cores": oracle.threads(),
+            "cpu_bh_s": round(t_build + t_walk * nt / m, 3),
+            "cpu_bh_sample": "tree build %.2f s + walk of %d of %d targets %.2f s, scaled"
+                             % (t_build, m, nt, t_walk),
+            "cpu_direct_s": round(t_direct * nt / md, 3),
+            "cpu_direct_sample": "%d of %d targets %.2f s, scaled" % (md, nt, t_direct)}
+
+
+def configs_table(args):
+    """One JSON line per measured configuration: the 4096 uniform cube against
+    the direct sum; the 1M lattice shuffled and in lattice order; the Plummer
+    sphere at theta 0.3/0.5/0.7 in random and in Morton-sorted input order;
+    the 5M galaxy pair; the surface sources at M = 2^15, 2^17, 2^20 with grid
+    and box queries.  Per line: build and walk device ms (HIP events, mean of
+    --steps), interactions, the walk's fraction of the fp32 vector peak at 20
+    flops per interaction, the build's algorithmic bytes against 8 TB/s, and
+    the oracle's CPU times (tree walk and direct sum, both scaled from
+    samples) unless --no-cpu-baseline."""
+    import numpy as np
+    import torch
+
+    import barnes_hut_tree_amd as bh
+    import workloads as W
+
+    def morton_sorted(p):
+        t = bh.BarnesHut(p.shape[0], 0, args.key_bits, args.leaf_cap, curve="morton")
+        t.build(torch.from_numpy(p).cuda())
+        _, perm = t.keys()
+        t.close()
+        return np.ascontiguousarray(p[perm.cpu().numpy()])
+
+    rows = [("uniform_n4096", lambda: W.uniform_cube(4096, seed=1), None, [0.5], 1e-3),
+            ("lattice_n1000000_shuffled", lambda: W.lattice(100, shuffled=True, seed=2), None,
+             [0.5], 1e-3),
+            ("lattice_n1000000_lattice_order", lambda: W.lattice(100, shuffled=False, seed=2),
+             None, [0.5], 1e-3),
+            ("plummer_n1048576_random_order", lambda: W.plummer(1 << 20, seed=3), None,
+             [0.3, 0.5, 0.7], 0.01),
+            ("plummer_n1048576_morton_sorted", lambda: morton_sorted(W.plummer(1 << 20, seed=3)),
+             None, [0.3, 0.5, 0.7], 0.01),
+            ("galaxy_pair_n5000000", lambda: W.galaxy_pair()[0], None, [0.5], 0.02)]
+    for m in (1 << 15, 1 << 17, 1 << 20):
+        for qn, qf in (("grid100", W.grid_queries), ("uniform1e6", W.box_queries)):
+            rows.append(("surfaces_m%d_%s" % (m, qn),
+                         (lambda m=m: W.surface_sources(m, seed=10)), qf, [0.5], 0.0))
+    for wname, pf, qf, thetas, eps in rows:
+        p = pf()
+        q = None if qf is None else qf()
+        n = p.shape[0]
+        nt = n if q is None else q.shape[0]
+        src = torch.from_numpy(p).cuda()
+        tq = None if q is None else torch.from_numpy(q).cuda()
+        out = torch.empty((nt, 4), dtype=torch.float32, device="cuda")
+        tree = bh.BarnesHut(n, 0 if q is None else nt, args.key_bits, args.leaf_cap,
+                            curve=args.curve)
+        for th in thetas:
+            for _ in range(2):
+                tree.build(src)
+                tree.gravity(th, 1.0, eps, targets=tq, out=out)
+            stream = torch.cuda.current_stream()
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                   for _ in range(args.steps)]
+            for e in evs:
+                e[0].record(stream)
+                tree.build(src)
+                e[1].record(stream)
+                tree.gravity(th, 1.0, eps, targets=tq, out=out)
+                e[2].record(stream)
+            torch.cuda.synchronize()
+            tree.sync()
+            build_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs)
+            walk_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / len(evs)
+            inter = tree.count_interactions(th, eps, targets=tq)
+            nodes = tree.nodes()
+            nn = int(nodes.shape[0])
+            nl = int(((nodes[:, 7] & (1 << 8)) != 0).sum().item())
+            bbytes = build_alg_bytes(n, nn, nl, args.key_bits)
+            row = {"config": wname, "n_sources": n, "n_targets": nt, "theta": th, "eps": eps,
+                   "leaf_cap": args.leaf_cap, "key_curve": args.curve,
+                   "build_ms": round(build_ms, 4), "walk_ms": round(walk_ms, 4),
+                   "step_ms": round(build_ms + walk_ms, 4), "interactions": inter,
+                   "walk_alu_frac": round(FLOPS_PER_INTERACTION * inter / (walk_ms * 1e-3)
+                                          / (FP32_PEAK_TFLOPS * 1e12), 4),
+                   "nodes": nn, "leaves": nl, "build_alg_bytes": bbytes,
+                   "build_hbm_frac": round(bbytes / (build_ms * 1e-3) / HBM_PEAK_BYTES, 4)}
+            if not args.no_cpu_baseline:
+                row.update(cpu_oracle_row(p, q, dict(theta=th, G=1.0, eps=eps), args.key_bits,
+                                          args.leaf_cap, args.curve))
+            print(json.dumps(row), flush=True)
+        tree.close()
+        del src, tq, out
+
+
 def build_only(args):
     """bh_build alone (bounding box, keys, sort with the sorted-source gather,
     tree, centres of mass), timed with HIP events on the launch stream; the
@@ -437,6 +572,9 @@ def main():
                     help="time-step the 5M galaxy pair (kick-drift-kick, rebuild every step)")
     ap.add_argument("--sbh", action="store_true",
                     help="stochastic Barnes-Hut vs the tree walk at separate query points")
+    ap.add_argument("--configs", action="store_true",
+                    help="one line per measured configuration (uniform 4096, lattice, Plummer "
+                         "theta and input order, galaxy pair, surfaces M sweep)")
     ap.add_argument("--build-only", action="store_true",
                     help="time bh_build alone on the workload (keys, sort, tree, centres of "
                          "mass) and print its JSON line")
@@ -445,7 +583,7 @@ def main():
                          "the reference kernel for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: the walk has no multi-GPU path in this build "
+        print("bench.py runs on one GPU only: the walk has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
@@ -482,6 +620,9 @@ def main():
     if args.build_only:
         build_only(args)
         return
+    if args.configs:
+        configs_table(args)
+        return
 
     p, prm, wname = make_workload(args.workload)
     if args.theta is not None:
@@ -516,7 +657,9 @@ def main():
           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    evb = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     for k in range(args.steps):
+        evb[k].record(stream)
         tree.build(src)
         ev[k][0].record(stream)
         tree.gravity(prm["theta"], prm["G"], prm["eps"], out=out)
@@ -526,12 +669,25 @@ def main():
     tree.sync()
     ms_step = (t1 - t0) * 1e3 / args.steps
     walk_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    build_ms = sum(evb[k].elapsed_time(ev[k][0]) for k in range(args.steps)) / args.steps
+    nodes = tree.nodes()
+    n_nodes = int(nodes.shape[0])
+    n_leaves = int(((nodes[:, 7] & (1 << 8)) != 0).sum().item())
+    del nodes
+    build_bytes = build_alg_bytes(n, n_nodes, n_leaves, args.key_bits)
     value = interactions / (ms_step * 1e-3)
 
     achieved = FLOPS_PER_INTERACTION * interactions / (walk_ms * 1e-3) / 1e12
     roofline = {"bound": "alu", "achieved": round(achieved, 3), "peak": FP32_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK_TFLOPS, 4),
-                "traffic": read_traffic(wname, args.curve)}
+                "traffic": read_traffic(wname, args.curve),
+                # the build (all of bh_build's kernels): algorithmic bytes
+                # against the HBM peak
+                "build": {"bound": "hbm",
+                          "achieved": round(build_bytes / (build_ms * 1e-3) / 1e9, 1),
+                          "peak": HBM_PEAK_BYTES / 1e9, "unit": "GB/s",
+                          "frac": round(build_bytes / (build_ms * 1e-3) / HBM_PEAK_BYTES, 4),
+                          "bytes_per_call": build_bytes, "ms": round(build_ms, 4)}}
 
     rec = {
         "metric": METRIC, "value": value, "unit": "interactions/s", "n_gpus": 1,
