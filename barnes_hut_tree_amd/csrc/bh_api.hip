@@ -247,8 +247,8 @@ bh_status bh_create(bh_ctx **out, int64_t max_sources, int64_t max_targets,
     c->bits = p.key_bits / 3;
     c->leaf_cap = p.leaf_cap;
     c->curve = p.key_curve;
-    const uint64_t worst = (uint64_t)max_sources * (uint64_t)(c->bits + 1) + 1;
-    c->node_cap = p.node_capacity ? (uint64_t)p.node_capacity : worst;
+    c->node_cap = p.node_capacity ? (uint64_t)p.node_capacity
+                                  : node_bound((uint64_t)max_sources, c->bits, c->leaf_cap);
     if (c->node_cap > 0xfffffff0ull) c->node_cap = 0xfffffff0ull;
 
     const size_t ns = (size_t)max_sources, nt = (size_t)max_targets;

@@ -61,8 +61,11 @@ typedef enum bh_status {
  *   leaf_cap      B >= 1: a cell holding more than B particles is split into its
  *                 octants unless it is at the deepest level ([Tree] 实现步骤: a
  *                 leaf holds a few particles).  At most 256.
- *   node_capacity maximum number of tree nodes; 0 selects the worst case
- *                 max_sources * (key_bits/3 + 1) + 1, which can never overflow.
+ *   node_capacity maximum number of tree nodes; 0 selects the bound
+ *                 (key_bits/3) * floor(max_sources / (B + 1)) + max_sources + 1,
+ *                 which no tree exceeds: the split cells of one level are
+ *                 disjoint and hold more than B sources each, and leaves are
+ *                 disjoint non-empty cells.
  *   key_curve     BH_CURVE_MORTON (default) or BH_CURVE_HILBERT (keys after
  *                 Skilling, "Programming the Hilbert curve", 2004); bh_get_keys
  *                 returns keys of this curve.  Separate targets are ordered by
@@ -273,9 +276,9 @@ bh_status bh_diagnostics(bh_ctx *ctx, const float *pos_mass, const float *vel,
  * of the library, 64 MiB on each GPU the library runs on, held until the
  * process ends.  The tree's node capacity is the bound
  * bits * floor(n / (leaf_cap + 1)) + n + 1, which no input can exceed, so a
- * step fits when about 220 bytes per source (63-bit keys, leaf_cap 16; about
- * 820 with leaf_cap 1) fit the array: up to roughly 300000 sources at
- * leaf_cap 16, 82000 at leaf_cap 1.
+ * step fits when about 225 bytes per source (63-bit keys, leaf_cap 16; about
+ * 825 with leaf_cap 1) fit the array: up to roughly 300000 sources at
+ * leaf_cap 16, 81000 at leaf_cap 1.
  *   src_pos_mass  device, n float4 rows (x, y, z, m), 16-byte aligned.
  *   params        key_bits, leaf_cap and key_curve as for bh_create
  *                 (node_capacity and reserved must be 0); NULL = 63-bit
