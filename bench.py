@@ -14,7 +14,9 @@ output.  Prints one JSON line.
 value = interactions per second of the whole step (interactions = accepted
 nodes + particle pairs of the walk, counted by the library in an untimed
 pass).  The roofline object describes the walk kernel (the dominant one),
-counted at 20 flops per interaction against the fp32 vector peak.
+counted at 20 flops per interaction against the fp32 vector peak, and in its
+"build" member bh_build's algorithmic bytes against the HBM peak.
+config.morton_keys times the same step with Morton keys (the pages' order).
 """
 import argparse
 import hashlib
@@ -703,6 +705,30 @@ def main():
                        ("bbox_keys", "sort", "tree_com", "walk"), phases)}},
         "roofline": roofline,
     }
+    tree.close()
+    if args.curve != "morton":
+        # the same step on Morton keys (the pages' order; the same cells), timed
+        # the same way after the timed region, so the curve's effect can be read
+        # off this line
+        tm = bh.BarnesHut(n, 0, args.key_bits, args.leaf_cap, curve="morton")
+        for _ in range(args.warmup):
+            tm.build(src)
+            tm.gravity(prm["theta"], prm["G"], prm["eps"], out=out)
+        tm.sync()
+        evm = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        for e in evm:
+            e[0].record(stream)
+            tm.build(src)
+            e[1].record(stream)
+            tm.gravity(prm["theta"], prm["G"], prm["eps"], out=out)
+            e[2].record(stream)
+        torch.cuda.synchronize()
+        tm.sync()
+        rec["config"]["morton_keys"] = {
+            "ms_per_step": round(sum(e[0].elapsed_time(e[2]) for e in evm) / len(evm), 4),
+            "walk_ms": round(sum(e[1].elapsed_time(e[2]) for e in evm) / len(evm), 4),
+            "interactions_per_step": tm.count_interactions(prm["theta"], prm["eps"])}
+        tm.close()
     if not args.no_cpu_baseline:
         rec["cpu_baseline"], oc = cpu_baseline(p, prm, args.key_bits, args.leaf_cap, args.curve)
         # the numerator checked against the oracle's own count (fp64 opening
@@ -711,7 +737,6 @@ def main():
         rec["config"]["interactions_oracle_kind"] = oc["kind"]
         rec["config"]["interactions_rel_diff"] = (interactions - oc["interactions"]) / max(
             oc["interactions"], 1)
-    tree.close()
     print(json.dumps(rec), flush=True)
 
 
