@@ -99,8 +99,8 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
 // gave 6, and the walk ran 7% faster at 68 than at 90 with the same code).
 //
 // The loop is bound by the latency of each visit's scalar load of its node
-// record (waves spend about half their cycles waiting on it), so the record
-// of the next visit is requested as early as its index is known.  Moves to
+// record together with the vector issue, so the record of the next visit is
+// requested as early as its index is known.  Moves to
 // the skip are the common case (a wave descends into about one node in five
 // it visits), so when a record arrives the loop at once requests the record
 // at its skip into the other slot, before any arithmetic; the wave moves
@@ -112,14 +112,16 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
 //
 // One visit of node XR (record slot R0..R7, the other slot OTHER):
 //   act  = rejoin <= X                         (vcc, then exec)
-//   T    = T0 * 4^-level, the exponent of T0 stepped down by 2 * level
-//   far  = T < r^2, by a compare that also narrows exec to act & far
+//   s    = r^2 + eps^2, accumulated from eps^2 by three fused steps
+//   far  = T + eps^2 < s (the record holds T + eps^2), by a compare that also
+//          narrows exec to act & far: the opening test T < r^2 on the softened
+//          scale, whose s is also the monopole's argument
 //   open = act & ~exec                          (SCC: some lane opens X)
 //   lanes in act & far add the monopole (their rejoin moves to the node's
 //   skip only where the wave descends into the node or returns, below)
-// The monopole is inv = rsq(r^2 + eps^2), f = m inv^3, a += f d, pot -= m inv,
-// with eps^2 in a vector register and the potential term unfused, so that all
-// but the node-field operands are register-only.  At least one instruction
+// The monopole is inv = rsq(s), f = m inv^3, a += f d, pot -= m inv, with
+// eps^2 in a vector register and the potential term unfused, so that all but
+// the node-field operands are register-only.  At least one instruction
 // sits between the reciprocal square root and the first use of its result,
 // which the hardware requires.  %[off] holds X + 1 from the head on.
 // CNT: the interaction count update, if any.
@@ -130,14 +132,13 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
     "s_load_dwordx8 " OTHER ", %[nb], " R6 "\n"                                        \
     "v_sub_f32_e32 %[dx], " R0 ", %[px]\n"                                             \
     "v_sub_f32_e32 %[dy], " R1 ", %[py]\n"                                             \
-    "v_mul_f32_e32 %[r2], %[dx], %[dx]\n"                                              \
+    "v_fma_f32 %[r2], %[dx], %[dx], %[eps2]\n"                                         \
     "v_sub_f32_e32 %[dz], " R2 ", %[pz]\n"                                             \
     "v_fmac_f32_e32 %[r2], %[dy], %[dy]\n"                                             \
     "v_fmac_f32_e32 %[r2], %[dz], %[dz]\n"                                             \
     "s_and_saveexec_b64 %[save], vcc\n"                                                \
     "v_cmpx_lt_f32_e64 %[far], |" R7 "|, %[r2]\n"                                      \
-    "v_add_f32_e32 %[w], %[eps2], %[r2]\n"                                             \
-    "v_rsq_f32_e32 %[w], %[w]\n"                                                       \
+    "v_rsq_f32_e32 %[w], %[r2]\n"                                                      \
     "s_andn2_b64 %[open], vcc, exec\n"
 #define BH_MONO(R3, CNT)                                                               \
     "v_mul_f32_e32 %[f], " R3 ", %[w]\n"                                               \
@@ -471,14 +472,15 @@ __device__ __attribute__((always_inline)) inline void walk_wave(
         const float cz = __uint_as_float(lo.z), m = __uint_as_float(mbits);
         const uint32_t skip = hi.z, meta = hi.w;
         const uint32_t level = node_level(meta);
-        const float T = ldexpf(T0, -2 * (int)level);
+        // the opening test on the softened scale: T + eps^2 < r^2 + eps^2
+        const float T = ldexpf(T0, -2 * (int)level) + eps2;
         const float dx = cx - p.x, dy = cy - p.y, dz = cz - p.z;
-        const float r2 = fmaf(dz, dz, fmaf(dy, dy, dx * dx));
+        const float r2 = fmaf(dz, dz, fmaf(dy, dy, fmaf(dx, dx, eps2)));
         const uint64_t act_m = __ballot(rejoin <= X);
         const uint64_t far_m = __ballot(T < r2);
         const uint64_t open_m = act_m & ~far_m;
         if (rejoin <= X && T < r2) {
-            const float inv = __builtin_amdgcn_rsqf(r2 + eps2);
+            const float inv = __builtin_amdgcn_rsqf(r2);
             const float mi = m * inv;
             const float f = mi * inv * inv;
             ax = fmaf(f, dx, ax);
@@ -636,14 +638,15 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
 }
 
 // The walk records of one call: per node X <= n_nodes (the end record
-// included) {com, mass, start, count, skip * 32, T | leaf << 31}, with the
-// opening threshold T = (L / theta)^2 4^-level by ldexp (exact wherever it is
-// representable, the value every walk form compares with) and the skip as a
-// byte offset, so the assembly loop uses both without arithmetic.  Written
+// included) {com, mass, start, count, skip * 32, (T + eps^2) | leaf << 31},
+// with the opening threshold T = (L / theta)^2 4^-level by ldexp (exact
+// wherever it is representable) shifted by eps^2 in one fp32 addition, the
+// value every per-target walk form compares r^2 + eps^2 with, and the skip as
+// a byte offset, so the assembly loop uses both without arithmetic.  Written
 // only when the loop will use them (see k_walk).
 __global__ __launch_bounds__(256) void k_walk_nodes(const Node *__restrict__ nodes,
                                                     const DevParams *__restrict__ prm,
-                                                    float theta, uint32_t wn_cap,
+                                                    float theta, float eps2, uint32_t wn_cap,
                                                     Node *__restrict__ wnodes)
 {
     if (prm->status != 0) return;
@@ -654,7 +657,7 @@ __global__ __launch_bounds__(256) void k_walk_nodes(const Node *__restrict__ nod
     for (uint32_t X = blockIdx.x * blockDim.x + threadIdx.x; X <= nn; X += gridDim.x * blockDim.x) {
         const uint4 lo = reinterpret_cast<const uint4 *>(&nodes[X])[0];
         const uint4 hi = reinterpret_cast<const uint4 *>(&nodes[X])[1];
-        const float T = ldexpf(T0, -2 * (int)node_level(hi.w));
+        const float T = ldexpf(T0, -2 * (int)node_level(hi.w)) + eps2;
         const uint32_t tb = (__float_as_uint(T) & 0x7fffffffu) | ((hi.w & kLeafBit) ? 0x80000000u : 0u);
         reinterpret_cast<uint4 *>(&wnodes[X])[0] = lo;
         reinterpret_cast<uint4 *>(&wnodes[X])[1] = make_uint4(hi.x, hi.y, hi.z << 5, tb);
@@ -715,7 +718,7 @@ void launch_walk(const WalkArgs &a, hipStream_t s)
     if (!a.vote && a.wn_cap > 0) {
         const uint32_t blocks = (uint32_t)std::min<uint64_t>((a.wn_cap + 255) / 256, 2048);
         hipLaunchKernelGGL(k_walk_nodes, dim3(blocks), dim3(256), 0, s, a.nodes, a.prm, a.theta,
-                           a.wn_cap, a.wnodes);
+                           a.eps * a.eps, a.wn_cap, a.wnodes);
     }
     // Plummer softening with eps^2 > 0 never meets r^2 + eps^2 == 0
     if (a.eps * a.eps > 0.f) launch1<true>(a, s); else launch1<false>(a, s);

@@ -428,7 +428,11 @@ static void walk(walker *w, int64_t c)
     double w_sq = width * width;
     double threshold = w_sq / w->theta_sq;
     int accept = threshold < r_sq;
-    if (isfinite(threshold) && fabs(r_sq - threshold) <= ldexp(threshold, -20)) {
+    /* near-tie: within 2^-20 of the threshold on the softened scale
+       (r_sq + eps_sq against threshold + eps_sq, the scale on which an fp32
+       walk may evaluate the same test) */
+    if (isfinite(threshold) &&
+        fabs(r_sq - threshold) <= ldexp(threshold + w->eps_sq, -20)) {
         w->n_ties++;
         if (w->tie_mode == 1) accept = 0;
         if (w->tie_mode == 2) accept = 1;
