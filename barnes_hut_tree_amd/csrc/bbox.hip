@@ -253,7 +253,10 @@ __global__ __launch_bounds__(kKeyThreads) void k_morton(const float4 *__restrict
     }
     const uint16_t *lut2 = lut, *lut1 = lut + kHilbertStates * 64;
     const uint64_t top = (1ull << BITS) - 1;
-    const double s = prm->scale;
+    // 2^BITS / L as one IEEE division: the tree's own scale when BITS is the
+    // tree's depth, and a coarser grid on the same cube for ordering targets
+    const double L = prm->L;
+    const double s = (L > 0.0) ? __builtin_ldexp(1.0, BITS) / L : 0.0;
     const uint32_t base = blockIdx.x * (kKeyThreads * kKeysPerThread) + threadIdx.x;
 #pragma unroll
     for (int t = 0; t < kKeysPerThread; ++t) {

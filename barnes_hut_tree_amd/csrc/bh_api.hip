@@ -344,19 +344,25 @@ bh_status bh_build(bh_ctx *c, const float *src_pos_mass, int64_t n, void *stream
     return BH_OK;
 }
 
-// Morton keys of separate targets on the sources' root cube (clamped), their
-// stable sort, and the sorted copy in c->tpos; returns the caller index of each
-// sorted target.
-static const uint32_t *sort_targets(bh_ctx *c, const float *targets, uint32_t nt, hipStream_t s)
+// Keys of separate targets on the sources' root cube (clamped) with `bits`
+// bits per axis on the tree's curve, their stable sort, and the sorted copy in
+// c->tpos; returns the caller index of each sorted target.
+static const uint32_t *sort_targets(bh_ctx *c, const float *targets, uint32_t nt, int bits,
+                                    hipStream_t s)
 {
     uint64_t *ko;
     uint32_t *vo;
-    launch_morton((const float4 *)targets, nt, c->prm, c->bits, c->curve, c->hlut, c->tkeys,
+    launch_morton((const float4 *)targets, nt, c->prm, bits, c->curve, c->hlut, c->tkeys,
                   c->tvals, s);
-    radix_sort(c->tkeys, c->tvals, c->tkeys_alt, c->tvals_alt, &ko, &vo, nt, c->key_bits,
+    radix_sort(c->tkeys, c->tvals, c->tkeys_alt, c->tvals_alt, &ko, &vo, nt, 3 * bits,
                c->tspine, (const float4 *)targets, c->tpos, s);
     return vo;
 }
+
+// The walk's order of separate targets only groups nearby targets into waves
+// (every target's result is independent of its wave), so 30-bit keys (a 1024^3
+// grid on the root cube, 4 sort passes) serve as well as the tree's own.
+constexpr int kTargetOrderBits = 10;
 
 static bh_status gravity_impl(bh_ctx *c, const float *targets, int64_t n_targets, float theta,
                               float G, float eps, uint32_t flags, float *out, uint64_t *count,
@@ -415,7 +421,7 @@ static bh_status gravity_impl(bh_ctx *c, const float *targets, int64_t n_targets
         }
     } else if (targets) {
         a.tpos = c->tpos;
-        a.tmap = sort_targets(c, targets, nt, s);
+        a.tmap = sort_targets(c, targets, nt, kTargetOrderBits, s);
         a.self = 0;
     } else {
         a.tpos = c->spos;
@@ -496,7 +502,7 @@ bh_status bh_sbh(bh_ctx *c, const float *targets, int64_t n_targets, int d, int 
     }
     SbhArgs a;
     a.nodes = c->nodes;
-    a.tperm = sort_targets(c, targets, nt, s);
+    a.tperm = sort_targets(c, targets, nt, c->bits, s);
     a.tpos = c->tpos;
     a.prm = c->prm;
     a.n_targets = nt;
