@@ -421,7 +421,9 @@ static bh_status gravity_impl(bh_ctx *c, const float *targets, int64_t n_targets
         }
     } else if (targets) {
         a.tpos = c->tpos;
-        a.tmap = sort_targets(c, targets, nt, kTargetOrderBits, s);
+        // the vote's groups are 64 consecutive targets of the tree's key
+        // order; the per-target walk's results do not depend on the grouping
+        a.tmap = sort_targets(c, targets, nt, a.vote ? c->bits : kTargetOrderBits, s);
         a.self = 0;
     } else {
         a.tpos = c->spos;

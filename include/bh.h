@@ -69,7 +69,9 @@ typedef enum bh_status {
  *   key_curve     BH_CURVE_MORTON (default) or BH_CURVE_HILBERT (keys after
  *                 Skilling, "Programming the Hilbert curve", 2004); bh_get_keys
  *                 returns keys of this curve.  Separate targets are ordered by
- *                 the same curve. */
+ *                 the same curve (for the per-target walk on a 1024^3 grid of
+ *                 the root cube, which groups nearby targets as well; its
+ *                 results do not depend on the order). */
 typedef struct bh_build_params {
     int32_t key_bits;
     int32_t leaf_cap;
@@ -136,8 +138,9 @@ bh_status bh_gravity_counted(bh_ctx *ctx, const float *targets, int64_t n_target
  *                     wave walk together, and when the opening test fails for any
  *                     of them, every one of them uses the node's children (or,
  *                     for a leaf, its particles).  Results depend on which
- *                     targets share a wave (64 consecutive targets of the walk
- *                     order) and are at least as accurate as the per-target walk.
+ *                     targets share a wave (64 consecutive targets in the
+ *                     order of the tree's keys) and are at least as accurate as
+ *                     the per-target walk.
  *   BH_WALK_UNSORTED  walk the targets in the caller's order instead of their
  *                     Morton order ([GASPHiA] 排序算法 measures what this order
  *                     buys).  Without BH_WALK_VOTE the results are bit-identical
