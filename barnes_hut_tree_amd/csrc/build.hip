@@ -25,12 +25,16 @@
 // The same tile pass keeps fp64 prefix sums P of (m, m (x - lo)) over the
 // sorted particles, so every node, leaf or internal, takes
 // (P[end] - P[start]) in one step; with fp64 sums the difference keeps about
-// 1e-10 relative accuracy even at N = 2^26, far below the fp32 result.
+// 1e-10 relative accuracy even at N = 2^26, far below the fp32 result.  Node
+// ranges start and end only where leaves start, so P is kept at leaf starts,
+// stored by leaf number (consecutive leaves, consecutive entries).
 //
-// Kernels: count (d, c, per-tile node totals and particle sums) -> one scan
-// over the tiles -> emit (node start/level, the index of the first node at
-// each position, the prefix sums P) -> ranges (cell end by galloping search,
-// skip = first node at the end, mass and centre of mass from P).
+// Kernels: count (d, c, per-tile node and leaf totals and particle sums) ->
+// one scan over the tiles -> emit (node start, leaf number and level; per
+// leaf start the first node there and its leaf number; P per leaf) -> ranges
+// (a leaf ends where the next node starts; an internal cell's end by
+// galloping search in the keys; skip = first node at the end; mass and
+// centre of mass from P).
 #include "bh_internal.h"
 
 namespace bh {
