@@ -213,6 +213,225 @@ __global__ __launch_bounds__(kSortThreads) void k_scatter(
     }
 }
 
+// ---- runs of equal top bits ----------------------------------------------
+//
+// 63-bit keys are sorted by their top 40 bits in five passes; the keys that
+// share those bits form runs (cells 2^-13.3 of the root cube wide: one to a few
+// dozen sources in every workload measured), and each run is then put in
+// order of its low 24 bits in one kernel, keeping the order of equal keys.
+// A source whose run has at most kRunHalo members finds the run in LDS and
+// its place by counting the run's members that precede it; longer runs are
+// sorted by the workgroup that holds their first member: in LDS up to
+// kRunLds members, else by three stable 8-bit counting passes over the run.
+constexpr int kRunHalo = 64;
+constexpr int kRunLds = 4096;
+constexpr int kLowBits = 24;
+
+__device__ inline uint32_t low_of(uint64_t k) { return (uint32_t)k & ((1u << kLowBits) - 1u); }
+
+// One stable counting pass of the run [0, L) by the 8-bit digit at `shift` of
+// the low bits: keys and values from (ki, vi) to (ko, vo), with the run held
+// at offset s of every array.  Keys may also sit in packed float4 rows
+// (PACKED_IN / PACKED_OUT: x, y = key halves, z = value).
+template <bool PACKED_IN, bool PACKED_OUT>
+__device__ void run_pass(const uint64_t *ki, const uint32_t *vi, const float4 *pi, uint64_t *ko,
+                         uint32_t *vo, float4 *po, uint32_t s, uint32_t L, int shift,
+                         uint32_t *hist, uint32_t (*wc)[kRadix], uint32_t *tmp)
+{
+    const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+    auto load = [&](uint32_t j, uint64_t &k, uint32_t &v) {
+        if (PACKED_IN) {
+            const uint4 r = reinterpret_cast<const uint4 *>(pi)[s + j];
+            k = (uint64_t)r.x | ((uint64_t)r.y << 32);
+            v = r.z;
+        } else {
+            k = ki[s + j];
+            v = vi[s + j];
+        }
+    };
+    hist[threadIdx.x] = 0;
+    __syncthreads();
+    for (uint32_t j = threadIdx.x; j < L; j += kSortThreads) {
+        uint64_t k;
+        uint32_t v;
+        load(j, k, v);
+        atomicAdd(&hist[(low_of(k) >> shift) & 0xffu], 1u);
+    }
+    __syncthreads();
+    uint32_t total;
+    const uint32_t base0 = block_excl_scan_256(hist[threadIdx.x], tmp, &total);
+    __syncthreads();
+    hist[threadIdx.x] = base0;   // running output start of each digit
+    __syncthreads();
+    for (uint32_t t0 = 0; t0 < L; t0 += kSortThreads) {
+        const uint32_t j = t0 + threadIdx.x;
+        const bool valid = j < L;
+        uint64_t k = 0;
+        uint32_t v = 0;
+        if (valid) load(j, k, v);
+        const uint32_t d = (low_of(k) >> shift) & 0xffu;
+        uint64_t peers = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const bool bit = (d >> b) & 1u;
+            const uint64_t m = __ballot(bit);
+            peers &= bit ? m : ~m;
+        }
+        for (int w = 0; w < kSortThreads / 64; ++w) wc[w][threadIdx.x] = 0;
+        __syncthreads();
+        if (valid && (peers & lt_mask) == 0) wc[wave][d] = (uint32_t)__popcll(peers);
+        __syncthreads();
+        if (valid) {
+            uint32_t before = 0;
+            for (uint32_t w = 0; w < wave; ++w) before += wc[w][d];
+            const uint32_t pos = hist[d] + before + (uint32_t)__popcll(peers & lt_mask);
+            if (PACKED_OUT) {
+                reinterpret_cast<uint4 *>(po)[s + pos] =
+                    make_uint4((uint32_t)k, (uint32_t)(k >> 32), v, 0u);
+            } else {
+                ko[s + pos] = k;
+                vo[s + pos] = v;
+            }
+        }
+        __syncthreads();
+        {
+            uint32_t c = 0;
+            for (int w = 0; w < kSortThreads / 64; ++w) c += wc[w][threadIdx.x];
+            hist[threadIdx.x] += c;
+        }
+        __syncthreads();
+    }
+}
+
+// (kin, vin) sorted by the bits above kLowBits, stably; out: (kout, vout)
+// sorted by the whole key, stably, and gdst[p] = gsrc[vout[p]].
+template <int ITEMS>
+__global__ __launch_bounds__(kSortThreads) void k_runs(
+    const uint64_t *__restrict__ kin, const uint32_t *__restrict__ vin,
+    uint64_t *__restrict__ kout, uint32_t *__restrict__ vout, uint32_t n, uint32_t n_tiles,
+    const float4 *__restrict__ gsrc, float4 *__restrict__ gdst)
+{
+    constexpr uint32_t kTile = kSortThreads * ITEMS;
+    constexpr uint32_t kWin = kTile + 2 * kRunHalo;
+    constexpr uint32_t kLds = kWin > (uint32_t)kRunLds ? kWin : (uint32_t)kRunLds;
+    __shared__ uint64_t sk[kLds];                // the tile and its halo; then a run
+    __shared__ uint32_t starts[kTile / (kRunHalo + 1) + 2];
+    __shared__ uint32_t n_starts;
+    __shared__ uint32_t hist[kRadix];
+    __shared__ uint32_t wc[kSortThreads / 64][kRadix];
+    __shared__ uint32_t tmp[kSortThreads / 64];
+    __shared__ uint32_t found;
+
+    const uint32_t tile = xcd_block(blockIdx.x, n_tiles);
+    const int64_t t0 = (int64_t)tile * kTile;
+    const int64_t w0 = t0 - kRunHalo;
+    if (threadIdx.x == 0) n_starts = 0;
+    for (uint32_t k = threadIdx.x; k < kWin; k += kSortThreads) {
+        const int64_t a = w0 + k;
+        sk[k] = (a >= 0 && a < (int64_t)n) ? kin[a] : 0ull;
+    }
+    __syncthreads();
+    auto top = [](uint64_t k) { return k >> kLowBits; };
+    for (int it = 0; it < ITEMS; ++it) {
+        const int64_t i = t0 + it * kSortThreads + threadIdx.x;
+        if (i >= (int64_t)n) break;
+        const uint32_t li = (uint32_t)(i - w0);
+        const uint64_t key = sk[li];
+        const uint64_t h = top(key);
+        // the run [s, e) around i, searched up to kRunHalo either side
+        uint32_t ls = li, le = li + 1;
+        int64_t s = i, e = i + 1;
+        while (s > 0 && li - ls < (uint32_t)kRunHalo && top(sk[ls - 1]) == h) { --ls; --s; }
+        while (e < (int64_t)n && le - li - 1 < (uint32_t)kRunHalo && top(sk[le]) == h) { ++le; ++e; }
+        // a search that used all its steps stopped inside a run of more than
+        // kRunHalo members; otherwise it stopped at the run's end
+        const bool lo_cap = li - ls >= (uint32_t)kRunHalo;
+        const bool hi_cap = le - li - 1 >= (uint32_t)kRunHalo;
+        if (!lo_cap && !hi_cap && e - s <= kRunHalo) {
+            uint32_t rank = 0;
+            const uint32_t lo = low_of(key);
+            for (uint32_t j = ls; j < le; ++j) {
+                const uint32_t lj = low_of(sk[j]);
+                rank += (lj < lo || (lj == lo && j < li)) ? 1u : 0u;
+            }
+            const int64_t p = s + rank;
+            const uint32_t v = vin[i];
+            kout[p] = key;
+            vout[p] = v;
+            gdst[p] = gsrc[v];
+        } else if (ls == li) {
+            starts[atomicAdd(&n_starts, 1u)] = (uint32_t)i;   // a long run starts here
+        }
+    }
+    __syncthreads();
+    const uint32_t ns = n_starts;
+    for (uint32_t r = 0; r < ns; ++r) {
+        const uint32_t s = starts[r];
+        const uint64_t h = top(kin[s]);
+        // the run's end: the first position past s with other top bits
+        uint32_t e = s + 1;
+        for (;;) {
+            if (threadIdx.x == 0) found = 0xffffffffu;
+            __syncthreads();
+            const uint32_t j = e + threadIdx.x;
+            if (j < n && top(kin[j]) != h) atomicMin(&found, j);
+            if (j >= n) atomicMin(&found, n);
+            __syncthreads();
+            const uint32_t f = found;
+            __syncthreads();
+            if (f != 0xffffffffu) {
+                e = f;
+                break;
+            }
+            e += kSortThreads;
+        }
+        const uint32_t L = e - s;
+        if (L <= (uint32_t)kRunLds) {
+            // bitonic sort of (low bits, place in the run) in LDS
+            uint32_t P = 1;
+            while (P < L) P <<= 1;
+            for (uint32_t j = threadIdx.x; j < P; j += kSortThreads)
+                sk[j] = j < L ? (((uint64_t)low_of(kin[s + j]) << 32) | j) : ~0ull;
+            __syncthreads();
+            for (uint32_t k = 2; k <= P; k <<= 1) {
+                for (uint32_t m = k >> 1; m > 0; m >>= 1) {
+                    for (uint32_t j = threadIdx.x; j < P; j += kSortThreads) {
+                        const uint32_t q = j ^ m;
+                        if (q > j) {
+                            const uint64_t a = sk[j], b = sk[q];
+                            const bool up = (j & k) == 0;
+                            if ((a > b) == up) {
+                                sk[j] = b;
+                                sk[q] = a;
+                            }
+                        }
+                    }
+                    __syncthreads();
+                }
+            }
+            for (uint32_t k = threadIdx.x; k < L; k += kSortThreads) {
+                const uint32_t src = s + (uint32_t)(sk[k] & 0xffffffffull);
+                const uint32_t v = vin[src];
+                kout[s + k] = kin[src];
+                vout[s + k] = v;
+                gdst[s + k] = gsrc[v];
+            }
+            __syncthreads();
+        } else {
+            // three stable counting passes over the low bits: (kin, vin) ->
+            // (kout, vout) -> rows of gdst -> (kout, vout), then the gather
+            run_pass<false, false>(kin, vin, nullptr, kout, vout, nullptr, s, L, 0, hist, wc, tmp);
+            run_pass<false, true>(kout, vout, nullptr, nullptr, nullptr, gdst, s, L, 8, hist, wc,
+                                  tmp);
+            run_pass<true, false>(nullptr, nullptr, gdst, kout, vout, nullptr, s, L, 16, hist, wc,
+                                  tmp);
+            for (uint32_t k = threadIdx.x; k < L; k += kSortThreads) gdst[s + k] = gsrc[vout[s + k]];
+            __syncthreads();
+        }
+    }
+}
+
 constexpr int kScanThreads = 256;
 
 // Exclusive scan of each row of a [rows][len] table, one workgroup per row:
@@ -264,9 +483,12 @@ void sort_passes(uint64_t *&ka, uint32_t *&va, uint64_t *&kb, uint32_t *&vb, uin
     const uint32_t entries = kRadix * tiles;
     uint32_t *hist = spine, *pref = spine + entries, *tot = spine + 2 * entries;
     const int passes = (key_bits + 7) / 8;
-    for (int p = 0; p < passes; ++p) {
+    // long keys with a gather: passes over the bits above kLowBits, then runs
+    const bool runs = gather_src && key_bits > 40;
+    const int p0 = runs ? kLowBits / 8 : 0;
+    for (int p = p0; p < passes; ++p) {
         const int shift = 8 * p;
-        const bool last = (p == passes - 1);
+        const bool last = !runs && (p == passes - 1);
         hipLaunchKernelGGL(k_hist<ITEMS>, dim3(tiles), dim3(kSortThreads), 0, s, ka, n, shift,
                            hist, tiles);
         launch_scan_rows(hist, pref, tot, kRadix, tiles, s);
@@ -278,6 +500,12 @@ void sort_passes(uint64_t *&ka, uint32_t *&va, uint64_t *&kb, uint32_t *&vb, uin
                                ka, va, kb, vb, n, shift, pref, tot, tiles,
                                (const float4 *)nullptr, (float4 *)nullptr);
         }
+        uint64_t *tk = ka; ka = kb; kb = tk;
+        uint32_t *tv = va; va = vb; vb = tv;
+    }
+    if (runs) {
+        hipLaunchKernelGGL(k_runs<ITEMS>, dim3(tiles), dim3(kSortThreads), 0, s, ka, va, kb, vb,
+                           n, tiles, gather_src, gather_dst);
         uint64_t *tk = ka; ka = kb; kb = tk;
         uint32_t *tv = va; va = vb; vb = tv;
     }

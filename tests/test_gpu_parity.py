@@ -51,6 +51,24 @@ def _dup(p):
     return np.concatenate([p, p[:100], p[:7]])
 
 
+def _clusters(sizes, radius, seed, background=0):
+    """Tight balls of sources (radius relative to a unit root cube) plus two
+    corners that fix the cube: many sources then share the top 40 bits of
+    their 63-bit keys, the long runs the sort finishes in a workgroup."""
+    rng = np.random.default_rng(seed)
+    parts = [np.array([[0.0, 0.0, 0.0], [1.0, 1.0, 1.0]])]
+    for k, m in enumerate(sizes):
+        c = rng.uniform(0.2, 0.8, 3)
+        d = rng.standard_normal((m, 3))
+        d *= (radius * rng.uniform(0, 1, (m, 1)) ** (1 / 3)) / np.linalg.norm(d, axis=1, keepdims=True)
+        parts.append(c + d)
+    if background:
+        parts.append(rng.uniform(0, 1, (background, 3)))
+    xyz = np.concatenate(parts)
+    xyz = xyz[rng.permutation(xyz.shape[0])]
+    return np.concatenate([xyz, np.full((xyz.shape[0], 1), 1.0 / xyz.shape[0])], 1).astype(np.float32)
+
+
 KEY_CASES = {
     "uniform4096": lambda: W.uniform_cube(4096, seed=1),
     "plummer65536": lambda: W.plummer(1 << 16, seed=3),
@@ -62,6 +80,11 @@ KEY_CASES = {
     # above the size from which the sort takes its larger tiles; every key twice
     "large_ragged": lambda: W.uniform_cube((1 << 22) + 777, seed=11),
     "large_duplicates": lambda: np.concatenate([W.plummer((1 << 21) + 5, seed=12)] * 2),
+    # runs of 65..4096 sources sharing their top key bits (sorted in LDS) and
+    # longer ones (counting passes), among short runs
+    "clusters_mid": lambda: _clusters([70, 300, 1000, 4000], 1e-5, 13, background=30000),
+    "clusters_long": lambda: _clusters([20000, 5000], 1e-5, 14, background=1000),
+    "cluster_duplicates": lambda: np.concatenate([_clusters([9000], 1e-6, 15)] * 2),
 }
 
 
