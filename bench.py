@@ -56,12 +56,18 @@ def make_workload(name):
 def build_alg_bytes(n, n_nodes, n_leaves, key_bits):
     """Algorithmic HBM bytes of one bh_build over n sources giving n_nodes
     nodes and n_leaves leaves: bounding box 16n read; keys 16n read and 12n
-    written; per sort pass an 8n histogram read and a 12n + 12n scatter, the
-    last pass also gathering the 16-byte rows (16n + 16n); count 26n read and
-    2n written; emit 18n read, 16 bytes per node and 40 per leaf written;
-    ranges 84 bytes read and 32 written per node."""
-    passes = (key_bits + 7) // 8
-    return (16 * n + 28 * n + passes * 32 * n + 32 * n + 28 * n + 18 * n
+    written; per sort pass an 8n histogram read and a 12n + 12n scatter; the
+    16-byte rows gathered in sorted order (16n + 16n), with 63-bit keys by the
+    kernel that finishes the runs of equal top 40 bits after five passes
+    (which also moves the keys and indices once more, 12n + 12n), with 30-bit
+    keys by the last of four passes; count 26n read and 2n written; emit 18n
+    read, 16 bytes per node and 40 per leaf written; ranges 84 bytes read and
+    32 written per node."""
+    if key_bits > 40:
+        sort = ((key_bits - 24 + 7) // 8) * 32 * n + 56 * n
+    else:
+        sort = ((key_bits + 7) // 8) * 32 * n + 32 * n
+    return (16 * n + 28 * n + sort + 28 * n + 18 * n
             + 16 * n_nodes + 40 * n_leaves + 116 * n_nodes)
 
 
