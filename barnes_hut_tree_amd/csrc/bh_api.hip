@@ -46,6 +46,9 @@ struct bh_ctx {
     Node *nodes = nullptr;
     Node *wnodes = nullptr;           // per-call walk records (see launch_walk)
     uint32_t wn_cap = 0;              // records wnodes holds
+    uint32_t *wbal = nullptr;         // the walk's XCD runs and per-group times
+    uint32_t hist_groups = 0;         // groups wbal holds times for (0: none)
+    int hist_kind = -1;               // 0: self-gravity, 1: separate targets
 
     uint64_t *tkeys = nullptr, *tkeys_alt = nullptr;
     uint32_t *tvals = nullptr, *tvals_alt = nullptr;
@@ -78,7 +81,8 @@ void free_all(bh_ctx *c)
 {
     void *ptrs[] = {c->prm, c->hlut, c->bbox_part, c->keys, c->keys_alt, c->vals, c->vals_alt, c->spine,
                     c->spos, c->bw.dc, c->bw.tile_counts, c->bw.tile_sums, c->bw.chunk_tot, c->bw.tile_scan,
-                    c->bw.first_node, c->bw.P, c->nodes, c->wnodes, c->tkeys, c->tkeys_alt, c->tvals,
+                    c->bw.first_node, c->bw.P, c->nodes, c->wnodes, c->wbal,
+                    c->tkeys, c->tkeys_alt, c->tvals,
                     c->tvals_alt, c->tspine, c->tpos, c->inv, c->diag, c->icount, c->lk_child,
                     c->lk_level, c->lk_next, c->lk_counter};
     for (void *p : ptrs)
@@ -139,6 +143,8 @@ static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 struct StaticDevice {
     unsigned char *base = nullptr;   // this device's copy of `scratch`
     bool ready = false;
+    int64_t hist_n = -1;             // sources of the last walk whose per-group times
+    uint32_t hist_groups = 0;        // `scratch` holds (the layout depends on n)
 };
 StaticDevice g_static[kStaticMaxDevices];
 std::mutex g_static_mu;
@@ -175,6 +181,7 @@ size_t static_layout(bh_ctx *c, unsigned char *base, uint32_t n)
     take(&c->nodes, (size_t)c->node_cap + 1);
     c->wn_cap = walk_records(n, c->bits, c->leaf_cap, c->node_cap);
     take(&c->wnodes, (size_t)c->wn_cap);
+    take(&c->wbal, (size_t)kWalkBalanceHead + walk_groups(n));
     return off;
 }
 
@@ -282,6 +289,8 @@ bh_status bh_create(bh_ctx **out, int64_t max_sources, int64_t max_targets,
     ok &= dalloc(&c->nodes, (size_t)c->node_cap + 1) == hipSuccess;
     c->wn_cap = walk_records((uint64_t)ns, c->bits, c->leaf_cap, c->node_cap);
     ok &= dalloc(&c->wnodes, (size_t)c->wn_cap) == hipSuccess;
+    ok &= dalloc(&c->wbal, (size_t)kWalkBalanceHead + walk_groups((uint32_t)(ns > nt ? ns : nt))) ==
+          hipSuccess;
     ok &= dalloc(&c->inv, ns) == hipSuccess;
     ok &= dalloc(&c->diag, (size_t)kDiagMaxPartials * kDiagTerms) == hipSuccess;
     ok &= dalloc(&c->icount, 1) == hipSuccess;
@@ -409,6 +418,13 @@ static bh_status gravity_impl(bh_ctx *c, const float *targets, int64_t n_targets
     a.count = (unsigned long long *)count;
     a.vote = (flags & BH_WALK_VOTE) != 0;
     a.unsorted = (flags & BH_WALK_UNSORTED) != 0;
+    // the per-target walk in key order balances its XCD runs on the previous
+    // such walk's per-group times when that walk had the same groups
+    const bool balanced = !a.vote && !a.unsorted && c->wn_cap > 0;
+    const int kind = targets ? 1 : 0;
+    const uint32_t groups = walk_groups(nt);
+    a.balance = balanced ? c->wbal : nullptr;
+    a.balance_hist = balanced && c->hist_groups == groups && c->hist_kind == kind;
     if (a.unsorted) {
         a.self = targets == nullptr;
         if (targets) {
@@ -433,6 +449,10 @@ static bh_status gravity_impl(bh_ctx *c, const float *targets, int64_t n_targets
     record(c, 5, s);
     launch_walk(a, s);
     record(c, 6, s);
+    if (balanced) {
+        c->hist_groups = groups;
+        c->hist_kind = kind;
+    }
     return launch_status();
 }
 
@@ -807,9 +827,20 @@ bh_status bh_gravity_static(const float *src_pos_mass, int64_t n, const bh_build
     bh_status st = static_base(c.device, &base);
     if (st != BH_OK) return st;
     static_layout(&c, base, (uint32_t)n);
+    {
+        std::lock_guard<std::mutex> lock(g_static_mu);
+        c.hist_groups = g_static[c.device].hist_n == n ? g_static[c.device].hist_groups : 0;
+        c.hist_kind = 0;
+    }
     st = bh_build(&c, src_pos_mass, n, stream);
     if (st != BH_OK) return st;
-    return gravity_impl(&c, nullptr, n, theta, G, eps, 0u, out_acc_pot, nullptr, stream);
+    st = gravity_impl(&c, nullptr, n, theta, G, eps, 0u, out_acc_pot, nullptr, stream);
+    {
+        std::lock_guard<std::mutex> lock(g_static_mu);
+        g_static[c.device].hist_n = st == BH_OK ? n : -1;
+        g_static[c.device].hist_groups = st == BH_OK ? c.hist_groups : 0;
+    }
+    return st;
 }
 
 }  // extern "C"

@@ -173,8 +173,21 @@ struct WalkArgs {
     float theta, G, eps;
     float4 *out;
     unsigned long long *count;  // optional interaction counter
+    // XCD balance of the sorted per-target walk (null: equal runs per XCD):
+    // the eight runs of groups for this walk, chosen from the previous walk's
+    // per-group times when balance_hist is set, and this walk's times (layout
+    // at kWalkBalanceHead)
+    uint32_t *balance;
+    int balance_hist;
 };
 void launch_walk(const WalkArgs &a, hipStream_t s);
+// walk groups of 64 targets, and the most groups one XCD's run may take
+__host__ __device__ inline uint32_t walk_groups(uint32_t n_targets) { return (n_targets + 63) / 64; }
+__host__ __device__ inline uint32_t walk_xcd_cap(uint32_t groups) { return (groups + 7) / 8 + (groups + 31) / 32; }
+// The walk's balance buffer: entries 0-8 the first group of each XCD's run
+// (the ninth = groups), 16-31 eight 64-bit sums of per-group times, from
+// kWalkBalanceHead on one time per group.
+constexpr uint32_t kWalkBalanceHead = 32;
 // inv[perm[k]] = k
 void launch_invert(const uint32_t *perm, uint32_t n, uint32_t *inv, hipStream_t s);
 void launch_fill_zero(float4 *out, uint32_t n, hipStream_t s);

@@ -571,14 +571,35 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
                                                        const DevParams *__restrict__ prm,
                                                        uint32_t n, float theta, float G,
                                                        float eps2, float4 *__restrict__ out,
-                                                       unsigned long long *__restrict__ count)
+                                                       unsigned long long *__restrict__ count,
+                                                       uint32_t *__restrict__ balance)
 {
     const uint32_t lane = threadIdx.x & 63;
-    const uint32_t blk = xcd_block(blockIdx.x, gridDim.x);
+    // the group this wave walks: each XCD (workgroups are dealt to the eight
+    // XCDs in turn) takes one contiguous run of groups, so the waves that run
+    // together share the nodes near their targets in that XCD's L2; with
+    // a balance buffer the runs are the ones balanced on the previous walk's times
+    uint32_t blk;
+    if (balance) {
+        // the grid holds 8 cap workgroups, cap per XCD; an XCD whose run is
+        // shorter lets its first ones return, while every XCD still has free
+        // slots (at the end of the dispatch they would hold up the others)
+        const uint32_t x = blockIdx.x & 7u, k = blockIdx.x >> 3;
+        const uint32_t b0 = sgpr(balance[x]), b1 = sgpr(balance[x + 1]);
+        const uint32_t idle = (gridDim.x >> 3) - (b1 - b0);
+        if (k < idle) return;
+        blk = b0 + (k - idle);
+    } else {
+        blk = xcd_block(blockIdx.x, gridDim.x);
+    }
     const uint32_t wave_base = sgpr(blk * kWalkThreads + (threadIdx.x & ~63u));
     const uint32_t c = wave_base + lane;
     const bool valid = c < n;
     if (wave_base >= n) return;
+    // the group's start time, kept in vector registers (scalar registers
+    // decide how many waves stay resident)
+    uint64_t t_start = balance ? __builtin_amdgcn_s_memrealtime() : 0;
+    asm volatile("" : "+v"(t_start));
     uint32_t i = c, slot = c;   // self index (Morton rank) and output slot
     if (valid) {
         if (!UNSORTED) slot = tmap[c];
@@ -630,6 +651,16 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
     }
 
     if (valid) out[slot] = make_float4(G * ax, G * ay, G * az, G * pot);
+    if (balance && lane == 0) {
+        // this group's time, and its share of the eighth of the groups it
+        // belongs to (which the next walk compares)
+        const uint32_t g = wave_base >> 6;
+        const uint32_t dt = (uint32_t)(__builtin_amdgcn_s_memrealtime() - t_start);
+        const float eighth = (float)g * 8.f / (float)walk_groups(n);
+        balance[kWalkBalanceHead + g] = dt;
+        atomicAdd(reinterpret_cast<unsigned long long *>(balance + 16) + min(7u, (uint32_t)eighth),
+                  (unsigned long long)dt);
+    }
     if (COUNT) {
         unsigned long long cnt = valid ? n_int : 0u;
         for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
@@ -644,11 +675,95 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
 // value every per-target walk form compares r^2 + eps^2 with, and the skip as
 // a byte offset, so the assembly loop uses both without arithmetic.  Written
 // only when the loop will use them (see k_walk).
+// The XCD runs of the coming walk.  xb[0..8]: the first group of each run
+// (xb[8] = ng); xb[16..31]: eight 64-bit sums of the per-group times of the
+// previous walk over the eighths of the groups, added by its waves.  Equal
+// runs unless those sums are more than kWalkRebalance out of balance; then
+// eight contiguous runs, on a grid of ng / 256 groups, whose sums of the
+// previous walk's per-group times are as equal as the cap of `cap` groups
+// per run allows.  (Equal runs of a centrally symmetric input coincide with
+// its root octants, so each XCD's L2 holds one octant's subtree; runs moved
+// off them to even out a few per cent of time measured slower.)  Clears the
+// sums for the coming walk.  One block of 256 threads.  Every run is at most
+// `cap` groups and 8 cap >= ng, so the walk's grid of 8 cap workgroups walks
+// every group once.
+constexpr double kWalkRebalance = 1.08;
+
+__device__ void walk_bounds(uint32_t ng, uint32_t cap, bool hist, uint32_t *__restrict__ xb)
+{
+    const uint32_t *__restrict__ wdur = xb + kWalkBalanceHead;
+    __shared__ unsigned long long part[256];
+    __shared__ uint32_t ideal[8];
+    __shared__ int balance;
+    unsigned long long *sums = reinterpret_cast<unsigned long long *>(xb + 16);
+    const uint32_t t = threadIdx.x;
+    if (t == 0) {
+        int bal = 0;
+        if (hist) {
+            unsigned long long total = 0, most = 0;
+            for (int x = 0; x < 8; ++x) {
+                total += sums[x];
+                most = max(most, sums[x]);
+            }
+            bal = (double)most * 8.0 > kWalkRebalance * (double)total;
+        }
+        balance = bal;
+    }
+    __syncthreads();
+    if (!balance) {
+        if (t <= 8) xb[t] = t * (ng >> 3) + min(t, ng & 7u);
+        if (t < 8) sums[t] = 0;
+        return;
+    }
+    // per-thread sums over chunks of consecutive groups, then an inclusive scan
+    const uint32_t chunk = (ng + 255) / 256;
+    const uint32_t g0 = min(ng, t * chunk), g1 = min(ng, g0 + chunk);
+    unsigned long long sum = 0;
+#pragma unroll 8
+    for (uint32_t g = g0; g < g1; ++g) sum += wdur[g];
+    part[t] = sum;
+    __syncthreads();
+    for (uint32_t o = 1; o < 256; o <<= 1) {
+        const unsigned long long v = t >= o ? part[t - o] : 0ull;
+        __syncthreads();
+        part[t] += v;
+        __syncthreads();
+    }
+    if (t >= 1 && t < 8) {
+        // the chunk boundary nearest to where the times reach t/8 of the total
+        const unsigned long long target = part[255] * t / 8;
+        uint32_t k = 0;
+        while (k < 255 && part[k] < target) ++k;
+        const unsigned long long before = k ? part[k - 1] : 0ull;
+        const uint32_t kb = target - before <= part[k] - target ? k : k + 1;
+        ideal[t] = min(ng, kb * chunk);
+    }
+    __syncthreads();
+    if (t == 0) {
+        // clamp: run x at most cap groups, and the runs after it able to hold
+        // the rest
+        uint32_t prev = 0;
+        xb[0] = 0;
+        for (uint32_t x = 1; x < 8; ++x) {
+            const uint64_t tail = (uint64_t)(8 - x) * cap;
+            const uint32_t lo = max(prev, (uint64_t)ng > tail ? (uint32_t)(ng - tail) : 0u);
+            const uint32_t hi = min(prev + cap, ng);
+            prev = min(max(ideal[x], lo), hi);
+            xb[x] = prev;
+        }
+        xb[8] = ng;
+    }
+    if (t < 8) sums[t] = 0;
+}
+
 __global__ __launch_bounds__(256) void k_walk_nodes(const Node *__restrict__ nodes,
                                                     const DevParams *__restrict__ prm,
                                                     float theta, float eps2, uint32_t wn_cap,
-                                                    Node *__restrict__ wnodes)
+                                                    Node *__restrict__ wnodes,
+                                                    uint32_t ng, uint32_t cap, int hist,
+                                                    uint32_t *__restrict__ balance)
 {
+    if (balance && blockIdx.x == 0) walk_bounds(ng, cap, hist != 0, balance);
     if (prm->status != 0) return;
     const uint32_t nn = prm->n_nodes;
     if (!(nn < kAsmMaxNodes && nn < wn_cap)) return;
@@ -680,10 +795,11 @@ __global__ void k_fill_zero(float4 *out, uint32_t n)
 template <bool SOFT, bool SELF, bool COUNT, bool VOTE, bool UNSORTED>
 void launch5(const WalkArgs &a, hipStream_t s)
 {
-    const uint32_t grid = (a.n_targets + kWalkThreads - 1) / kWalkThreads;
+    const uint32_t groups = walk_groups(a.n_targets);
+    const uint32_t grid = a.balance ? 8 * walk_xcd_cap(groups) : groups;
     hipLaunchKernelGGL((k_walk<SOFT, SELF, COUNT, VOTE, UNSORTED>), dim3(grid), dim3(kWalkThreads),
                        0, s, a.nodes, a.wnodes, a.wn_cap, a.src, a.tpos, a.tmap, a.prm, a.n_targets, a.theta, a.G,
-                       a.eps * a.eps, a.out, a.count);
+                       a.eps * a.eps, a.out, a.count, a.balance);
 }
 
 template <bool SOFT, bool SELF, bool COUNT>
@@ -712,13 +828,22 @@ void launch1(const WalkArgs &a, hipStream_t s)
 
 }  // namespace
 
-void launch_walk(const WalkArgs &a, hipStream_t s)
+void launch_walk(const WalkArgs &args, hipStream_t s)
 {
-    if (a.n_targets == 0) return;
+    if (args.n_targets == 0) return;
+    // the balanced XCD runs are written by k_walk_nodes, which runs for the
+    // per-target walks only; the caller-order and vote walks keep equal runs
+    WalkArgs a = args;
+    if (a.vote || a.unsorted || a.wn_cap == 0 || !a.balance) {
+        a.balance = nullptr;
+        a.balance_hist = 0;
+    }
     if (!a.vote && a.wn_cap > 0) {
         const uint32_t blocks = (uint32_t)std::min<uint64_t>((a.wn_cap + 255) / 256, 2048);
+        const uint32_t groups = walk_groups(a.n_targets);
         hipLaunchKernelGGL(k_walk_nodes, dim3(blocks), dim3(256), 0, s, a.nodes, a.prm, a.theta,
-                           a.eps * a.eps, a.wn_cap, a.wnodes);
+                           a.eps * a.eps, a.wn_cap, a.wnodes, groups, walk_xcd_cap(groups),
+                           a.balance_hist, a.balance);
     }
     // Plummer softening with eps^2 > 0 never meets r^2 + eps^2 == 0
     if (a.eps * a.eps > 0.f) launch1<true>(a, s); else launch1<false>(a, s);

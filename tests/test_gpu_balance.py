@@ -1,0 +1,122 @@
+"""The per-target walk's XCD runs, balanced on the previous walk's per-group
+times (through bh_gravity).
+
+Each XCD walks one contiguous run of the groups of 64 targets; after a first
+walk with equal runs, later walks of the same groups move the runs' ends so
+that their sums of the previous walk's times are equal.  Which XCD walks a
+group changes nothing in that group's arithmetic, so every call must give the
+same bits as the first, and as the caller-order walk (which keeps equal runs
+and, lane by lane, the same walk).  Outputs are filled with NaN before each
+call, so a group that no workgroup walked shows up."""
+import numpy as np
+import pytest
+
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import barnes_hut_tree_amd
+    barnes_hut_tree_amd.load_library()
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+def _nan_out(n):
+    return torch.full((n, 4), float("nan"), dtype=torch.float32, device="cuda")
+
+
+def _walk(t, n, eps, targets=None, flags=0):
+    out = _nan_out(n)
+    t.gravity(0.5, 1.0, eps, targets=targets, out=out, flags=flags)
+    return out.cpu().numpy()
+
+
+CASES = {
+    "plummer65536": lambda: W.plummer(1 << 16, seed=3),
+    "plummer_ragged100003": lambda: W.plummer(100003, seed=9),
+    "galaxy_pair200000": lambda: W.galaxy_pair(200_000, seed=4)[0],
+    "uniform300": lambda: W.uniform_cube(300, seed=7),
+    "uniform65": lambda: W.uniform_cube(65, seed=8),
+    "single": lambda: W.uniform_cube(1, seed=1),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_balanced_runs_walk_every_group_once(case):
+    import barnes_hut_tree_amd as bh
+    p = CASES[case]()
+    n = p.shape[0]
+    eps = 0.01
+    log("balanced runs", case, n)
+    t = bh.BarnesHut(n, 0, 63, 16, curve="hilbert")
+    t.build(torch.from_numpy(p).cuda())
+    first = _walk(t, n, eps)
+    assert np.all(np.isfinite(first)) or n == 1
+    for k in range(3):
+        again = _walk(t, n, eps)
+        assert np.array_equal(again, first, equal_nan=True), "call %d" % (k + 2)
+    # a rebuild of the same sources keeps the groups (and the history)
+    t.build(torch.from_numpy(p).cuda())
+    assert np.array_equal(_walk(t, n, eps), first, equal_nan=True)
+    caller_order = _walk(t, n, eps, flags=bh.WALK_UNSORTED)
+    assert np.array_equal(caller_order, first, equal_nan=True)
+    t.close()
+
+
+def test_history_follows_the_grouping():
+    """Self-gravity and separate targets of another count alternate on one
+    context: each walk's result equals that of a fresh context."""
+    import barnes_hut_tree_amd as bh
+    src = W.plummer(1 << 15, seed=5)
+    q = W.box_queries(50001, seed=21)
+    n, m = src.shape[0], q.shape[0]
+    qt = torch.from_numpy(q).cuda()
+    fresh = bh.BarnesHut(n, m, 63, 16, curve="hilbert")
+    fresh.build(torch.from_numpy(src).cuda())
+    ref_self = _walk(fresh, n, 0.01)
+    fresh.close()
+    fresh = bh.BarnesHut(n, m, 63, 16, curve="hilbert")
+    fresh.build(torch.from_numpy(src).cuda())
+    ref_q = _walk(fresh, m, 0.01, targets=qt)
+    fresh.close()
+    t = bh.BarnesHut(n, m, 63, 16, curve="hilbert")
+    t.build(torch.from_numpy(src).cuda())
+    for k in range(3):
+        log("alternating walks, round", k)
+        assert np.array_equal(_walk(t, n, 0.01), ref_self)
+        assert np.array_equal(_walk(t, n, 0.01), ref_self)
+        assert np.array_equal(_walk(t, m, 0.01, targets=qt), ref_q)
+        assert np.array_equal(_walk(t, m, 0.01, targets=qt), ref_q)
+        # a vote walk between them leaves the per-target walk's history alone
+        t.gravity(0.5, 1.0, 0.01, flags=bh.WALK_VOTE)
+    t.close()
+
+
+def test_fewer_sources_on_a_larger_context():
+    """A context built for more sources, rebuilt with fewer: the groups change,
+    so the walk starts again from equal runs, and then balances again."""
+    import barnes_hut_tree_amd as bh
+    big = W.plummer(1 << 16, seed=3)
+    small = W.plummer(20000, seed=6)
+    t = bh.BarnesHut(big.shape[0], 0, 63, 16, curve="hilbert")
+    t.build(torch.from_numpy(big).cuda())
+    for _ in range(2):
+        _walk(t, big.shape[0], 0.01)
+    ref = bh.BarnesHut(small.shape[0], 0, 63, 16, curve="hilbert")
+    ref.build(torch.from_numpy(small).cuda())
+    want = _walk(ref, small.shape[0], 0.01)
+    ref.close()
+    t.build(torch.from_numpy(small).cuda())
+    for k in range(3):
+        log("smaller rebuild, call", k)
+        assert np.array_equal(_walk(t, small.shape[0], 0.01), want)
+    t.close()
