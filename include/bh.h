@@ -122,7 +122,12 @@ bh_status bh_build(bh_ctx *ctx, const float *src_pos_mass, int64_t n, void *stre
  *   out_acc_pot   device, n_targets float4 rows (ax, ay, az, phi) in the
  *                 caller's order of the targets (for targets == NULL,
  *                 n_targets must equal the n given to bh_build).
- *   theta >= 0 (0 = exact direct sum), eps >= 0, G any finite value. */
+ *   theta >= 0 (0 = exact direct sum), eps >= 0, G any finite value.
+ * The context remembers each walk's time per group of 64 targets; when the
+ * next walk has the same groups (the same target count, self-gravity or not)
+ * and those times show the eight XCDs' equal runs of groups out of balance,
+ * it moves the runs' ends.  That changes only where each group runs: the
+ * results are the same bits either way. */
 bh_status bh_gravity(bh_ctx *ctx, const float *targets, int64_t n_targets, float theta,
                      float G, float eps, float *out_acc_pot, void *stream);
 
