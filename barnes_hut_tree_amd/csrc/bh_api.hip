@@ -47,6 +47,8 @@ struct bh_ctx {
     Node *wnodes = nullptr;           // per-call walk records (see launch_walk)
     uint32_t wn_cap = 0;              // records wnodes holds
     uint32_t *wbal = nullptr;         // the walk's XCD runs and per-group times
+    int *bal_want = nullptr;          // pinned, written by the device: the last walk's
+    int *bal_want_dev = nullptr;      //   times call for uneven XCD runs (its device address)
     uint32_t hist_groups = 0;         // groups wbal holds times for (0: none)
     int hist_kind = -1;               // 0: self-gravity, 1: separate targets
 
@@ -88,6 +90,7 @@ void free_all(bh_ctx *c)
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
     if (c->host_prm) (void)hipHostFree(c->host_prm);
+    if (c->bal_want) (void)hipHostFree(c->bal_want);
     for (hipEvent_t &e : c->ev)
         if (e) (void)hipEventDestroy(e);
 }
@@ -271,6 +274,13 @@ bh_status bh_create(bh_ctx **out, int64_t max_sources, int64_t max_targets,
                   hipSuccess;
     }
     ok &= hipHostMalloc((void **)&c->host_prm, sizeof(DevParams), hipHostMallocDefault) == hipSuccess;
+    if (hipHostMalloc((void **)&c->bal_want, sizeof(int), hipHostMallocMapped) == hipSuccess) {
+        *c->bal_want = 0;
+        ok &= hipHostGetDevicePointer((void **)&c->bal_want_dev, c->bal_want, 0) == hipSuccess;
+    } else {
+        c->bal_want = nullptr;
+        ok = false;
+    }
     ok &= dalloc(&c->bbox_part, 8 * 1024) == hipSuccess;
     ok &= dalloc(&c->keys, ns) == hipSuccess;
     ok &= dalloc(&c->keys_alt, ns) == hipSuccess;
@@ -425,6 +435,10 @@ static bh_status gravity_impl(bh_ctx *c, const float *targets, int64_t n_targets
     const uint32_t groups = walk_groups(nt);
     a.balance = balanced ? c->wbal : nullptr;
     a.balance_hist = balanced && c->hist_groups == groups && c->hist_kind == kind;
+    // the device's verdict on an earlier walk's times (read without waiting:
+    // it may lag a call behind); uneven runs need a grid with room for them
+    a.balance_runs = a.balance_hist && c->bal_want && __atomic_load_n(c->bal_want, __ATOMIC_RELAXED);
+    a.balance_want = balanced ? c->bal_want_dev : nullptr;
     if (a.unsorted) {
         a.self = targets == nullptr;
         if (targets) {

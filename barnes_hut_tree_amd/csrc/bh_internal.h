@@ -173,12 +173,16 @@ struct WalkArgs {
     float theta, G, eps;
     float4 *out;
     unsigned long long *count;  // optional interaction counter
-    // XCD balance of the sorted per-target walk (null: equal runs per XCD):
-    // the eight runs of groups for this walk, chosen from the previous walk's
-    // per-group times when balance_hist is set, and this walk's times (layout
-    // at kWalkBalanceHead)
+    // XCD balance of the sorted per-target walk.  balance (null: none) gets
+    // this walk's per-group times (layout at kWalkBalanceHead); balance_hist:
+    // it holds the previous walk's times for the same groups; balance_runs:
+    // walk the runs chosen from them (a grid with room for uneven runs), else
+    // the equal runs of xcd_block; balance_want (host-mapped, may be null)
+    // receives whether those times call for uneven runs
     uint32_t *balance;
     int balance_hist;
+    int balance_runs;
+    int *balance_want;
 };
 void launch_walk(const WalkArgs &a, hipStream_t s);
 // walk groups of 64 targets, and the most groups one XCD's run may take

@@ -572,7 +572,8 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
                                                        uint32_t n, float theta, float G,
                                                        float eps2, float4 *__restrict__ out,
                                                        unsigned long long *__restrict__ count,
-                                                       uint32_t *__restrict__ balance)
+                                                       uint32_t *__restrict__ balance,
+                                                       int runs)
 {
     const uint32_t lane = threadIdx.x & 63;
     // the group this wave walks: each XCD (workgroups are dealt to the eight
@@ -580,7 +581,7 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
     // together share the nodes near their targets in that XCD's L2; with
     // a balance buffer the runs are the ones balanced on the previous walk's times
     uint32_t blk;
-    if (balance) {
+    if (runs) {
         // the grid holds 8 cap workgroups, cap per XCD; an XCD whose run is
         // shorter lets its first ones return, while every XCD still has free
         // slots (at the end of the dispatch they would hold up the others)
@@ -651,16 +652,11 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
     }
 
     if (valid) out[slot] = make_float4(G * ax, G * ay, G * az, G * pot);
-    if (balance && lane == 0) {
-        // this group's time, and its share of the eighth of the groups it
-        // belongs to (which the next walk compares)
-        const uint32_t g = wave_base >> 6;
-        const uint32_t dt = (uint32_t)(__builtin_amdgcn_s_memrealtime() - t_start);
-        const float eighth = (float)g * 8.f / (float)walk_groups(n);
-        balance[kWalkBalanceHead + g] = dt;
-        atomicAdd(reinterpret_cast<unsigned long long *>(balance + 16) + min(7u, (uint32_t)eighth),
-                  (unsigned long long)dt);
-    }
+    // this group's time (one plain store: the per-wave device atomic this
+    // replaced serialised on its few addresses)
+    if (balance && lane == 0)
+        balance[kWalkBalanceHead + (wave_base >> 6)] =
+            (uint32_t)(__builtin_amdgcn_s_memrealtime() - t_start);
     if (COUNT) {
         unsigned long long cnt = valid ? n_int : 0u;
         for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
@@ -675,68 +671,116 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
 // value every per-target walk form compares r^2 + eps^2 with, and the skip as
 // a byte offset, so the assembly loop uses both without arithmetic.  Written
 // only when the loop will use them (see k_walk).
-// The XCD runs of the coming walk.  xb[0..8]: the first group of each run
-// (xb[8] = ng); xb[16..31]: eight 64-bit sums of the per-group times of the
-// previous walk over the eighths of the groups, added by its waves.  Equal
-// runs unless those sums are more than kWalkRebalance out of balance; then
-// eight contiguous runs, on a grid of ng / 256 groups, whose sums of the
-// previous walk's per-group times are as equal as the cap of `cap` groups
-// per run allows.  (Equal runs of a centrally symmetric input coincide with
-// its root octants, so each XCD's L2 holds one octant's subtree; runs moved
-// off them to even out a few per cent of time measured slower.)  Clears the
-// sums for the coming walk.  One block of 256 threads.  Every run is at most
-// `cap` groups and 8 cap >= ng, so the walk's grid of 8 cap workgroups walks
-// every group once.
+// The XCD balance before a walk, from the previous walk's per-group times
+// (xb[kWalkBalanceHead + g]); xb[0..8] receive the first group of each XCD's
+// run (xb[8] = ng).  The times are summed over the eighths of the groups (the
+// equal runs of xcd_block); when the largest sum is more than kWalkRebalance
+// above their mean and the waves lived longer than kWalkBalanceMinTicks on
+// average, *want = 1 (the host then launches the next walks with room for
+// uneven runs), else 0.  With `runs` (such a walk) and *want = 1, the runs
+// become eight contiguous ranges with equal sums of the previous times, as far
+// as the cap of `cap` groups per run allows; otherwise the equal runs.  (Equal
+// runs of a centrally symmetric input coincide with its root octants, so each
+// XCD's L2 holds one octant's subtree; runs moved off them to even out a few
+// per cent of time measured slower.)  One block of 256 threads, the times read
+// four per thread and load, in order.  Every run is at most `cap` groups and
+// 8 cap >= ng, so a grid of 8 cap workgroups walks every group once.
 constexpr double kWalkRebalance = 1.08;
+// Waves that live less than this on average (s_memrealtime ticks, 100 MHz:
+// 100 us) are bound by the rate at which workgroups are dispatched, which
+// equal runs already share evenly.
+constexpr unsigned long long kWalkBalanceMinTicks = 10000;
 
-__device__ void walk_bounds(uint32_t ng, uint32_t cap, bool hist, uint32_t *__restrict__ xb)
+__device__ void walk_bounds(uint32_t ng, uint32_t cap, bool hist, bool runs,
+                            uint32_t *__restrict__ xb, int *__restrict__ want)
 {
     const uint32_t *__restrict__ wdur = xb + kWalkBalanceHead;
-    __shared__ unsigned long long part[256];
+    __shared__ unsigned long long esum[8];
+    __shared__ unsigned long long scan[256];
     __shared__ uint32_t ideal[8];
     __shared__ int balance;
-    unsigned long long *sums = reinterpret_cast<unsigned long long *>(xb + 16);
     const uint32_t t = threadIdx.x;
-    if (t == 0) {
-        int bal = 0;
-        if (hist) {
-            unsigned long long total = 0, most = 0;
-            for (int x = 0; x < 8; ++x) {
-                total += sums[x];
-                most = max(most, sums[x]);
+    if (t < 8) {
+        esum[t] = 0;
+        ideal[t] = 0;
+    }
+    __syncthreads();
+    if (hist) {
+        // sums over the eighths of the groups (group g in eighth floor(8 g / ng),
+        // which starts at ceil(x ng / 8)); a thread's groups only increase
+        // (sixteen loads in flight per thread: four tiles of 1024 groups)
+        uint32_t x = 0, next = (ng + 7) >> 3;
+        unsigned long long acc = 0;
+        for (uint32_t g0 = 4 * t; g0 < ng; g0 += 4096) {
+            uint32_t v[16];
+#pragma unroll
+            for (uint32_t j = 0; j < 16; ++j) {
+                const uint32_t g = g0 + 1024 * (j >> 2) + (j & 3);
+                v[j] = g < ng ? wdur[g] : 0u;
             }
-            bal = (double)most * 8.0 > kWalkRebalance * (double)total;
+#pragma unroll
+            for (uint32_t j = 0; j < 16; ++j) {
+                const uint32_t g = g0 + 1024 * (j >> 2) + (j & 3);
+                if (g >= ng) continue;
+                while (g >= next) {
+                    if (acc) atomicAdd(&esum[x], acc);
+                    acc = 0;
+                    ++x;
+                    next = ((x + 1) * ng + 7) >> 3;   // ng < 2^26: no overflow
+                }
+                acc += v[j];
+            }
         }
-        balance = bal;
+        if (acc) atomicAdd(&esum[x], acc);
+    }
+    __syncthreads();
+    unsigned long long total = 0, most = 0;
+    for (int x = 0; x < 8; ++x) {
+        total += esum[x];
+        most = max(most, esum[x]);
+    }
+    if (t == 0) {
+        const int bal = hist && (double)most * 8.0 > kWalkRebalance * (double)total &&
+                        total > (unsigned long long)ng * kWalkBalanceMinTicks;
+        if (want) *want = bal;
+        balance = bal && runs;
     }
     __syncthreads();
     if (!balance) {
         if (t <= 8) xb[t] = t * (ng >> 3) + min(t, ng & 7u);
-        if (t < 8) sums[t] = 0;
         return;
     }
-    // per-thread sums over chunks of consecutive groups, then an inclusive scan
-    const uint32_t chunk = (ng + 255) / 256;
-    const uint32_t g0 = min(ng, t * chunk), g1 = min(ng, g0 + chunk);
-    unsigned long long sum = 0;
-#pragma unroll 8
-    for (uint32_t g = g0; g < g1; ++g) sum += wdur[g];
-    part[t] = sum;
-    __syncthreads();
-    for (uint32_t o = 1; o < 256; o <<= 1) {
-        const unsigned long long v = t >= o ? part[t - o] : 0ull;
+    // the first group b with the times of the groups before it reaching x/8
+    // of the total, for x = 1..7: tiles of 1024 groups, four per thread, a
+    // block scan per tile
+    unsigned long long run = 0;
+    for (uint32_t base = 0; base < ng; base += 1024) {
+        const uint32_t g0 = base + 4 * t;
+        unsigned long long d[4], mine = 0;
+        for (uint32_t k = 0; k < 4; ++k) {
+            d[k] = g0 + k < ng ? wdur[g0 + k] : 0ull;
+            mine += d[k];
+        }
+        scan[t] = mine;
         __syncthreads();
-        part[t] += v;
+        for (uint32_t o = 1; o < 256; o <<= 1) {
+            const unsigned long long v = t >= o ? scan[t - o] : 0ull;
+            __syncthreads();
+            scan[t] += v;
+            __syncthreads();
+        }
+        // before: the times of all groups before g0
+        unsigned long long before = run + scan[t] - mine;
+        for (uint32_t k = 0; k < 4 && g0 + k < ng; ++k) {
+            // groups [0, g0 + k) reach `before`, [0, g0 + k + 1) reach `before + d[k]`
+            for (uint32_t x = 1; x < 8; ++x) {
+                const unsigned long long target = total * x / 8;
+                if (before < target && before + d[k] >= target) ideal[x] = g0 + k + 1;
+            }
+            before += d[k];
+        }
+        run += scan[255];
         __syncthreads();
-    }
-    if (t >= 1 && t < 8) {
-        // the chunk boundary nearest to where the times reach t/8 of the total
-        const unsigned long long target = part[255] * t / 8;
-        uint32_t k = 0;
-        while (k < 255 && part[k] < target) ++k;
-        const unsigned long long before = k ? part[k - 1] : 0ull;
-        const uint32_t kb = target - before <= part[k] - target ? k : k + 1;
-        ideal[t] = min(ng, kb * chunk);
     }
     __syncthreads();
     if (t == 0) {
@@ -753,7 +797,6 @@ __device__ void walk_bounds(uint32_t ng, uint32_t cap, bool hist, uint32_t *__re
         }
         xb[8] = ng;
     }
-    if (t < 8) sums[t] = 0;
 }
 
 __global__ __launch_bounds__(256) void k_walk_nodes(const Node *__restrict__ nodes,
@@ -761,9 +804,10 @@ __global__ __launch_bounds__(256) void k_walk_nodes(const Node *__restrict__ nod
                                                     float theta, float eps2, uint32_t wn_cap,
                                                     Node *__restrict__ wnodes,
                                                     uint32_t ng, uint32_t cap, int hist,
-                                                    uint32_t *__restrict__ balance)
+                                                    int runs, uint32_t *__restrict__ balance,
+                                                    int *__restrict__ want)
 {
-    if (balance && blockIdx.x == 0) walk_bounds(ng, cap, hist != 0, balance);
+    if (balance && blockIdx.x == 0) walk_bounds(ng, cap, hist != 0, runs != 0, balance, want);
     if (prm->status != 0) return;
     const uint32_t nn = prm->n_nodes;
     if (!(nn < kAsmMaxNodes && nn < wn_cap)) return;
@@ -796,10 +840,10 @@ template <bool SOFT, bool SELF, bool COUNT, bool VOTE, bool UNSORTED>
 void launch5(const WalkArgs &a, hipStream_t s)
 {
     const uint32_t groups = walk_groups(a.n_targets);
-    const uint32_t grid = a.balance ? 8 * walk_xcd_cap(groups) : groups;
+    const uint32_t grid = a.balance_runs ? 8 * walk_xcd_cap(groups) : groups;
     hipLaunchKernelGGL((k_walk<SOFT, SELF, COUNT, VOTE, UNSORTED>), dim3(grid), dim3(kWalkThreads),
                        0, s, a.nodes, a.wnodes, a.wn_cap, a.src, a.tpos, a.tmap, a.prm, a.n_targets, a.theta, a.G,
-                       a.eps * a.eps, a.out, a.count, a.balance);
+                       a.eps * a.eps, a.out, a.count, a.balance, a.balance_runs);
 }
 
 template <bool SOFT, bool SELF, bool COUNT>
@@ -837,13 +881,15 @@ void launch_walk(const WalkArgs &args, hipStream_t s)
     if (a.vote || a.unsorted || a.wn_cap == 0 || !a.balance) {
         a.balance = nullptr;
         a.balance_hist = 0;
+        a.balance_want = nullptr;
     }
+    if (!a.balance || !a.balance_hist) a.balance_runs = 0;
     if (!a.vote && a.wn_cap > 0) {
         const uint32_t blocks = (uint32_t)std::min<uint64_t>((a.wn_cap + 255) / 256, 2048);
         const uint32_t groups = walk_groups(a.n_targets);
         hipLaunchKernelGGL(k_walk_nodes, dim3(blocks), dim3(256), 0, s, a.nodes, a.prm, a.theta,
                            a.eps * a.eps, a.wn_cap, a.wnodes, groups, walk_xcd_cap(groups),
-                           a.balance_hist, a.balance);
+                           a.balance_hist, a.balance_runs, a.balance, a.balance_want);
     }
     // Plummer softening with eps^2 > 0 never meets r^2 + eps^2 == 0
     if (a.eps * a.eps > 0.f) launch1<true>(a, s); else launch1<false>(a, s);
