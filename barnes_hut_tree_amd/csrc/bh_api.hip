@@ -51,6 +51,10 @@ struct bh_ctx {
     int *bal_want_dev = nullptr;      //   times call for uneven XCD runs (its device address)
     uint32_t hist_groups = 0;         // groups wbal holds times for (0: none)
     int hist_kind = -1;               // 0: self-gravity, 1: separate targets
+    bool hist_new = false;            // those times are not yet looked at
+    uint32_t runs_groups = 0;         // groups wbal holds runs for
+    int runs_kind = -1;
+    uint32_t walk_calls = 0;          // per-target walks so far (times kept every 4th)
 
     uint64_t *tkeys = nullptr, *tkeys_alt = nullptr;
     uint32_t *tvals = nullptr, *tvals_alt = nullptr;
@@ -146,8 +150,6 @@ static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 struct StaticDevice {
     unsigned char *base = nullptr;   // this device's copy of `scratch`
     bool ready = false;
-    int64_t hist_n = -1;             // sources of the last walk whose per-group times
-    uint32_t hist_groups = 0;        // `scratch` holds (the layout depends on n)
 };
 StaticDevice g_static[kStaticMaxDevices];
 std::mutex g_static_mu;
@@ -184,7 +186,6 @@ size_t static_layout(bh_ctx *c, unsigned char *base, uint32_t n)
     take(&c->nodes, (size_t)c->node_cap + 1);
     c->wn_cap = walk_records(n, c->bits, c->leaf_cap, c->node_cap);
     take(&c->wnodes, (size_t)c->wn_cap);
-    take(&c->wbal, (size_t)kWalkBalanceHead + walk_groups(n));
     return off;
 }
 
@@ -383,6 +384,9 @@ static const uint32_t *sort_targets(bh_ctx *c, const float *targets, uint32_t nt
 // grid on the root cube, 4 sort passes) serve as well as the tree's own.
 constexpr int kTargetOrderBits = 10;
 
+// every this many per-target walks of one context store their per-group times
+constexpr uint32_t kWalkTimedEvery = 4;
+
 static bh_status gravity_impl(bh_ctx *c, const float *targets, int64_t n_targets, float theta,
                               float G, float eps, uint32_t flags, float *out, uint64_t *count,
                               void *stream)
@@ -430,14 +434,24 @@ static bh_status gravity_impl(bh_ctx *c, const float *targets, int64_t n_targets
     a.unsorted = (flags & BH_WALK_UNSORTED) != 0;
     // the per-target walk in key order balances its XCD runs on the previous
     // such walk's per-group times when that walk had the same groups
-    const bool balanced = !a.vote && !a.unsorted && c->wn_cap > 0;
+    const bool balanced = !a.vote && !a.unsorted && c->wn_cap > 0 && c->bal_want;
     const int kind = targets ? 1 : 0;
     const uint32_t groups = walk_groups(nt);
+    // Balance of the XCD runs: every kWalkTimedEvery-th walk of the same
+    // groups stores its per-group times (each wave reads the clock twice);
+    // the walk after it chooses runs from them and the ones between keep
+    // those runs.  The device's verdict (read without waiting, so it may lag
+    // a call behind) says whether they are uneven, which needs a grid with
+    // room for them.
+    const bool same_hist = c->hist_groups == groups && c->hist_kind == kind;
+    const bool same_runs = c->runs_groups == groups && c->runs_kind == kind;
     a.balance = balanced ? c->wbal : nullptr;
-    a.balance_hist = balanced && c->hist_groups == groups && c->hist_kind == kind;
-    // the device's verdict on an earlier walk's times (read without waiting:
-    // it may lag a call behind); uneven runs need a grid with room for them
-    a.balance_runs = a.balance_hist && c->bal_want && __atomic_load_n(c->bal_want, __ATOMIC_RELAXED);
+    a.balance_eval = balanced && same_hist && c->hist_new;
+    a.balance_fresh = balanced && !same_runs && !a.balance_eval;
+    a.balance_runs = balanced && (same_runs || a.balance_eval) && c->bal_want &&
+                     __atomic_load_n(c->bal_want, __ATOMIC_RELAXED);
+    a.balance_record = balanced && (!same_hist || c->walk_calls < 2 ||
+                                    c->walk_calls % kWalkTimedEvery == 0);
     a.balance_want = balanced ? c->bal_want_dev : nullptr;
     if (a.unsorted) {
         a.self = targets == nullptr;
@@ -464,8 +478,17 @@ static bh_status gravity_impl(bh_ctx *c, const float *targets, int64_t n_targets
     launch_walk(a, s);
     record(c, 6, s);
     if (balanced) {
-        c->hist_groups = groups;
-        c->hist_kind = kind;
+        if (a.balance_eval || a.balance_fresh) {
+            c->runs_groups = groups;
+            c->runs_kind = kind;
+        }
+        if (a.balance_eval) c->hist_new = false;
+        if (a.balance_record) {
+            c->hist_groups = groups;
+            c->hist_kind = kind;
+            c->hist_new = true;
+        }
+        ++c->walk_calls;
     }
     return launch_status();
 }
@@ -841,20 +864,9 @@ bh_status bh_gravity_static(const float *src_pos_mass, int64_t n, const bh_build
     bh_status st = static_base(c.device, &base);
     if (st != BH_OK) return st;
     static_layout(&c, base, (uint32_t)n);
-    {
-        std::lock_guard<std::mutex> lock(g_static_mu);
-        c.hist_groups = g_static[c.device].hist_n == n ? g_static[c.device].hist_groups : 0;
-        c.hist_kind = 0;
-    }
     st = bh_build(&c, src_pos_mass, n, stream);
     if (st != BH_OK) return st;
-    st = gravity_impl(&c, nullptr, n, theta, G, eps, 0u, out_acc_pot, nullptr, stream);
-    {
-        std::lock_guard<std::mutex> lock(g_static_mu);
-        g_static[c.device].hist_n = st == BH_OK ? n : -1;
-        g_static[c.device].hist_groups = st == BH_OK ? c.hist_groups : 0;
-    }
-    return st;
+    return gravity_impl(&c, nullptr, n, theta, G, eps, 0u, out_acc_pot, nullptr, stream);
 }
 
 }  // extern "C"

@@ -173,15 +173,19 @@ struct WalkArgs {
     float theta, G, eps;
     float4 *out;
     unsigned long long *count;  // optional interaction counter
-    // XCD balance of the sorted per-target walk.  balance (null: none) gets
-    // this walk's per-group times (layout at kWalkBalanceHead); balance_hist:
-    // it holds the previous walk's times for the same groups; balance_runs:
-    // walk the runs chosen from them (a grid with room for uneven runs), else
-    // the equal runs of xcd_block; balance_want (host-mapped, may be null)
-    // receives whether those times call for uneven runs
+    // XCD balance of the sorted per-target walk (layout of the buffer at
+    // kWalkBalanceHead; null: none).  balance_eval: the buffer holds times of
+    // a recent walk of the same groups not yet looked at, from which to choose
+    // the runs (and set *balance_want, host-mapped, may be null); else keep
+    // the runs it holds (balance_fresh: none for these groups, write the equal
+    // runs).  balance_runs: walk those runs (a grid with room for uneven
+    // runs), else the equal runs of xcd_block.  balance_record: store this
+    // walk's per-group times.
     uint32_t *balance;
-    int balance_hist;
+    int balance_eval;
+    int balance_fresh;
     int balance_runs;
+    int balance_record;
     int *balance_want;
 };
 void launch_walk(const WalkArgs &a, hipStream_t s);

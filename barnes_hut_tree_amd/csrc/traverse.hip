@@ -573,7 +573,7 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
                                                        float eps2, float4 *__restrict__ out,
                                                        unsigned long long *__restrict__ count,
                                                        uint32_t *__restrict__ balance,
-                                                       int runs)
+                                                       int runs, int record)
 {
     const uint32_t lane = threadIdx.x & 63;
     // the group this wave walks: each XCD (workgroups are dealt to the eight
@@ -599,7 +599,7 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
     if (wave_base >= n) return;
     // the group's start time, kept in vector registers (scalar registers
     // decide how many waves stay resident)
-    uint64_t t_start = balance ? __builtin_amdgcn_s_memrealtime() : 0;
+    uint64_t t_start = record ? __builtin_amdgcn_s_memrealtime() : 0;
     asm volatile("" : "+v"(t_start));
     uint32_t i = c, slot = c;   // self index (Morton rank) and output slot
     if (valid) {
@@ -654,7 +654,7 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
     if (valid) out[slot] = make_float4(G * ax, G * ay, G * az, G * pot);
     // this group's time (one plain store: the per-wave device atomic this
     // replaced serialised on its few addresses)
-    if (balance && lane == 0)
+    if (record && lane == 0)
         balance[kWalkBalanceHead + (wave_base >> 6)] =
             (uint32_t)(__builtin_amdgcn_s_memrealtime() - t_start);
     if (COUNT) {
@@ -672,76 +672,89 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
 // a byte offset, so the assembly loop uses both without arithmetic.  Written
 // only when the loop will use them (see k_walk).
 // The XCD balance before a walk, from the previous walk's per-group times
-// (xb[kWalkBalanceHead + g]); xb[0..8] receive the first group of each XCD's
-// run (xb[8] = ng).  The times are summed over the eighths of the groups (the
-// equal runs of xcd_block); when the largest sum is more than kWalkRebalance
-// above their mean and the waves lived longer than kWalkBalanceMinTicks on
-// average, *want = 1 (the host then launches the next walks with room for
-// uneven runs), else 0.  With `runs` (such a walk) and *want = 1, the runs
-// become eight contiguous ranges with equal sums of the previous times, as far
-// as the cap of `cap` groups per run allows; otherwise the equal runs.  (Equal
-// runs of a centrally symmetric input coincide with its root octants, so each
-// XCD's L2 holds one octant's subtree; runs moved off them to even out a few
-// per cent of time measured slower.)  One block of 256 threads, the times read
-// four per thread and load, in order.  Every run is at most `cap` groups and
-// 8 cap >= ng, so a grid of 8 cap workgroups walks every group once.
+// (xb[kWalkBalanceHead + g], every kWalkBalanceSample-th read); xb[0..8]
+// receive the first group of each XCD's run (xb[8] = ng).  The sampled times
+// are summed over 256 chunks of consecutive groups (chunk c starts at
+// ceil(c ng / 256); chunks 32x..32x+31 are the eighth x of the groups, the
+// equal runs of xcd_block).  When the largest
+// eighth is more than kWalkRebalance above their mean and the waves lived
+// longer than kWalkBalanceMinTicks on average, *want = 1 (the host then
+// launches the next walks with room for uneven runs), else 0.  With `runs`
+// (such a walk) and *want = 1, the runs become eight contiguous ranges, ending
+// on chunk boundaries, whose sums of the previous times are as equal as the
+// cap of `cap` groups per run allows; otherwise the equal runs.  (Equal runs
+// of a centrally symmetric input coincide with its root octants, so each XCD's
+// L2 holds one octant's subtree; runs moved off them to even out a few per cent
+// of time measured slower.)  One block of 256 threads.  Every run is at most
+// `cap` groups and 8 cap >= ng, so a grid of 8 cap workgroups walks every
+// group once.
 constexpr double kWalkRebalance = 1.08;
 // Waves that live less than this on average (s_memrealtime ticks, 100 MHz:
 // 100 us) are bound by the rate at which workgroups are dispatched, which
 // equal runs already share evenly.
 constexpr unsigned long long kWalkBalanceMinTicks = 10000;
+// The balance reads every 8th group's time: an eighth of the groups holds
+// 256 samples or more from 2^17 targets on, and the pass stays a few loads
+// per thread.
+constexpr uint32_t kWalkBalanceSample = 8;
+
+__device__ inline uint32_t walk_chunk_start(uint32_t c, uint32_t ng)
+{
+    return (uint32_t)(((uint64_t)c * ng + 255) >> 8);
+}
 
 __device__ void walk_bounds(uint32_t ng, uint32_t cap, bool hist, bool runs,
                             uint32_t *__restrict__ xb, int *__restrict__ want)
 {
     const uint32_t *__restrict__ wdur = xb + kWalkBalanceHead;
-    __shared__ unsigned long long esum[8];
-    __shared__ unsigned long long scan[256];
+    __shared__ unsigned long long csum[256];
     __shared__ uint32_t ideal[8];
     __shared__ int balance;
     const uint32_t t = threadIdx.x;
-    if (t < 8) {
-        esum[t] = 0;
-        ideal[t] = 0;
-    }
+    csum[t] = 0;
+    if (t < 8) ideal[t] = 0;
     __syncthreads();
     if (hist) {
-        // sums over the eighths of the groups (group g in eighth floor(8 g / ng),
-        // which starts at ceil(x ng / 8)); a thread's groups only increase
-        // (sixteen loads in flight per thread: four tiles of 1024 groups)
-        uint32_t x = 0, next = (ng + 7) >> 3;
+        // every kWalkBalanceSample-th group's time (sixteen loads in flight per
+        // thread); a thread's groups only increase: add its run of times in
+        // one chunk, then move on
+        constexpr uint32_t S = kWalkBalanceSample;
+        uint32_t c = 0, next = walk_chunk_start(1, ng);
         unsigned long long acc = 0;
-        for (uint32_t g0 = 4 * t; g0 < ng; g0 += 4096) {
+        for (uint32_t g0 = S * t; g0 < ng; g0 += 16 * 256 * S) {
             uint32_t v[16];
 #pragma unroll
             for (uint32_t j = 0; j < 16; ++j) {
-                const uint32_t g = g0 + 1024 * (j >> 2) + (j & 3);
+                const uint32_t g = g0 + 256 * S * j;
                 v[j] = g < ng ? wdur[g] : 0u;
             }
 #pragma unroll
             for (uint32_t j = 0; j < 16; ++j) {
-                const uint32_t g = g0 + 1024 * (j >> 2) + (j & 3);
+                const uint32_t g = g0 + 256 * S * j;
                 if (g >= ng) continue;
                 while (g >= next) {
-                    if (acc) atomicAdd(&esum[x], acc);
+                    if (acc) atomicAdd(&csum[c], acc);
                     acc = 0;
-                    ++x;
-                    next = ((x + 1) * ng + 7) >> 3;   // ng < 2^26: no overflow
+                    ++c;
+                    next = walk_chunk_start(c + 1, ng);
                 }
                 acc += v[j];
             }
         }
-        if (acc) atomicAdd(&esum[x], acc);
+        if (acc) atomicAdd(&csum[c], acc);
     }
     __syncthreads();
-    unsigned long long total = 0, most = 0;
-    for (int x = 0; x < 8; ++x) {
-        total += esum[x];
-        most = max(most, esum[x]);
-    }
     if (t == 0) {
+        unsigned long long total = 0, most = 0;
+        for (int x = 0; x < 8; ++x) {
+            unsigned long long e = 0;
+            for (int k = 0; k < 32; ++k) e += csum[32 * x + k];
+            total += e;
+            most = max(most, e);
+        }
+        const unsigned long long samples = (ng + kWalkBalanceSample - 1) / kWalkBalanceSample;
         const int bal = hist && (double)most * 8.0 > kWalkRebalance * (double)total &&
-                        total > (unsigned long long)ng * kWalkBalanceMinTicks;
+                        total > samples * kWalkBalanceMinTicks;
         if (want) *want = bal;
         balance = bal && runs;
     }
@@ -750,37 +763,21 @@ __device__ void walk_bounds(uint32_t ng, uint32_t cap, bool hist, bool runs,
         if (t <= 8) xb[t] = t * (ng >> 3) + min(t, ng & 7u);
         return;
     }
-    // the first group b with the times of the groups before it reaching x/8
-    // of the total, for x = 1..7: tiles of 1024 groups, four per thread, a
-    // block scan per tile
-    unsigned long long run = 0;
-    for (uint32_t base = 0; base < ng; base += 1024) {
-        const uint32_t g0 = base + 4 * t;
-        unsigned long long d[4], mine = 0;
-        for (uint32_t k = 0; k < 4; ++k) {
-            d[k] = g0 + k < ng ? wdur[g0 + k] : 0ull;
-            mine += d[k];
-        }
-        scan[t] = mine;
+    // inclusive scan of the chunk sums
+    for (uint32_t o = 1; o < 256; o <<= 1) {
+        const unsigned long long v = t >= o ? csum[t - o] : 0ull;
         __syncthreads();
-        for (uint32_t o = 1; o < 256; o <<= 1) {
-            const unsigned long long v = t >= o ? scan[t - o] : 0ull;
-            __syncthreads();
-            scan[t] += v;
-            __syncthreads();
-        }
-        // before: the times of all groups before g0
-        unsigned long long before = run + scan[t] - mine;
-        for (uint32_t k = 0; k < 4 && g0 + k < ng; ++k) {
-            // groups [0, g0 + k) reach `before`, [0, g0 + k + 1) reach `before + d[k]`
-            for (uint32_t x = 1; x < 8; ++x) {
-                const unsigned long long target = total * x / 8;
-                if (before < target && before + d[k] >= target) ideal[x] = g0 + k + 1;
-            }
-            before += d[k];
-        }
-        run += scan[255];
+        csum[t] += v;
         __syncthreads();
+    }
+    if (t >= 1 && t < 8) {
+        // the chunk boundary nearest to where the times reach t/8 of the total
+        const unsigned long long target = csum[255] * t / 8;
+        uint32_t k = 0;
+        while (k < 255 && csum[k] < target) ++k;
+        const unsigned long long before = k ? csum[k - 1] : 0ull;
+        const uint32_t kb = target - before <= csum[k] - target ? k : k + 1;
+        ideal[t] = walk_chunk_start(kb, ng);
     }
     __syncthreads();
     if (t == 0) {
@@ -803,11 +800,15 @@ __global__ __launch_bounds__(256) void k_walk_nodes(const Node *__restrict__ nod
                                                     const DevParams *__restrict__ prm,
                                                     float theta, float eps2, uint32_t wn_cap,
                                                     Node *__restrict__ wnodes,
-                                                    uint32_t ng, uint32_t cap, int hist,
-                                                    int runs, uint32_t *__restrict__ balance,
+                                                    uint32_t ng, uint32_t cap, int eval,
+                                                    int fresh, int runs,
+                                                    uint32_t *__restrict__ balance,
                                                     int *__restrict__ want)
 {
-    if (balance && blockIdx.x == 0) walk_bounds(ng, cap, hist != 0, runs != 0, balance, want);
+    // new runs from recent times, or the equal runs for groups without any;
+    // otherwise the runs chosen last time stand
+    if (balance && blockIdx.x == 0 && (eval || fresh))
+        walk_bounds(ng, cap, eval != 0, runs != 0, balance, want);
     if (prm->status != 0) return;
     const uint32_t nn = prm->n_nodes;
     if (!(nn < kAsmMaxNodes && nn < wn_cap)) return;
@@ -843,7 +844,8 @@ void launch5(const WalkArgs &a, hipStream_t s)
     const uint32_t grid = a.balance_runs ? 8 * walk_xcd_cap(groups) : groups;
     hipLaunchKernelGGL((k_walk<SOFT, SELF, COUNT, VOTE, UNSORTED>), dim3(grid), dim3(kWalkThreads),
                        0, s, a.nodes, a.wnodes, a.wn_cap, a.src, a.tpos, a.tmap, a.prm, a.n_targets, a.theta, a.G,
-                       a.eps * a.eps, a.out, a.count, a.balance, a.balance_runs);
+                       a.eps * a.eps, a.out, a.count, a.balance, a.balance_runs,
+                       a.balance_record);
 }
 
 template <bool SOFT, bool SELF, bool COUNT>
@@ -880,16 +882,16 @@ void launch_walk(const WalkArgs &args, hipStream_t s)
     WalkArgs a = args;
     if (a.vote || a.unsorted || a.wn_cap == 0 || !a.balance) {
         a.balance = nullptr;
-        a.balance_hist = 0;
+        a.balance_eval = a.balance_fresh = a.balance_runs = a.balance_record = 0;
         a.balance_want = nullptr;
     }
-    if (!a.balance || !a.balance_hist) a.balance_runs = 0;
     if (!a.vote && a.wn_cap > 0) {
         const uint32_t blocks = (uint32_t)std::min<uint64_t>((a.wn_cap + 255) / 256, 2048);
         const uint32_t groups = walk_groups(a.n_targets);
         hipLaunchKernelGGL(k_walk_nodes, dim3(blocks), dim3(256), 0, s, a.nodes, a.prm, a.theta,
                            a.eps * a.eps, a.wn_cap, a.wnodes, groups, walk_xcd_cap(groups),
-                           a.balance_hist, a.balance_runs, a.balance, a.balance_want);
+                           a.balance_eval, a.balance_fresh, a.balance_runs, a.balance,
+                           a.balance_want);
     }
     // Plummer softening with eps^2 > 0 never meets r^2 + eps^2 == 0
     if (a.eps * a.eps > 0.f) launch1<true>(a, s); else launch1<false>(a, s);
