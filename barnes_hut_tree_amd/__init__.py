@@ -32,7 +32,7 @@ EXPORTS = ("bh_create", "bh_build", "bh_gravity", "bh_gravity_counted", "bh_grav
            "bh_leapfrog_step", "bh_diagnostics", "bh_sync", "bh_destroy",
            "bh_status_string", "bh_get_keys", "bh_get_node_count", "bh_get_nodes", "bh_get_bbox",
            "bh_set_profiling", "bh_get_profile", "bh_node_hmax", "bh_get_cells",
-           "bh_set_counting", "bh_get_interactions", "bh_gravity_static")
+           "bh_set_counting", "bh_get_interactions", "bh_gravity_static", "bh_get_walk_runs")
 
 NODE_DTYPE_FIELDS = [("com_x", "f4"), ("com_y", "f4"), ("com_z", "f4"), ("mass", "f4"),
                      ("start", "u4"), ("count", "u4"), ("skip", "u4"), ("meta", "u4")]
@@ -92,6 +92,7 @@ def load_library():
         "bh_set_counting": [P, i32],
         "bh_get_interactions": [P, ctypes.POINTER(ctypes.c_uint64)],
         "bh_gravity_static": [P, i64, ctypes.POINTER(_Params), f32, f32, f32, P, P],
+        "bh_get_walk_runs": [P, P, ctypes.POINTER(ctypes.c_int32)],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -268,6 +269,17 @@ class BarnesHut:
         """Count interactions of every following gravity() call that has no
         counter of its own (bh_set_counting); read with interactions()."""
         _check(load_library().bh_set_counting(self._h, int(bool(on))), "bh_set_counting")
+
+    def walk_runs(self):
+        """(uneven, starts) of the last per-target walk (bh_get_walk_runs):
+        whether it walked XCD runs balanced on an earlier walk's times, and
+        then the first group of each of the eight runs plus the group count."""
+        import numpy as np
+        starts = np.zeros(9, np.uint32)
+        uneven = ctypes.c_int32()
+        _check(load_library().bh_get_walk_runs(self._h, ctypes.c_void_p(starts.ctypes.data),
+                                               ctypes.byref(uneven)), "bh_get_walk_runs")
+        return bool(uneven.value), (starts.tolist() if uneven.value else None)
 
     def interactions(self):
         """Interactions of the last counted gravity() call (bh_get_interactions)."""

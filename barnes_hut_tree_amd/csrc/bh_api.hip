@@ -55,6 +55,7 @@ struct bh_ctx {
     uint32_t runs_groups = 0;         // groups wbal holds runs for
     int runs_kind = -1;
     uint32_t walk_calls = 0;          // per-target walks so far (times kept every 4th)
+    int last_runs = -1;               // the last per-target walk used uneven runs (-1: none yet)
 
     uint64_t *tkeys = nullptr, *tkeys_alt = nullptr;
     uint32_t *tvals = nullptr, *tvals_alt = nullptr;
@@ -483,6 +484,7 @@ static bh_status gravity_impl(bh_ctx *c, const float *targets, int64_t n_targets
             c->runs_kind = kind;
         }
         if (a.balance_eval) c->hist_new = false;
+        c->last_runs = a.balance_runs ? 1 : 0;
         if (a.balance_record) {
             c->hist_groups = groups;
             c->hist_kind = kind;
@@ -780,6 +782,18 @@ bh_status bh_set_counting(bh_ctx *c, int enable)
 {
     if (!c) return BH_ERR_INVALID;
     c->counting = enable != 0;
+    return BH_OK;
+}
+
+bh_status bh_get_walk_runs(bh_ctx *c, uint32_t *starts, int32_t *uneven)
+{
+    if (!c || !uneven || c->last_runs < 0) return BH_ERR_INVALID;
+    *uneven = c->last_runs;
+    if (!starts) return BH_OK;
+    if (hipMemcpyAsync(starts, c->wbal, 9 * sizeof(uint32_t), hipMemcpyDeviceToHost,
+                       c->last_stream) != hipSuccess ||
+        hipStreamSynchronize(c->last_stream) != hipSuccess)
+        return BH_ERR_HIP;
     return BH_OK;
 }
 

@@ -367,6 +367,15 @@ bh_status bh_get_bbox(bh_ctx *ctx, double *lo, double *hi, double *L, void *stre
 bh_status bh_set_profiling(bh_ctx *ctx, int enable);
 bh_status bh_get_profile(bh_ctx *ctx, float *ms, int n);
 
+/* How the last per-target walk (bh_gravity, bh_gravity_counted) shared its
+ * groups of 64 targets among the eight XCDs (synchronous): *uneven = 1 when it
+ * walked runs balanced on an earlier walk's times, and then starts[0..8] are
+ * the first group of each XCD's run (starts[8] = the group count); *uneven = 0
+ * when it walked the equal runs (starts then unspecified).  starts may be
+ * NULL.  For measurement and tests; BH_ERR_INVALID if the context has not yet
+ * walked that way. */
+bh_status bh_get_walk_runs(bh_ctx *ctx, uint32_t *starts, int32_t *uneven);
+
 #ifdef __cplusplus
 }
 #endif

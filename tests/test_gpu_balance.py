@@ -1,9 +1,10 @@
-"""The per-target walk's XCD runs, balanced on the previous walk's per-group
-times (through bh_gravity).
+"""The per-target walk's XCD runs, balanced on an earlier walk's per-group
+times (through bh_gravity; bh_get_walk_runs reports the runs used).
 
-Each XCD walks one contiguous run of the groups of 64 targets; after a first
-walk with equal runs, later walks of the same groups move the runs' ends so
-that their sums of the previous walk's times are equal.  Which XCD walks a
+Each XCD walks one contiguous run of the groups of 64 targets.  Every fourth
+walk of the same groups stores its per-group times; when those show the equal
+runs more than 8% out of balance (and the waves long-lived), later walks move
+the runs' ends so that their sums of those times are equal.  Which XCD walks a
 group changes nothing in that group's arithmetic, so every call must give the
 same bits as the first, and as the caller-order walk (which keeps equal runs
 and, lane by lane, the same walk).  Outputs are filled with NaN before each
@@ -119,4 +120,38 @@ def test_fewer_sources_on_a_larger_context():
     for k in range(3):
         log("smaller rebuild, call", k)
         assert np.array_equal(_walk(t, small.shape[0], 0.01), want)
+    t.close()
+
+
+def test_uneven_runs_walk_every_group_once():
+    """The galaxy pair: its groups' walk times differ by far more than 8%
+    between eighths of the key order, and its waves live long, so after a few
+    walks the XCD runs become uneven.  Every call, rebuilt like a time step,
+    gives the first call's bits; the runs are contiguous, cover every group
+    and stay within the grid's room of 1.25 equal shares."""
+    import barnes_hut_tree_amd as bh
+    p = W.galaxy_pair(500_000, seed=4)[0]
+    n = p.shape[0]
+    groups = (n + 63) // 64
+    cap = (groups + 7) // 8 + (groups + 31) // 32
+    src = torch.from_numpy(p).cuda()
+    t = bh.BarnesHut(n, 0, 63, 16, curve="hilbert")
+    t.build(src)
+    first = _walk(t, n, 0.02)
+    uneven_calls = 0
+    for k in range(12):
+        t.build(src)
+        got = _walk(t, n, 0.02)
+        assert np.array_equal(got, first), "call %d" % (k + 2)
+        uneven, starts = t.walk_runs()
+        log("galaxy pair call", k + 2, "uneven runs" if uneven else "equal runs", starts)
+        if uneven:
+            uneven_calls += 1
+            s = np.array(starts, np.int64)
+            assert s[0] == 0 and s[8] == groups
+            assert np.all(np.diff(s) >= 0) and np.all(np.diff(s) <= cap)
+            assert not np.array_equal(s, [x * (groups // 8) + min(x, groups % 8) for x in range(9)])
+    assert uneven_calls >= 4
+    # the caller-order walk keeps equal runs: the same bits again
+    assert np.array_equal(_walk(t, n, 0.02, flags=bh.WALK_UNSORTED), first)
     t.close()
