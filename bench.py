@@ -446,9 +446,10 @@ def configs_table(args):
     the 5M galaxy pair; the surface sources at M = 2^15, 2^17, 2^20 with grid
     and box queries.  Per line: build and walk device ms (HIP events, mean of
     --steps), interactions, the walk's fraction of the fp32 vector peak at 20
-    flops per interaction, the build's algorithmic bytes against 8 TB/s, and
-    the oracle's CPU times (tree walk and direct sum, both scaled from
-    samples) unless --no-cpu-baseline."""
+    flops per interaction, the build's algorithmic bytes against 8 TB/s,
+    whether the timed walks took uneven XCD runs, and the oracle's CPU times
+    (tree walk and direct sum, both scaled from samples) unless
+    --no-cpu-baseline.  Six warm-up steps per line, each waited for."""
     import numpy as np
     import torch
 
@@ -487,9 +488,13 @@ def configs_table(args):
         tree = bh.BarnesHut(n, 0 if q is None else nt, args.key_bits, args.leaf_cap,
                             curve=args.curve)
         for th in thetas:
-            for _ in range(2):
+            # warm-up steps, each waited for: the walk balances its XCD runs on
+            # earlier walks' times (bh_get_walk_runs), whose verdict the host
+            # reads between calls
+            for _ in range(6):
                 tree.build(src)
                 tree.gravity(th, 1.0, eps, targets=tq, out=out)
+                torch.cuda.synchronize()
             stream = torch.cuda.current_stream()
             evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
                    for _ in range(args.steps)]
@@ -501,6 +506,7 @@ def configs_table(args):
                 e[2].record(stream)
             torch.cuda.synchronize()
             tree.sync()
+            uneven_runs = tree.walk_runs()[0]   # the last timed walk's XCD runs
             build_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs)
             walk_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / len(evs)
             inter = tree.count_interactions(th, eps, targets=tq)
@@ -510,6 +516,7 @@ def configs_table(args):
             bbytes = build_alg_bytes(n, nn, nl, args.key_bits)
             row = {"config": wname, "n_sources": n, "n_targets": nt, "theta": th, "eps": eps,
                    "leaf_cap": args.leaf_cap, "key_curve": args.curve,
+                   "uneven_xcd_runs": uneven_runs,
                    "build_ms": round(build_ms, 4), "walk_ms": round(walk_ms, 4),
                    "step_ms": round(build_ms + walk_ms, 4), "interactions": inter,
                    "walk_alu_frac": round(FLOPS_PER_INTERACTION * inter / (walk_ms * 1e-3)
