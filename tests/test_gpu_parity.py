@@ -85,6 +85,11 @@ KEY_CASES = {
     "clusters_mid": lambda: _clusters([70, 300, 1000, 4000], 1e-5, 13, background=30000),
     "clusters_long": lambda: _clusters([20000, 5000], 1e-5, 14, background=1000),
     "cluster_duplicates": lambda: np.concatenate([_clusters([9000], 1e-6, 15)] * 2),
+    # many runs of 65..1100 sources starting in the same tiles (sorted a wave
+    # per run), beside longer ones
+    "clusters_many": lambda: _clusters([65, 66, 100, 127, 128, 129, 300, 511, 512, 513, 700,
+                                        1023, 1024, 1025, 1100] * 4 + [3000], 1e-5, 16,
+                                       background=2000),
 }
 
 
