@@ -8,7 +8,6 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include <algorithm>
 #include <mutex>
 #include <new>
 #include <type_traits>
@@ -56,9 +55,7 @@ struct bh_ctx {
     uint32_t runs_groups = 0;         // groups wbal holds runs for
     int runs_kind = -1;
     uint32_t walk_calls = 0;          // per-target walks so far (times kept every 4th)
-    int last_runs = -1;               // the last per-target walk took its runs from wbal (-1: none yet)
-    int last_ordered = 0;             // ... and its groups in wbal's dispatch order
-    bool order_valid = false;         // wbal holds a dispatch order for runs_groups
+    int last_runs = -1;               // the last per-target walk used uneven runs (-1: none yet)
 
     uint64_t *tkeys = nullptr, *tkeys_alt = nullptr;
     uint32_t *tvals = nullptr, *tvals_alt = nullptr;
@@ -304,8 +301,7 @@ bh_status bh_create(bh_ctx **out, int64_t max_sources, int64_t max_targets,
     ok &= dalloc(&c->nodes, (size_t)c->node_cap + 1) == hipSuccess;
     c->wn_cap = walk_records((uint64_t)ns, c->bits, c->leaf_cap, c->node_cap);
     ok &= dalloc(&c->wnodes, (size_t)c->wn_cap) == hipSuccess;
-    ok &= dalloc(&c->wbal,
-                 (size_t)kWalkBalanceHead + 3 * (size_t)walk_groups((uint32_t)(ns > nt ? ns : nt))) ==
+    ok &= dalloc(&c->wbal, (size_t)kWalkBalanceHead + walk_groups((uint32_t)(ns > nt ? ns : nt))) ==
           hipSuccess;
     ok &= dalloc(&c->inv, ns) == hipSuccess;
     ok &= dalloc(&c->diag, (size_t)kDiagMaxPartials * kDiagTerms) == hipSuccess;
@@ -455,13 +451,6 @@ static bh_status gravity_impl(bh_ctx *c, const float *targets, int64_t n_targets
     a.balance_fresh = balanced && !same_runs && !a.balance_eval;
     a.balance_runs = balanced && (same_runs || a.balance_eval) && c->bal_want &&
                      __atomic_load_n(c->bal_want, __ATOMIC_RELAXED);
-    // Dispatch order: each walk that chooses runs from times also orders
-    // the runs' groups by the recorded walk's node visits, and the walks
-    // until the next such one keep that order.
-    const bool ordered = groups >= kWalkOrderMinGroups && groups <= kWalkOrderMaxGroups;
-    a.balance_order = a.balance_eval && ordered;
-    if (balanced && ordered && (a.balance_order || (same_runs && c->order_valid && !a.balance_eval)))
-        a.balance_runs |= 2;
     a.balance_record = balanced && (!same_hist || c->walk_calls < 2 ||
                                     c->walk_calls % kWalkTimedEvery == 0);
     a.balance_want = balanced ? c->bal_want_dev : nullptr;
@@ -493,11 +482,9 @@ static bh_status gravity_impl(bh_ctx *c, const float *targets, int64_t n_targets
         if (a.balance_eval || a.balance_fresh) {
             c->runs_groups = groups;
             c->runs_kind = kind;
-            c->order_valid = a.balance_order;
         }
         if (a.balance_eval) c->hist_new = false;
-        c->last_runs = a.balance_runs & 1;
-        c->last_ordered = (a.balance_runs & 2) != 0;
+        c->last_runs = a.balance_runs ? 1 : 0;
         if (a.balance_record) {
             c->hist_groups = groups;
             c->hist_kind = kind;
@@ -798,21 +785,15 @@ bh_status bh_set_counting(bh_ctx *c, int enable)
     return BH_OK;
 }
 
-bh_status bh_get_walk_runs(bh_ctx *c, uint32_t *starts, int32_t *uneven, int32_t *ordered)
+bh_status bh_get_walk_runs(bh_ctx *c, uint32_t *starts, int32_t *uneven)
 {
     if (!c || !uneven || c->last_runs < 0) return BH_ERR_INVALID;
-    *uneven = 0;
-    if (ordered) *ordered = c->last_ordered;
-    if (!c->last_runs) return BH_OK;
-    uint32_t b[9];
-    if (hipMemcpyAsync(b, c->wbal, sizeof(b), hipMemcpyDeviceToHost, c->last_stream) !=
-            hipSuccess ||
+    *uneven = c->last_runs;
+    if (!starts) return BH_OK;
+    if (hipMemcpyAsync(starts, c->wbal, 9 * sizeof(uint32_t), hipMemcpyDeviceToHost,
+                       c->last_stream) != hipSuccess ||
         hipStreamSynchronize(c->last_stream) != hipSuccess)
         return BH_ERR_HIP;
-    // the runs the buffer holds, equal ones included
-    for (uint32_t x = 0; x <= 8; ++x)
-        if (b[x] != x * (b[8] >> 3) + std::min(x, b[8] & 7u)) *uneven = 1;
-    if (starts && *uneven) memcpy(starts, b, sizeof(b));
     return BH_OK;
 }
 

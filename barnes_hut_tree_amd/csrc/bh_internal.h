@@ -178,17 +178,13 @@ struct WalkArgs {
     // a recent walk of the same groups not yet looked at, from which to choose
     // the runs (and set *balance_want, host-mapped, may be null); else keep
     // the runs it holds (balance_fresh: none for these groups, write the equal
-    // runs).  balance_runs bit 0: walk those runs (a grid with room for
-    // uneven runs), else the equal runs of xcd_block; bit 1: each run's
-    // groups in the dispatch order the buffer holds.  balance_order: with
-    // balance_eval, also choose that order (heaviest chunks of each run
-    // first) from the times.  balance_record: store this walk's per-group
-    // times.
+    // runs).  balance_runs: walk those runs (a grid with room for uneven
+    // runs), else the equal runs of xcd_block.  balance_record: store this
+    // walk's per-group times.
     uint32_t *balance;
     int balance_eval;
     int balance_fresh;
     int balance_runs;
-    int balance_order;
     int balance_record;
     int *balance_want;
 };
@@ -196,20 +192,10 @@ void launch_walk(const WalkArgs &a, hipStream_t s);
 // walk groups of 64 targets, and the most groups one XCD's run may take
 __host__ __device__ inline uint32_t walk_groups(uint32_t n_targets) { return (n_targets + 63) / 64; }
 __host__ __device__ inline uint32_t walk_xcd_cap(uint32_t groups) { return (groups + 7) / 8 + (groups + 31) / 32; }
-// The walk's balance buffer (kWalkBalanceHead + 3 groups entries): entries
-// 0-8 the first group of each XCD's run (the ninth = groups), from
-// kWalkBalanceHead on one time per group, then one node-visit count per
-// group, then the groups in dispatch order (the k-th group each run walks
-// is entry run start + k).
+// The walk's balance buffer: entries 0-8 the first group of each XCD's run
+// (the ninth = groups), 16-31 eight 64-bit sums of per-group times, from
+// kWalkBalanceHead on one time per group.
 constexpr uint32_t kWalkBalanceHead = 32;
-// The dispatch order is chosen for 2048 to 16384 groups: from 2048 its 1024
-// chunks hold at least two groups each; up to 16384 an XCD walks at most
-// two waves per wave slot (1024 slots at eight waves per SIMD), where the
-// order, which acts on which waves share a CU and on the last waves to
-// start, pays for the locality it costs (measured: 2^20 targets 1-7%
-// faster; 2^21, four waves per slot, 2% slower; 5M 2-3% slower).
-constexpr uint32_t kWalkOrderMinGroups = 2048;
-constexpr uint32_t kWalkOrderMaxGroups = 16384;
 // inv[perm[k]] = k
 void launch_invert(const uint32_t *perm, uint32_t n, uint32_t *inv, hipStream_t s);
 void launch_fill_zero(float4 *out, uint32_t n, hipStream_t s);

@@ -128,7 +128,6 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
 #define BH_HEAD(R0, R1, R2, R6, R7, XR, OTHER)                                         \
     "v_cmp_ge_u32_e32 vcc, " XR ", %[rej]\n"                                           \
     "s_add_u32 %[off], " XR ", 32\n"                                                   \
-    "s_add_u32 %[vis], %[vis], 1\n"                                                    \
     "s_waitcnt lgkmcnt(0)\n"                                                           \
     "s_load_dwordx8 " OTHER ", %[nb], " R6 "\n"                                        \
     "v_sub_f32_e32 %[dx], " R0 ", %[px]\n"                                             \
@@ -352,7 +351,7 @@ __device__ inline uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstl
         [dx] "=&v"(dx), [dy] "=&v"(dy), [dz] "=&v"(dz), [r2] "=&v"(r2), [w] "=&v"(w),    \
         [f] "=&v"(f), [off] "=&s"(off), [t] "=&s"(t), [far] "=&s"(far),                   \
         [save] "=&s"(save), [open] "=&s"(open), [le] "=&s"(le), [j] "=&s"(jj),          \
-        [left] "=&s"(left), [vis] "+s"(vis)
+        [left] "=&s"(left)
 #define BH_RUN_INS                                                                     \
     [nb] "s"(nb), [srclo] "s"(sb_lo), [srchi] "s"(sb_hi), [eps2] "v"(eps2v), [px] "v"(p.x),  \
         [py] "v"(p.y), [pz] "v"(p.z), [wb] "s"(wb), [wbe] "s"(wbe)
@@ -386,7 +385,7 @@ __device__ __attribute__((always_inline)) inline void walk_wave(
     const Node *__restrict__ nodes, const Node *__restrict__ wnodes,
     const float4 *__restrict__ src, uint32_t nn, float4 p, uint32_t i, uint32_t wave_base,
     bool valid, float T0, float eps2, float &ax, float &ay, float &az, float &pot,
-    uint32_t &n_int, uint32_t &visits)
+    uint32_t &n_int)
 {
     const char *node_bytes = reinterpret_cast<const char *>(ASM ? wnodes : nodes);
     // Lane state: a lane takes part at node X when rejoin <= X (both as byte
@@ -420,7 +419,6 @@ __device__ __attribute__((always_inline)) inline void walk_wave(
         const uint32_t wbe = SELF ? (ANY_MINE ? 0xffffffffu : wave_base + 64) : 0u;
         float eps2v = eps2;
         asm volatile("" : "+v"(eps2v));   // held in a vector register
-        uint32_t vis = 0;   // node visits of the wave (its share of the walk's work)
         for (;;) {
             X = sgpr(X);
             uint32_t first, cnt, skip, off, t, le, jj, left;
@@ -459,12 +457,10 @@ __device__ __attribute__((always_inline)) inline void walk_wave(
             first = sgpr(first);
             cnt = sgpr(cnt);
             skip = sgpr(skip);
-            vis = sgpr(vis);
             if (cnt == 0) break;   // the end record (every other leaf holds a source)
             open_leaf(first, first + cnt, eps2v);
             X = skip;   // leave the leaf (skip == X + 1, as a byte offset)
         }
-        visits = vis;
         return;
     }
     while (X < nn) {
@@ -585,7 +581,7 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
     // together share the nodes near their targets in that XCD's L2; with
     // a balance buffer the runs are the ones balanced on the previous walk's times
     uint32_t blk;
-    if (runs & 1) {
+    if (runs) {
         // the grid holds 8 cap workgroups, cap per XCD; an XCD whose run is
         // shorter lets its first ones return, while every XCD still has free
         // slots (at the end of the dispatch they would hold up the others)
@@ -597,9 +593,6 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
     } else {
         blk = xcd_block(blockIdx.x, gridDim.x);
     }
-    // the k-th group of each run in the dispatch order the buffer holds (a
-    // permutation of all groups that keeps each run's groups in the run)
-    if (runs & 2) blk = sgpr(balance[kWalkBalanceHead + 2 * walk_groups(n) + blk]);
     const uint32_t wave_base = sgpr(blk * kWalkThreads + (threadIdx.x & ~63u));
     const uint32_t c = wave_base + lane;
     const bool valid = c < n;
@@ -639,7 +632,7 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
     // would put the wait on every iteration
     asm volatile("" ::"v"(p.x), "v"(p.y), "v"(p.z));
     float ax = 0.f, ay = 0.f, az = 0.f, pot = 0.f;
-    uint32_t n_int = 0, visits = 0;
+    uint32_t n_int = 0;
     if (VOTE) {
         if (exact)
             walk_vote<SOFT, SELF, COUNT, true, UNSORTED>(nodes, src, nn, p, i, wave_base, valid, T0,
@@ -652,20 +645,18 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
     } else {
         if (use_asm)
             walk_wave<SOFT, SELF, COUNT, true, UNSORTED>(nodes, wnodes, src, nn, p, i, wave_base,
-                                                         valid, T0, eps2, ax, ay, az, pot, n_int, visits);
+                                                         valid, T0, eps2, ax, ay, az, pot, n_int);
         else
             walk_wave<SOFT, SELF, COUNT, false, UNSORTED>(nodes, wnodes, src, nn, p, i, wave_base,
-                                                          valid, T0, eps2, ax, ay, az, pot, n_int, visits);
+                                                          valid, T0, eps2, ax, ay, az, pot, n_int);
     }
 
     if (valid) out[slot] = make_float4(G * ax, G * ay, G * az, G * pot);
-    // this group's time and node visits (plain stores: the per-wave device
-    // atomic these replaced serialised on its few addresses)
-    if (record && lane == 0) {
-        const uint32_t g = wave_base >> 6;
-        balance[kWalkBalanceHead + g] = (uint32_t)(__builtin_amdgcn_s_memrealtime() - t_start);
-        balance[kWalkBalanceHead + walk_groups(n) + g] = visits;
-    }
+    // this group's time (one plain store: the per-wave device atomic this
+    // replaced serialised on its few addresses)
+    if (record && lane == 0)
+        balance[kWalkBalanceHead + (wave_base >> 6)] =
+            (uint32_t)(__builtin_amdgcn_s_memrealtime() - t_start);
     if (COUNT) {
         unsigned long long cnt = valid ? n_int : 0u;
         for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
@@ -712,27 +703,12 @@ __device__ inline uint32_t walk_chunk_start(uint32_t c, uint32_t ng)
     return (uint32_t)(((uint64_t)c * ng + 255) >> 8);
 }
 
-// The dispatch order's chunks: kWalkOrderChunks runs of consecutive groups,
-// chunk c from ceil(c ng / kWalkOrderChunks) (every fourth boundary is a
-// balance chunk's); walk_ochunk_of(g) is the chunk holding group g, the
-// largest c whose start is at most g.
-constexpr uint32_t kWalkOrderChunks = 1024;
-__device__ inline uint32_t walk_ochunk_start(uint32_t c, uint32_t ng)
-{
-    return (uint32_t)(((uint64_t)c * ng + kWalkOrderChunks - 1) / kWalkOrderChunks);
-}
-__device__ inline uint32_t walk_ochunk_of(uint32_t g, uint32_t ng)
-{
-    return (uint32_t)((uint64_t)g * kWalkOrderChunks / ng);
-}
-
-__device__ void walk_bounds(uint32_t ng, uint32_t cap, bool hist, bool runs, bool order,
+__device__ void walk_bounds(uint32_t ng, uint32_t cap, bool hist, bool runs,
                             uint32_t *__restrict__ xb, int *__restrict__ want)
 {
     const uint32_t *__restrict__ wdur = xb + kWalkBalanceHead;
     __shared__ unsigned long long csum[256];
     __shared__ uint32_t ideal[8];
-    __shared__ uint32_t bnd[9];
     __shared__ int balance;
     const uint32_t t = threadIdx.x;
     csum[t] = 0;
@@ -784,91 +760,39 @@ __device__ void walk_bounds(uint32_t ng, uint32_t cap, bool hist, bool runs, boo
     }
     __syncthreads();
     if (!balance) {
-        if (t <= 8) bnd[t] = t * (ng >> 3) + min(t, ng & 7u);
-    } else {
-        // inclusive scan of the chunk sums
-        for (uint32_t o = 1; o < 256; o <<= 1) {
-            const unsigned long long v = t >= o ? csum[t - o] : 0ull;
-            __syncthreads();
-            csum[t] += v;
-            __syncthreads();
-        }
-        if (t >= 1 && t < 8) {
-            // the chunk boundary nearest to where the times reach t/8 of the total
-            const unsigned long long target = csum[255] * t / 8;
-            uint32_t k = 0;
-            while (k < 255 && csum[k] < target) ++k;
-            const unsigned long long before = k ? csum[k - 1] : 0ull;
-            const uint32_t kb = target - before <= csum[k] - target ? k : k + 1;
-            ideal[t] = walk_chunk_start(kb, ng);
-        }
+        if (t <= 8) xb[t] = t * (ng >> 3) + min(t, ng & 7u);
+        return;
+    }
+    // inclusive scan of the chunk sums
+    for (uint32_t o = 1; o < 256; o <<= 1) {
+        const unsigned long long v = t >= o ? csum[t - o] : 0ull;
         __syncthreads();
-        if (t == 0) {
-            // clamp: run x at most cap groups, and the runs after it able to
-            // hold the rest
-            uint32_t prev = 0;
-            bnd[0] = 0;
-            for (uint32_t x = 1; x < 8; ++x) {
-                const uint64_t tail = (uint64_t)(8 - x) * cap;
-                const uint32_t lo = max(prev, (uint64_t)ng > tail ? (uint32_t)(ng - tail) : 0u);
-                const uint32_t hi = min(prev + cap, ng);
-                prev = min(max(ideal[x], lo), hi);
-                bnd[x] = prev;
-            }
-            bnd[8] = ng;
-        }
+        csum[t] += v;
+        __syncthreads();
+    }
+    if (t >= 1 && t < 8) {
+        // the chunk boundary nearest to where the times reach t/8 of the total
+        const unsigned long long target = csum[255] * t / 8;
+        uint32_t k = 0;
+        while (k < 255 && csum[k] < target) ++k;
+        const unsigned long long before = k ? csum[k - 1] : 0ull;
+        const uint32_t kb = target - before <= csum[k] - target ? k : k + 1;
+        ideal[t] = walk_chunk_start(kb, ng);
     }
     __syncthreads();
-    if (t <= 8) xb[t] = bnd[t];
-    if (!(order && hist) || ng < kWalkOrderMinGroups) return;
-    // The dispatch order: a run is cut where order chunks begin into pieces,
-    // which it walks heaviest first (most node visits counted on the recorded
-    // walk; ties in key order), each piece's groups in key order.  Visits, not
-    // times: a group's time depends on when it ran and beside what (the
-    // first waves of a walk share their CUs with a full complement, the last
-    // run nearly alone), while its visits are its own work.  Pieces of
-    // consecutive keys keep the waves that run together near one another in
-    // the tree.
-    __shared__ uint32_t vsum[kWalkOrderChunks];
-    const uint32_t *__restrict__ wvis = xb + kWalkBalanceHead + ng;
-    for (uint32_t c = t; c < kWalkOrderChunks; c += 256) vsum[c] = 0;
-    __syncthreads();
-    for (uint32_t g0 = t; g0 < ng; g0 += 8 * 256) {
-        uint32_t v[8];
-#pragma unroll
-        for (uint32_t j = 0; j < 8; ++j) {
-            const uint32_t g = g0 + 256 * j;
-            v[j] = g < ng ? wvis[g] : 0u;
+    if (t == 0) {
+        // clamp: run x at most cap groups, and the runs after it able to hold
+        // the rest
+        uint32_t prev = 0;
+        xb[0] = 0;
+        for (uint32_t x = 1; x < 8; ++x) {
+            const uint64_t tail = (uint64_t)(8 - x) * cap;
+            const uint32_t lo = max(prev, (uint64_t)ng > tail ? (uint32_t)(ng - tail) : 0u);
+            const uint32_t hi = min(prev + cap, ng);
+            prev = min(max(ideal[x], lo), hi);
+            xb[x] = prev;
         }
-#pragma unroll
-        for (uint32_t j = 0; j < 8; ++j) {
-            const uint32_t g = g0 + 256 * j;
-            if (g < ng) atomicAdd(&vsum[walk_ochunk_of(g, ng)], v[j]);
-        }
-    }
-    __syncthreads();
-    // one wave per run, lanes over its pieces (a run holds at most 5/32 of
-    // the groups, so about 162 pieces at most)
-    uint32_t *__restrict__ perm = xb + kWalkBalanceHead + 2 * ng;
-    for (uint32_t x = t >> 6; x < 8; x += 4) {
-        const uint32_t r0 = bnd[x], r1 = bnd[x + 1];
-        if (r0 == r1) continue;
-        const uint32_t c0 = walk_ochunk_of(r0, ng), c1 = walk_ochunk_of(r1 - 1, ng);
-        const uint32_t np = c1 - c0 + 1;
-        for (uint32_t q = t & 63u; q < np; q += 64) {
-            const uint32_t c = c0 + q;
-            const uint32_t p0 = max(r0, walk_ochunk_start(c, ng));
-            const uint32_t p1 = min(r1, walk_ochunk_start(c + 1, ng));
-            const uint32_t key = vsum[c];
-            uint32_t off = 0;
-            for (uint32_t j = 0; j < np; ++j) {
-                const uint32_t kj = vsum[c0 + j];
-                if (kj > key || (kj == key && j < q))
-                    off += min(r1, walk_ochunk_start(c0 + j + 1, ng)) -
-                           max(r0, walk_ochunk_start(c0 + j, ng));
-            }
-            for (uint32_t g = p0; g < p1; ++g) perm[r0 + off + (g - p0)] = g;
-        }
+        xb[8] = ng;
     }
 }
 
@@ -877,14 +801,14 @@ __global__ __launch_bounds__(256) void k_walk_nodes(const Node *__restrict__ nod
                                                     float theta, float eps2, uint32_t wn_cap,
                                                     Node *__restrict__ wnodes,
                                                     uint32_t ng, uint32_t cap, int eval,
-                                                    int fresh, int runs, int order,
+                                                    int fresh, int runs,
                                                     uint32_t *__restrict__ balance,
                                                     int *__restrict__ want)
 {
     // new runs from recent times, or the equal runs for groups without any;
     // otherwise the runs chosen last time stand
     if (balance && blockIdx.x == 0 && (eval || fresh))
-        walk_bounds(ng, cap, eval != 0, (runs & 1) != 0, order != 0, balance, want);
+        walk_bounds(ng, cap, eval != 0, runs != 0, balance, want);
     if (prm->status != 0) return;
     const uint32_t nn = prm->n_nodes;
     if (!(nn < kAsmMaxNodes && nn < wn_cap)) return;
@@ -917,7 +841,7 @@ template <bool SOFT, bool SELF, bool COUNT, bool VOTE, bool UNSORTED>
 void launch5(const WalkArgs &a, hipStream_t s)
 {
     const uint32_t groups = walk_groups(a.n_targets);
-    const uint32_t grid = (a.balance_runs & 1) ? 8 * walk_xcd_cap(groups) : groups;
+    const uint32_t grid = a.balance_runs ? 8 * walk_xcd_cap(groups) : groups;
     hipLaunchKernelGGL((k_walk<SOFT, SELF, COUNT, VOTE, UNSORTED>), dim3(grid), dim3(kWalkThreads),
                        0, s, a.nodes, a.wnodes, a.wn_cap, a.src, a.tpos, a.tmap, a.prm, a.n_targets, a.theta, a.G,
                        a.eps * a.eps, a.out, a.count, a.balance, a.balance_runs,
@@ -958,8 +882,7 @@ void launch_walk(const WalkArgs &args, hipStream_t s)
     WalkArgs a = args;
     if (a.vote || a.unsorted || a.wn_cap == 0 || !a.balance) {
         a.balance = nullptr;
-        a.balance_eval = a.balance_fresh = a.balance_runs = a.balance_order = 0;
-        a.balance_record = 0;
+        a.balance_eval = a.balance_fresh = a.balance_runs = a.balance_record = 0;
         a.balance_want = nullptr;
     }
     if (!a.vote && a.wn_cap > 0) {
@@ -967,8 +890,8 @@ void launch_walk(const WalkArgs &args, hipStream_t s)
         const uint32_t groups = walk_groups(a.n_targets);
         hipLaunchKernelGGL(k_walk_nodes, dim3(blocks), dim3(256), 0, s, a.nodes, a.prm, a.theta,
                            a.eps * a.eps, a.wn_cap, a.wnodes, groups, walk_xcd_cap(groups),
-                           a.balance_eval, a.balance_fresh, a.balance_runs, a.balance_order,
-                           a.balance, a.balance_want);
+                           a.balance_eval, a.balance_fresh, a.balance_runs, a.balance,
+                           a.balance_want);
     }
     // Plummer softening with eps^2 > 0 never meets r^2 + eps^2 == 0
     if (a.eps * a.eps > 0.f) launch1<true>(a, s); else launch1<false>(a, s);

@@ -123,13 +123,11 @@ bh_status bh_build(bh_ctx *ctx, const float *src_pos_mass, int64_t n, void *stre
  *                 caller's order of the targets (for targets == NULL,
  *                 n_targets must equal the n given to bh_build).
  *   theta >= 0 (0 = exact direct sum), eps >= 0, G any finite value.
- * The context remembers each walk's time and node visits per group of 64
- * targets; when the next walk has the same groups (the same target count,
- * self-gravity or not) and those times show the eight XCDs' equal runs of
- * groups out of balance, it moves the runs' ends, and from 2^17 to 2^20
- * targets each XCD takes its run's groups heaviest part first by those
- * visits.  That changes only where and when each group runs: the results
- * are the same bits either way. */
+ * The context remembers each walk's time per group of 64 targets; when the
+ * next walk has the same groups (the same target count, self-gravity or not)
+ * and those times show the eight XCDs' equal runs of groups out of balance,
+ * it moves the runs' ends.  That changes only where each group runs: the
+ * results are the same bits either way. */
 bh_status bh_gravity(bh_ctx *ctx, const float *targets, int64_t n_targets, float theta,
                      float G, float eps, float *out_acc_pot, void *stream);
 
@@ -373,12 +371,10 @@ bh_status bh_get_profile(bh_ctx *ctx, float *ms, int n);
  * groups of 64 targets among the eight XCDs (synchronous): *uneven = 1 when it
  * walked runs balanced on an earlier walk's times, and then starts[0..8] are
  * the first group of each XCD's run (starts[8] = the group count); *uneven = 0
- * when it walked the equal runs (starts then unspecified).  *ordered = 1 when
- * each run took its groups in the dispatch order chosen from an earlier walk's
- * node visits, 0 in key order.  starts and ordered may be NULL.  For
- * measurement and tests; BH_ERR_INVALID if the context has not yet walked that
- * way. */
-bh_status bh_get_walk_runs(bh_ctx *ctx, uint32_t *starts, int32_t *uneven, int32_t *ordered);
+ * when it walked the equal runs (starts then unspecified).  starts may be
+ * NULL.  For measurement and tests; BH_ERR_INVALID if the context has not yet
+ * walked that way. */
+bh_status bh_get_walk_runs(bh_ctx *ctx, uint32_t *starts, int32_t *uneven);
 
 #ifdef __cplusplus
 }
