@@ -111,12 +111,15 @@ void launch_morton(const float4 *pts, uint32_t n, const DevParams *prm, int bits
 
 // radix_sort.hip
 size_t sort_spine_entries(uint32_t n);
-// Stable LSD sort of (keys, vals) over the low `key_bits` bits.  Ping-pongs
-// between the two buffer pairs; the result ends in (keys_out, vals_out).  With
-// gather_src != NULL the last pass also writes gather_dst[i] = gather_src[vals[i]].
+// Stable LSD sort of (keys, vals) over the key bits [skip_bits, key_bits)
+// (skip_bits a multiple of 8; 0: every bit below key_bits): keys equal in
+// those bits keep their input order.  Ping-pongs between the two buffer
+// pairs; the result ends in (keys_out, vals_out).  With gather_src != NULL the
+// last pass also writes gather_dst[i] = gather_src[vals[i]].
 void radix_sort(uint64_t *keys, uint32_t *vals, uint64_t *keys_alt, uint32_t *vals_alt,
                 uint64_t **keys_out, uint32_t **vals_out, uint32_t n, int key_bits,
-                uint32_t *spine, const float4 *gather_src, float4 *gather_dst, hipStream_t s);
+                int skip_bits, uint32_t *spine, const float4 *gather_src, float4 *gather_dst,
+                hipStream_t s);
 
 // Exclusive scan of each row of a [rows][len] table, one workgroup per row:
 // pref[r][t] = sum(in[r][0..t)), tot[r] = row total.

@@ -475,8 +475,8 @@ namespace {
 
 template <int ITEMS>
 void sort_passes(uint64_t *&ka, uint32_t *&va, uint64_t *&kb, uint32_t *&vb, uint32_t n,
-                 int key_bits, uint32_t *spine, const float4 *gather_src, float4 *gather_dst,
-                 hipStream_t s)
+                 int key_bits, int skip_bits, uint32_t *spine, const float4 *gather_src,
+                 float4 *gather_dst, hipStream_t s)
 {
     constexpr uint32_t tile = kSortThreads * ITEMS;
     const uint32_t tiles = (n + tile - 1) / tile;
@@ -485,7 +485,7 @@ void sort_passes(uint64_t *&ka, uint32_t *&va, uint64_t *&kb, uint32_t *&vb, uin
     const int passes = (key_bits + 7) / 8;
     // long keys with a gather: passes over the bits above kLowBits, then runs
     const bool runs = gather_src && key_bits > 40;
-    const int p0 = runs ? kLowBits / 8 : 0;
+    const int p0 = runs ? kLowBits / 8 : skip_bits / 8;
     for (int p = p0; p < passes; ++p) {
         const int shift = 8 * p;
         const bool last = !runs && (p == passes - 1);
@@ -518,17 +518,18 @@ void sort_passes(uint64_t *&ka, uint32_t *&va, uint64_t *&kb, uint32_t *&vb, uin
 // the scattered writes fill whole cache lines.
 void radix_sort(uint64_t *keys, uint32_t *vals, uint64_t *keys_alt, uint32_t *vals_alt,
                 uint64_t **keys_out, uint32_t **vals_out, uint32_t n, int key_bits,
-                uint32_t *spine, const float4 *gather_src, float4 *gather_dst, hipStream_t s)
+                int skip_bits, uint32_t *spine, const float4 *gather_src, float4 *gather_dst,
+                hipStream_t s)
 {
     uint64_t *ka = keys, *kb = keys_alt;
     uint32_t *va = vals, *vb = vals_alt;
     if (n > 0) {
         if (n >= kSortLargeN)
-            sort_passes<kSortItemsLarge>(ka, va, kb, vb, n, key_bits, spine, gather_src,
-                                         gather_dst, s);
+            sort_passes<kSortItemsLarge>(ka, va, kb, vb, n, key_bits, skip_bits, spine,
+                                         gather_src, gather_dst, s);
         else
-            sort_passes<kSortItems>(ka, va, kb, vb, n, key_bits, spine, gather_src, gather_dst,
-                                    s);
+            sort_passes<kSortItems>(ka, va, kb, vb, n, key_bits, skip_bits, spine, gather_src,
+                                    gather_dst, s);
     }
     *keys_out = ka;
     *vals_out = va;
