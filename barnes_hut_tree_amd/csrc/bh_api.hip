@@ -49,6 +49,8 @@ struct bh_ctx {
     uint32_t *wbal = nullptr;         // the walk's XCD runs and per-group times
     int *bal_want = nullptr;          // pinned, written by the device: the last walk's
     int *bal_want_dev = nullptr;      //   times call for uneven XCD runs (its device address)
+    uint32_t *clustered = nullptr;    // the word after it: a sort found long runs of equal
+    uint32_t *clustered_dev = nullptr; //   top key bits clustered in tiles (sticky)
     uint32_t hist_groups = 0;         // groups wbal holds times for (0: none)
     int hist_kind = -1;               // 0: self-gravity, 1: separate targets
     bool hist_new = false;            // those times are not yet looked at
@@ -276,9 +278,12 @@ bh_status bh_create(bh_ctx **out, int64_t max_sources, int64_t max_targets,
                   hipSuccess;
     }
     ok &= hipHostMalloc((void **)&c->host_prm, sizeof(DevParams), hipHostMallocDefault) == hipSuccess;
-    if (hipHostMalloc((void **)&c->bal_want, sizeof(int), hipHostMallocMapped) == hipSuccess) {
-        *c->bal_want = 0;
+    if (hipHostMalloc((void **)&c->bal_want, 2 * sizeof(int), hipHostMallocMapped) ==
+        hipSuccess) {
+        c->bal_want[0] = c->bal_want[1] = 0;
         ok &= hipHostGetDevicePointer((void **)&c->bal_want_dev, c->bal_want, 0) == hipSuccess;
+        c->clustered = reinterpret_cast<uint32_t *>(c->bal_want + 1);
+        c->clustered_dev = reinterpret_cast<uint32_t *>(c->bal_want_dev + 1);
     } else {
         c->bal_want = nullptr;
         ok = false;
@@ -349,8 +354,17 @@ bh_status bh_build(bh_ctx *c, const float *src_pos_mass, int64_t n, void *stream
     if (un > 0) {
         launch_morton(src, un, c->prm, c->bits, c->curve, c->hlut, c->keys, c->vals, s);
         record(c, 1, s);
+        // Once a sort of this context has found runs of equal top key bits
+        // clustered in tiles (the device's flag, read without waiting, so
+        // perhaps a few builds late), its later builds sort every bit in LSD
+        // passes: the runs' kernel would wait on its busiest tiles.
+        SortRuns sr;
+        if (c->clustered) {
+            sr.clustered = c->clustered_dev;
+            sr.all_passes = __atomic_load_n(c->clustered, __ATOMIC_RELAXED) != 0;
+        }
         radix_sort(c->keys, c->vals, c->keys_alt, c->vals_alt, &c->keys_sorted, &c->perm, un,
-                   c->key_bits, 0, c->spine, src, c->spos, s);
+                   c->key_bits, 0, c->spine, src, c->spos, sr, s);
         record(c, 2, s);
         build_tree(c->keys_sorted, c->spos, un, c->bits, c->leaf_cap, c->node_cap, c->bw,
                    c->nodes, c->prm, s);
@@ -379,7 +393,7 @@ static const uint32_t *sort_targets(bh_ctx *c, const float *targets, uint32_t nt
     launch_morton((const float4 *)targets, nt, c->prm, bits, c->curve, c->hlut, c->tkeys,
                   c->tvals, s);
     radix_sort(c->tkeys, c->tvals, c->tkeys_alt, c->tvals_alt, &ko, &vo, nt, 3 * bits,
-               skip_bits, c->tspine, (const float4 *)targets, c->tpos, s);
+               skip_bits, c->tspine, (const float4 *)targets, c->tpos, SortRuns(), s);
     return vo;
 }
 

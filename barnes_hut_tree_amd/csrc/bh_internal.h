@@ -111,6 +111,16 @@ void launch_morton(const float4 *pts, uint32_t n, const DevParams *prm, int bits
 
 // radix_sort.hip
 size_t sort_spine_entries(uint32_t n);
+// The 63-bit key sort with a gather sorts the top 40 bits in five passes and
+// then orders each run of equal top bits in one kernel, whose workgroups sort
+// the runs of more than 64 members that start in their tile one after another.
+// clustered (host-mapped, may be null) is set to 1 when some tile starts
+// several; all_passes sorts all 64 bits in eight passes instead (the same
+// order), with no such kernel.
+struct SortRuns {
+    uint32_t *clustered = nullptr;
+    bool all_passes = false;
+};
 // Stable LSD sort of (keys, vals) over the key bits [skip_bits, key_bits)
 // (skip_bits a multiple of 8; 0: every bit below key_bits): keys equal in
 // those bits keep their input order.  Ping-pongs between the two buffer
@@ -119,7 +129,7 @@ size_t sort_spine_entries(uint32_t n);
 void radix_sort(uint64_t *keys, uint32_t *vals, uint64_t *keys_alt, uint32_t *vals_alt,
                 uint64_t **keys_out, uint32_t **vals_out, uint32_t n, int key_bits,
                 int skip_bits, uint32_t *spine, const float4 *gather_src, float4 *gather_dst,
-                hipStream_t s);
+                const SortRuns &sr, hipStream_t s);
 
 // Exclusive scan of each row of a [rows][len] table, one workgroup per row:
 // pref[r][t] = sum(in[r][0..t)), tot[r] = row total.

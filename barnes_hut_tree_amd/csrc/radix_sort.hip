@@ -226,6 +226,10 @@ __global__ __launch_bounds__(kSortThreads) void k_scatter(
 constexpr int kRunHalo = 64;
 constexpr int kRunLds = 4096;
 constexpr int kLowBits = 24;
+// a tile that starts this many runs of more than kRunHalo members marks the
+// keys as clustered: the workgroup sorts those runs one after another while
+// the others wait for it
+constexpr uint32_t kRunsClustered = 2;
 
 __device__ inline uint32_t low_of(uint64_t k) { return (uint32_t)k & ((1u << kLowBits) - 1u); }
 
@@ -305,12 +309,15 @@ __device__ void run_pass(const uint64_t *ki, const uint32_t *vi, const float4 *p
 }
 
 // (kin, vin) sorted by the bits above kLowBits, stably; out: (kout, vout)
-// sorted by the whole key, stably, and gdst[p] = gsrc[vout[p]].
+// sorted by the whole key, stably, and gdst[p] = gsrc[vout[p]].  clustered
+// (host-mapped, may be null) is set to 1 when a tile starts kRunsClustered or
+// more runs of more than kRunHalo members.
 template <int ITEMS>
 __global__ __launch_bounds__(kSortThreads) void k_runs(
     const uint64_t *__restrict__ kin, const uint32_t *__restrict__ vin,
     uint64_t *__restrict__ kout, uint32_t *__restrict__ vout, uint32_t n, uint32_t n_tiles,
-    const float4 *__restrict__ gsrc, float4 *__restrict__ gdst)
+    const float4 *__restrict__ gsrc, float4 *__restrict__ gdst,
+    uint32_t *__restrict__ clustered)
 {
     constexpr uint32_t kTile = kSortThreads * ITEMS;
     constexpr uint32_t kWin = kTile + 2 * kRunHalo;
@@ -366,6 +373,7 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(
     }
     __syncthreads();
     const uint32_t ns = n_starts;
+    if (clustered && threadIdx.x == 0 && ns >= kRunsClustered) *clustered = 1u;
     for (uint32_t r = 0; r < ns; ++r) {
         const uint32_t s = starts[r];
         const uint64_t h = top(kin[s]);
@@ -476,7 +484,7 @@ namespace {
 template <int ITEMS>
 void sort_passes(uint64_t *&ka, uint32_t *&va, uint64_t *&kb, uint32_t *&vb, uint32_t n,
                  int key_bits, int skip_bits, uint32_t *spine, const float4 *gather_src,
-                 float4 *gather_dst, hipStream_t s)
+                 float4 *gather_dst, const SortRuns &sr, hipStream_t s)
 {
     constexpr uint32_t tile = kSortThreads * ITEMS;
     const uint32_t tiles = (n + tile - 1) / tile;
@@ -484,7 +492,8 @@ void sort_passes(uint64_t *&ka, uint32_t *&va, uint64_t *&kb, uint32_t *&vb, uin
     uint32_t *hist = spine, *pref = spine + entries, *tot = spine + 2 * entries;
     const int passes = (key_bits + 7) / 8;
     // long keys with a gather: passes over the bits above kLowBits, then runs
-    const bool runs = gather_src && key_bits > 40;
+    // (unless the caller asks for every pass)
+    const bool runs = gather_src && key_bits > 40 && !sr.all_passes;
     const int p0 = runs ? kLowBits / 8 : skip_bits / 8;
     for (int p = p0; p < passes; ++p) {
         const int shift = 8 * p;
@@ -505,7 +514,7 @@ void sort_passes(uint64_t *&ka, uint32_t *&va, uint64_t *&kb, uint32_t *&vb, uin
     }
     if (runs) {
         hipLaunchKernelGGL(k_runs<ITEMS>, dim3(tiles), dim3(kSortThreads), 0, s, ka, va, kb, vb,
-                           n, tiles, gather_src, gather_dst);
+                           n, tiles, gather_src, gather_dst, sr.clustered);
         uint64_t *tk = ka; ka = kb; kb = tk;
         uint32_t *tv = va; va = vb; vb = tv;
     }
@@ -519,17 +528,17 @@ void sort_passes(uint64_t *&ka, uint32_t *&va, uint64_t *&kb, uint32_t *&vb, uin
 void radix_sort(uint64_t *keys, uint32_t *vals, uint64_t *keys_alt, uint32_t *vals_alt,
                 uint64_t **keys_out, uint32_t **vals_out, uint32_t n, int key_bits,
                 int skip_bits, uint32_t *spine, const float4 *gather_src, float4 *gather_dst,
-                hipStream_t s)
+                const SortRuns &sr, hipStream_t s)
 {
     uint64_t *ka = keys, *kb = keys_alt;
     uint32_t *va = vals, *vb = vals_alt;
     if (n > 0) {
         if (n >= kSortLargeN)
             sort_passes<kSortItemsLarge>(ka, va, kb, vb, n, key_bits, skip_bits, spine,
-                                         gather_src, gather_dst, s);
+                                         gather_src, gather_dst, sr, s);
         else
             sort_passes<kSortItems>(ka, va, kb, vb, n, key_bits, skip_bits, spine, gather_src,
-                                    gather_dst, s);
+                                    gather_dst, sr, s);
     }
     *keys_out = ka;
     *vals_out = va;

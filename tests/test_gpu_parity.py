@@ -90,6 +90,9 @@ KEY_CASES = {
     "clusters_many": lambda: _clusters([65, 66, 100, 127, 128, 129, 300, 511, 512, 513, 700,
                                         1023, 1024, 1025, 1100] * 4 + [3000], 1e-5, 16,
                                        background=2000),
+    # several long runs to a tile beside runs longer than the LDS sort takes
+    "clusters_heavy_long": lambda: _clusters([65, 80, 100, 120] * 8 + [20000, 6000], 1e-5, 17,
+                                             background=500),
 }
 
 
@@ -108,6 +111,30 @@ def test_keys_perm_bbox_bitexact(orc, case, bits):
     rperm = ref.perm()
     assert np.array_equal(perm.cpu().numpy().astype(np.int64), rperm)
     assert np.array_equal(k.cpu().numpy().view(np.uint64), rk[rperm])
+    t.close()
+
+
+@pytest.mark.parametrize("case", ["clusters_many", "clusters_heavy_long", "cluster_duplicates",
+                                  "plummer65536"])
+def test_clustered_keys_sorted_in_all_passes_bitexact(orc, case):
+    """A sort that finds several runs of more than 64 equal top key bits
+    starting in one tile flags the context; its next builds sort all 63 bits
+    in eight passes instead of five passes and the runs' kernel.  Keys and
+    order stay bit-exact over repeated builds, whichever way each build took
+    (the first of each case takes the runs' kernel; Plummer's runs never
+    reach 65, so it always does)."""
+    p = KEY_CASES[case]()
+    log("clustered keys", case, p.shape[0])
+    ref = orc.Tree(p, key_bits=63, leaf_cap=16)
+    rk, rperm = ref.keys(), ref.perm()
+    t = make_tree(p, key_bits=63)
+    src = torch.from_numpy(p).cuda()
+    for b in range(3):
+        if b:
+            t.build(src)
+        k, perm = t.keys()   # waits for the build, so the next one sees its flag
+        assert np.array_equal(perm.cpu().numpy().astype(np.int64), rperm), "build %d" % b
+        assert np.array_equal(k.cpu().numpy().view(np.uint64), rk[rperm]), "build %d" % b
     t.close()
 
 
