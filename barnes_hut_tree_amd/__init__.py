@@ -92,7 +92,7 @@ def load_library():
         "bh_set_counting": [P, i32],
         "bh_get_interactions": [P, ctypes.POINTER(ctypes.c_uint64)],
         "bh_gravity_static": [P, i64, ctypes.POINTER(_Params), f32, f32, f32, P, P],
-        "bh_get_walk_runs": [P, P, ctypes.POINTER(ctypes.c_int32)],
+        "bh_get_walk_runs": [P, P, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -278,8 +278,16 @@ class BarnesHut:
         starts = np.zeros(9, np.uint32)
         uneven = ctypes.c_int32()
         _check(load_library().bh_get_walk_runs(self._h, ctypes.c_void_p(starts.ctypes.data),
-                                               ctypes.byref(uneven)), "bh_get_walk_runs")
+                                               ctypes.byref(uneven), None), "bh_get_walk_runs")
         return bool(uneven.value), (starts.tolist() if uneven.value else None)
+
+    def walk_split(self):
+        """How many groups the last per-target walk walked as four waves of 16
+        targets each (bh_get_walk_runs)."""
+        uneven, split = ctypes.c_int32(), ctypes.c_int32()
+        _check(load_library().bh_get_walk_runs(self._h, None, ctypes.byref(uneven),
+                                               ctypes.byref(split)), "bh_get_walk_runs")
+        return int(split.value)
 
     def interactions(self):
         """Interactions of the last counted gravity() call (bh_get_interactions)."""

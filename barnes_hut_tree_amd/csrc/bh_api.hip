@@ -58,6 +58,7 @@ struct bh_ctx {
     int runs_kind = -1;
     uint32_t walk_calls = 0;          // per-target walks so far (times kept every 4th)
     int last_runs = -1;               // the last per-target walk used uneven runs (-1: none yet)
+    int last_split = 0;               // ... and split its heaviest groups
 
     uint64_t *tkeys = nullptr, *tkeys_alt = nullptr;
     uint32_t *tvals = nullptr, *tvals_alt = nullptr;
@@ -306,7 +307,8 @@ bh_status bh_create(bh_ctx **out, int64_t max_sources, int64_t max_targets,
     ok &= dalloc(&c->nodes, (size_t)c->node_cap + 1) == hipSuccess;
     c->wn_cap = walk_records((uint64_t)ns, c->bits, c->leaf_cap, c->node_cap);
     ok &= dalloc(&c->wnodes, (size_t)c->wn_cap) == hipSuccess;
-    ok &= dalloc(&c->wbal, (size_t)kWalkBalanceHead + walk_groups((uint32_t)(ns > nt ? ns : nt))) ==
+    ok &= dalloc(&c->wbal,
+                 (size_t)kWalkBalanceHead + 3 * (size_t)walk_groups((uint32_t)(ns > nt ? ns : nt))) ==
           hipSuccess;
     ok &= dalloc(&c->inv, ns) == hipSuccess;
     ok &= dalloc(&c->diag, (size_t)kDiagMaxPartials * kDiagTerms) == hipSuccess;
@@ -475,8 +477,11 @@ static bh_status gravity_impl(bh_ctx *c, const float *targets, int64_t n_targets
     a.balance = balanced ? c->wbal : nullptr;
     a.balance_eval = balanced && same_hist && c->hist_new;
     a.balance_fresh = balanced && !same_runs && !a.balance_eval;
-    a.balance_runs = balanced && (same_runs || a.balance_eval) && c->bal_want &&
-                     __atomic_load_n(c->bal_want, __ATOMIC_RELAXED);
+    const int want = c->bal_want ? __atomic_load_n(c->bal_want, __ATOMIC_RELAXED) : 0;
+    a.balance_runs = balanced && (same_runs || a.balance_eval) && (want & 1);
+    // heavy groups split into waves of their own (not with uneven runs)
+    a.balance_split = balanced && !a.balance_fresh && !a.balance_runs && (want & 2) &&
+                      walk_split_max(groups) > 0;
     a.balance_record = balanced && (!same_hist || c->walk_calls < 2 ||
                                     c->walk_calls % kWalkTimedEvery == 0);
     a.balance_want = balanced ? c->bal_want_dev : nullptr;
@@ -512,6 +517,7 @@ static bh_status gravity_impl(bh_ctx *c, const float *targets, int64_t n_targets
         }
         if (a.balance_eval) c->hist_new = false;
         c->last_runs = a.balance_runs ? 1 : 0;
+        c->last_split = a.balance_split ? 1 : 0;
         if (a.balance_record) {
             c->hist_groups = groups;
             c->hist_kind = kind;
@@ -812,15 +818,19 @@ bh_status bh_set_counting(bh_ctx *c, int enable)
     return BH_OK;
 }
 
-bh_status bh_get_walk_runs(bh_ctx *c, uint32_t *starts, int32_t *uneven)
+bh_status bh_get_walk_runs(bh_ctx *c, uint32_t *starts, int32_t *uneven, int32_t *split)
 {
     if (!c || !uneven || c->last_runs < 0) return BH_ERR_INVALID;
     *uneven = c->last_runs;
-    if (!starts) return BH_OK;
-    if (hipMemcpyAsync(starts, c->wbal, 9 * sizeof(uint32_t), hipMemcpyDeviceToHost,
-                       c->last_stream) != hipSuccess ||
+    if (split) *split = 0;
+    if (!starts && !(split && c->last_split)) return BH_OK;
+    uint32_t head[kWalkSplitCount + 1];
+    if (hipMemcpyAsync(head, c->wbal, sizeof(head), hipMemcpyDeviceToHost, c->last_stream) !=
+            hipSuccess ||
         hipStreamSynchronize(c->last_stream) != hipSuccess)
         return BH_ERR_HIP;
+    if (starts) memcpy(starts, head, 9 * sizeof(uint32_t));
+    if (split && c->last_split) *split = (int32_t)head[kWalkSplitCount];
     return BH_OK;
 }
 

@@ -194,10 +194,13 @@ struct WalkArgs {
     // runs).  balance_runs: walk those runs (a grid with room for uneven
     // runs), else the equal runs of xcd_block.  balance_record: store this
     // walk's per-group times.
+    // balance_split: the launch also walks the heaviest groups (listed in the
+    // buffer) as kWalkSplitParts waves of their own, ahead of the rest.
     uint32_t *balance;
     int balance_eval;
     int balance_fresh;
     int balance_runs;
+    int balance_split;
     int balance_record;
     int *balance_want;
 };
@@ -205,10 +208,22 @@ void launch_walk(const WalkArgs &a, hipStream_t s);
 // walk groups of 64 targets, and the most groups one XCD's run may take
 __host__ __device__ inline uint32_t walk_groups(uint32_t n_targets) { return (n_targets + 63) / 64; }
 __host__ __device__ inline uint32_t walk_xcd_cap(uint32_t groups) { return (groups + 7) / 8 + (groups + 31) / 32; }
-// The walk's balance buffer: entries 0-8 the first group of each XCD's run
-// (the ninth = groups), 16-31 eight 64-bit sums of per-group times, from
-// kWalkBalanceHead on one time per group.
+// The walk's balance buffer (kWalkBalanceHead + 3 groups entries): entries
+// 0-8 the first group of each XCD's run (the ninth = groups), entry
+// kWalkSplitCount the number of split groups; from kWalkBalanceHead on one
+// time per group, then the split groups (walk_split_max(groups) entries),
+// then one split flag per group.
 constexpr uint32_t kWalkBalanceHead = 32;
+constexpr uint32_t kWalkSplitCount = 9;
+// A group whose recorded time stands far above the mean is walked as
+// kWalkSplitParts waves of 64 / kWalkSplitParts targets each (every target's
+// result is its own walk, so the same bits): its waves then end sooner, and
+// they start first.  At most one group in 32 is split (none below 512).
+constexpr uint32_t kWalkSplitParts = 4;
+__host__ __device__ inline uint32_t walk_split_max(uint32_t groups)
+{
+    return groups < 512 ? 0u : 2 * ((groups + 63) / 64);
+}
 // inv[perm[k]] = k
 void launch_invert(const uint32_t *perm, uint32_t n, uint32_t *inv, hipStream_t s);
 void launch_fill_zero(float4 *out, uint32_t n, hipStream_t s);

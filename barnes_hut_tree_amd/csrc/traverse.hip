@@ -581,7 +581,11 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
     // together share the nodes near their targets in that XCD's L2; with
     // a balance buffer the runs are the ones balanced on the previous walk's times
     uint32_t blk;
-    if (runs) {
+    uint32_t part = 0;   // 0: the whole group; p > 0: its targets' p-th share
+    // (the vote and caller-order walks keep the equal runs: mode 0)
+    if (VOTE || UNSORTED) {
+        blk = xcd_block(blockIdx.x, gridDim.x);
+    } else if (runs & 1) {
         // the grid holds 8 cap workgroups, cap per XCD; an XCD whose run is
         // shorter lets its first ones return, while every XCD still has free
         // slots (at the end of the dispatch they would hold up the others)
@@ -590,13 +594,28 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
         const uint32_t idle = (gridDim.x >> 3) - (b1 - b0);
         if (k < idle) return;
         blk = b0 + (k - idle);
+    } else if (runs & 2) {
+        // the first kWalkSplitParts * smax workgroups walk the listed heavy
+        // groups a share each; the rest the equal runs, less those groups
+        const uint32_t ng = walk_groups(n), smax = walk_split_max(ng);
+        const uint32_t extra = kWalkSplitParts * smax;
+        if (blockIdx.x < extra) {
+            const uint32_t si = blockIdx.x / kWalkSplitParts;
+            if (si >= sgpr(balance[kWalkSplitCount])) return;
+            blk = sgpr(balance[kWalkBalanceHead + ng + si]);
+            part = 1 + blockIdx.x % kWalkSplitParts;
+        } else {
+            blk = xcd_block(blockIdx.x - extra, gridDim.x - extra);
+            if (sgpr(balance[kWalkBalanceHead + ng + smax + blk])) return;
+        }
     } else {
         blk = xcd_block(blockIdx.x, gridDim.x);
     }
     const uint32_t wave_base = sgpr(blk * kWalkThreads + (threadIdx.x & ~63u));
-    const uint32_t c = wave_base + lane;
-    const bool valid = c < n;
-    if (wave_base >= n) return;
+    constexpr uint32_t kShare = 64 / kWalkSplitParts;
+    const uint32_t c = part ? wave_base + (part - 1) * kShare + lane : wave_base + lane;
+    const bool valid = c < n && (part == 0 || lane < kShare);
+    if (wave_base + (part ? (part - 1) * kShare : 0u) >= n) return;
     // the group's start time, kept in vector registers (scalar registers
     // decide how many waves stay resident)
     uint64_t t_start = record ? __builtin_amdgcn_s_memrealtime() : 0;
@@ -654,7 +673,7 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(const Node *__restrict__ 
     if (valid) out[slot] = make_float4(G * ax, G * ay, G * az, G * pot);
     // this group's time (one plain store: the per-wave device atomic this
     // replaced serialised on its few addresses)
-    if (record && lane == 0)
+    if (record && lane == 0 && part == 0)
         balance[kWalkBalanceHead + (wave_base >> 6)] =
             (uint32_t)(__builtin_amdgcn_s_memrealtime() - t_start);
     if (COUNT) {
@@ -703,15 +722,41 @@ __device__ inline uint32_t walk_chunk_start(uint32_t c, uint32_t ng)
     return (uint32_t)(((uint64_t)c * ng + 255) >> 8);
 }
 
-__device__ void walk_bounds(uint32_t ng, uint32_t cap, bool hist, bool runs,
+// Bin of a group's time on a log scale, four bins per octave: bin 4e + m
+// holds [(4 + m) 2^(e-2), (5 + m) 2^(e-2)) for e >= 2.
+__device__ inline uint32_t time_bin(uint32_t v)
+{
+    if (v < 4) return v;
+    const uint32_t e = 31u - (uint32_t)__builtin_clz(v);
+    return 4 * e + ((v >> (e - 2)) & 3u);
+}
+__device__ inline uint32_t time_bin_floor(uint32_t b)
+{
+    if (b < 8) return b;
+    return (4u + (b & 3u)) << ((b >> 2) - 2);
+}
+
+// Split groups: whether a walk's heaviest groups would end sooner as
+// kWalkSplitParts waves each (the smallest time bin of which the samples put
+// no more than walk_split_max groups at or above it must start more than
+// kWalkSplitRatio times the mean time), and the list and flags of those groups.
+constexpr double kWalkSplitRatio = 3.0;
+
+__device__ void walk_bounds(uint32_t ng, uint32_t cap, bool hist, bool runs, bool split,
                             uint32_t *__restrict__ xb, int *__restrict__ want)
 {
     const uint32_t *__restrict__ wdur = xb + kWalkBalanceHead;
+    const uint32_t smax = walk_split_max(ng);
+    uint32_t *__restrict__ slist = xb + kWalkBalanceHead + ng;
+    uint32_t *__restrict__ sflag = slist + smax;
     __shared__ unsigned long long csum[256];
+    __shared__ uint32_t tbin[128];
     __shared__ uint32_t ideal[8];
     __shared__ int balance;
+    __shared__ uint32_t split_thr, split_n;
     const uint32_t t = threadIdx.x;
     csum[t] = 0;
+    if (t < 128) tbin[t] = 0;
     if (t < 8) ideal[t] = 0;
     __syncthreads();
     if (hist) {
@@ -739,11 +784,52 @@ __device__ void walk_bounds(uint32_t ng, uint32_t cap, bool hist, bool runs,
                     next = walk_chunk_start(c + 1, ng);
                 }
                 acc += v[j];
+                atomicAdd(&tbin[time_bin(v[j])], 1u);
             }
         }
         if (acc) atomicAdd(&csum[c], acc);
     }
     __syncthreads();
+    if (t == 0) {
+        // the split threshold: the smallest bin with at most smax groups (by
+        // the samples) at or above it
+        uint32_t above = 0, b = 128;
+        while (b > 0 && (above + tbin[b - 1]) * kWalkBalanceSample <= smax) above += tbin[--b];
+        unsigned long long total = 0;
+        for (int k = 0; k < 256; ++k) total += csum[k];
+        const unsigned long long samples = (ng + kWalkBalanceSample - 1) / kWalkBalanceSample;
+        const bool heavy = hist && smax > 0 && b < 128 && above > 0 &&
+                           (double)time_bin_floor(b) * (double)samples >
+                               kWalkSplitRatio * (double)total;
+        split_thr = heavy ? time_bin_floor(b) : 0xffffffffu;
+        split_n = 0;
+    }
+    __syncthreads();
+    // the split list: clear the flags of the groups listed before (all flags
+    // for groups without a list yet), then list the groups at or above the
+    // threshold when this walk can split them
+    if (smax > 0) {
+        if (!hist) {
+            for (uint32_t g = t; g < ng; g += 256) sflag[g] = 0u;
+        } else {
+            const uint32_t old = min(xb[kWalkSplitCount], smax);
+            for (uint32_t k = t; k < old; k += 256) sflag[slist[k]] = 0u;
+        }
+        __syncthreads();
+        if (split && split_thr != 0xffffffffu) {
+            for (uint32_t g = t; g < ng; g += 256) {
+                if (wdur[g] >= split_thr) {
+                    const uint32_t k = atomicAdd(&split_n, 1u);
+                    if (k < smax) {
+                        slist[k] = g;
+                        sflag[g] = 1u;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        if (t == 0) xb[kWalkSplitCount] = min(split_n, smax);
+    }
     if (t == 0) {
         unsigned long long total = 0, most = 0;
         for (int x = 0; x < 8; ++x) {
@@ -755,7 +841,7 @@ __device__ void walk_bounds(uint32_t ng, uint32_t cap, bool hist, bool runs,
         const unsigned long long samples = (ng + kWalkBalanceSample - 1) / kWalkBalanceSample;
         const int bal = hist && (double)most * 8.0 > kWalkRebalance * (double)total &&
                         total > samples * kWalkBalanceMinTicks;
-        if (want) *want = bal;
+        if (want) *want = bal | (split_thr != 0xffffffffu ? 2 : 0);
         balance = bal && runs;
     }
     __syncthreads();
@@ -808,7 +894,7 @@ __global__ __launch_bounds__(256) void k_walk_nodes(const Node *__restrict__ nod
     // new runs from recent times, or the equal runs for groups without any;
     // otherwise the runs chosen last time stand
     if (balance && blockIdx.x == 0 && (eval || fresh))
-        walk_bounds(ng, cap, eval != 0, runs != 0, balance, want);
+        walk_bounds(ng, cap, eval != 0, (runs & 1) != 0, (runs & 2) != 0, balance, want);
     if (prm->status != 0) return;
     const uint32_t nn = prm->n_nodes;
     if (!(nn < kAsmMaxNodes && nn < wn_cap)) return;
@@ -841,11 +927,13 @@ template <bool SOFT, bool SELF, bool COUNT, bool VOTE, bool UNSORTED>
 void launch5(const WalkArgs &a, hipStream_t s)
 {
     const uint32_t groups = walk_groups(a.n_targets);
-    const uint32_t grid = a.balance_runs ? 8 * walk_xcd_cap(groups) : groups;
+    const uint32_t grid = a.balance_runs ? 8 * walk_xcd_cap(groups)
+                          : a.balance_split ? groups + kWalkSplitParts * walk_split_max(groups)
+                                            : groups;
+    const int mode = a.balance_runs ? 1 : a.balance_split ? 2 : 0;
     hipLaunchKernelGGL((k_walk<SOFT, SELF, COUNT, VOTE, UNSORTED>), dim3(grid), dim3(kWalkThreads),
                        0, s, a.nodes, a.wnodes, a.wn_cap, a.src, a.tpos, a.tmap, a.prm, a.n_targets, a.theta, a.G,
-                       a.eps * a.eps, a.out, a.count, a.balance, a.balance_runs,
-                       a.balance_record);
+                       a.eps * a.eps, a.out, a.count, a.balance, mode, a.balance_record);
 }
 
 template <bool SOFT, bool SELF, bool COUNT>
@@ -882,7 +970,8 @@ void launch_walk(const WalkArgs &args, hipStream_t s)
     WalkArgs a = args;
     if (a.vote || a.unsorted || a.wn_cap == 0 || !a.balance) {
         a.balance = nullptr;
-        a.balance_eval = a.balance_fresh = a.balance_runs = a.balance_record = 0;
+        a.balance_eval = a.balance_fresh = a.balance_runs = a.balance_split = 0;
+        a.balance_record = 0;
         a.balance_want = nullptr;
     }
     if (!a.vote && a.wn_cap > 0) {
@@ -890,7 +979,8 @@ void launch_walk(const WalkArgs &args, hipStream_t s)
         const uint32_t groups = walk_groups(a.n_targets);
         hipLaunchKernelGGL(k_walk_nodes, dim3(blocks), dim3(256), 0, s, a.nodes, a.prm, a.theta,
                            a.eps * a.eps, a.wn_cap, a.wnodes, groups, walk_xcd_cap(groups),
-                           a.balance_eval, a.balance_fresh, a.balance_runs, a.balance,
+                           a.balance_eval, a.balance_fresh,
+                           a.balance_runs ? 1 : a.balance_split ? 2 : 0, a.balance,
                            a.balance_want);
     }
     // Plummer softening with eps^2 > 0 never meets r^2 + eps^2 == 0

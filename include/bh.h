@@ -126,8 +126,10 @@ bh_status bh_build(bh_ctx *ctx, const float *src_pos_mass, int64_t n, void *stre
  * The context remembers each walk's time per group of 64 targets; when the
  * next walk has the same groups (the same target count, self-gravity or not)
  * and those times show the eight XCDs' equal runs of groups out of balance,
- * it moves the runs' ends.  That changes only where each group runs: the
- * results are the same bits either way. */
+ * it moves the runs' ends, and when a few groups take far longer than the
+ * mean, it walks each of them as four waves of 16 targets, started first.
+ * That changes only where and how each target's walk runs: the results are
+ * the same bits either way. */
 bh_status bh_gravity(bh_ctx *ctx, const float *targets, int64_t n_targets, float theta,
                      float G, float eps, float *out_acc_pot, void *stream);
 
@@ -371,10 +373,12 @@ bh_status bh_get_profile(bh_ctx *ctx, float *ms, int n);
  * groups of 64 targets among the eight XCDs (synchronous): *uneven = 1 when it
  * walked runs balanced on an earlier walk's times, and then starts[0..8] are
  * the first group of each XCD's run (starts[8] = the group count); *uneven = 0
- * when it walked the equal runs (starts then unspecified).  starts may be
- * NULL.  For measurement and tests; BH_ERR_INVALID if the context has not yet
- * walked that way. */
-bh_status bh_get_walk_runs(bh_ctx *ctx, uint32_t *starts, int32_t *uneven);
+ * when it walked the equal runs (starts then unspecified).  *split = the number
+ * of groups it walked as four waves of 16 targets each (its heaviest, by an
+ * earlier walk's times), 0 for none.  starts and split may be NULL.  For
+ * measurement and tests; BH_ERR_INVALID if the context has not yet walked that
+ * way. */
+bh_status bh_get_walk_runs(bh_ctx *ctx, uint32_t *starts, int32_t *uneven, int32_t *split);
 
 #ifdef __cplusplus
 }

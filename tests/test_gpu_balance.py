@@ -1,5 +1,6 @@
 """The per-target walk's XCD runs, balanced on an earlier walk's per-group
-times (through bh_gravity; bh_get_walk_runs reports the runs used).
+times, and its heaviest groups walked as four waves of 16 targets (through
+bh_gravity; bh_get_walk_runs reports the runs and the split groups used).
 
 Each XCD walks one contiguous run of the groups of 64 targets.  Every fourth
 walk of the same groups stores its per-group times; when those show the equal
@@ -154,4 +155,43 @@ def test_uneven_runs_walk_every_group_once():
     assert uneven_calls >= 4
     # the caller-order walk keeps equal runs: the same bits again
     assert np.array_equal(_walk(t, n, 0.02, flags=bh.WALK_UNSORTED), first)
+    t.close()
+
+
+def test_heavy_groups_split_walk_every_target_once():
+    """Separate queries around dense surfaces: a few groups of 64 queries take
+    far longer than the mean (queries on a surface open many leaves), so after
+    the first recorded walk the heaviest are walked as four waves of 16
+    queries each.  Every call gives the first call's bits (outputs filled
+    with NaN before each), and so does the caller-order walk."""
+    import barnes_hut_tree_amd as bh
+    src = torch.from_numpy(W.surface_sources(1 << 20, seed=10)).cuda()
+    q = torch.from_numpy(W.grid_queries()).cuda()
+    m = q.shape[0]
+    t = bh.BarnesHut(src.shape[0], m, 63, 16, curve="hilbert")
+    t.build(src)
+    first = _walk(t, m, 0.0, targets=q)
+    assert np.all(np.isfinite(first))
+    split = []
+    for k in range(10):
+        assert np.array_equal(_walk(t, m, 0.0, targets=q), first), "call %d" % (k + 2)
+        split.append(t.walk_split())
+    log("split groups per call", split)
+    limit = 2 * ((((m + 63) // 64) + 63) // 64)
+    assert max(split) > 0 and all(0 <= s <= limit for s in split)
+    assert np.array_equal(_walk(t, m, 0.0, targets=q, flags=bh.WALK_UNSORTED), first)
+    t.close()
+
+
+def test_plummer_groups_not_split():
+    """Plummer self-gravity: group times differ by less than the split ratio,
+    so no group is split."""
+    import barnes_hut_tree_amd as bh
+    p = W.plummer(1 << 18, seed=3)
+    n = p.shape[0]
+    t = bh.BarnesHut(n, 0, 63, 16, curve="hilbert")
+    t.build(torch.from_numpy(p).cuda())
+    for _ in range(8):
+        _walk(t, n, 0.01)
+        assert t.walk_split() == 0
     t.close()
