@@ -478,10 +478,11 @@ static bh_status gravity_impl(bh_ctx *c, const float *targets, int64_t n_targets
     a.balance_eval = balanced && same_hist && c->hist_new;
     a.balance_fresh = balanced && !same_runs && !a.balance_eval;
     const int want = c->bal_want ? __atomic_load_n(c->bal_want, __ATOMIC_RELAXED) : 0;
-    a.balance_runs = balanced && (same_runs || a.balance_eval) && (want & 1);
-    // heavy groups split into waves of their own (not with uneven runs)
-    a.balance_split = balanced && !a.balance_fresh && !a.balance_runs && (want & 2) &&
-                      walk_split_max(groups) > 0;
+    // heavy groups split into waves of their own, in front of the grid and
+    // dealt to every XCD in turn (so they also even out the XCDs' work), in
+    // preference to uneven runs
+    a.balance_split = balanced && !a.balance_fresh && (want & 2) && walk_split_max(groups) > 0;
+    a.balance_runs = balanced && (same_runs || a.balance_eval) && (want & 1) && !a.balance_split;
     a.balance_record = balanced && (!same_hist || c->walk_calls < 2 ||
                                     c->walk_calls % kWalkTimedEvery == 0);
     a.balance_want = balanced ? c->bal_want_dev : nullptr;

@@ -792,9 +792,11 @@ __device__ void walk_bounds(uint32_t ng, uint32_t cap, bool hist, bool runs, boo
     __syncthreads();
     if (t == 0) {
         // the split threshold: the smallest bin with at most smax groups (by
-        // the samples) at or above it
+        // the samples) at or above it; if the heaviest bin alone holds more,
+        // that bin (the list then takes the first smax of its groups)
         uint32_t above = 0, b = 128;
         while (b > 0 && (above + tbin[b - 1]) * kWalkBalanceSample <= smax) above += tbin[--b];
+        if (above == 0 && b > 0) above = tbin[--b];
         unsigned long long total = 0;
         for (int k = 0; k < 256; ++k) total += csum[k];
         const unsigned long long samples = (ng + kWalkBalanceSample - 1) / kWalkBalanceSample;

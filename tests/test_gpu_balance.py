@@ -195,3 +195,30 @@ def test_plummer_groups_not_split():
         _walk(t, n, 0.01)
         assert t.walk_split() == 0
     t.close()
+
+
+def test_self_gravity_split_walk_every_target_once():
+    """Self-gravity with 20000 coincident sources in a uniform background:
+    they share one leaf far over the capacity (no key bit separates them), so
+    each of their groups sums that leaf whole and takes far longer than the
+    rest; those groups are walked as four waves of 16 targets each, whose
+    leaf holds their own targets (the self pair masked per lane).  Every call
+    gives the first call's bits, and so does the caller-order walk."""
+    import barnes_hut_tree_amd as bh
+    rng = np.random.default_rng(21)
+    bg = rng.uniform(-1.0, 1.0, (200_000, 3))
+    xyz = np.concatenate([bg, np.full((20_000, 3), 0.3)])[rng.permutation(220_000)]
+    p = np.concatenate([xyz, np.full((xyz.shape[0], 1), 1.0 / xyz.shape[0])], 1).astype(np.float32)
+    n = p.shape[0]
+    t = bh.BarnesHut(n, 0, 63, 16, curve="hilbert")
+    t.build(torch.from_numpy(p).cuda())
+    first = _walk(t, n, 1e-4)
+    assert np.all(np.isfinite(first))
+    split = []
+    for k in range(10):
+        assert np.array_equal(_walk(t, n, 1e-4), first), "call %d" % (k + 2)
+        split.append(t.walk_split())
+    log("self-gravity split groups per call", split)
+    assert max(split) > 0
+    assert np.array_equal(_walk(t, n, 1e-4, flags=bh.WALK_UNSORTED), first)
+    t.close()
