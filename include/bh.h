@@ -106,7 +106,12 @@ bh_status bh_create(bh_ctx **out, int64_t max_sources, int64_t max_targets,
  * centre of mass of every node ([GASPHiA] 计算节点质心).
  *   src_pos_mass  device, n float4 rows (x, y, z, m), read only, 16-byte aligned.
  * The sources are copied in sorted order; src_pos_mass is not needed after
- * the stream passes this call.  n = 0 builds an empty tree. */
+ * the stream passes this call.  n = 0 builds an empty tree.  With 63-bit keys
+ * the sort orders the top 40 bits in passes and then each run of keys equal
+ * in those bits; once a build of the context has found many long such runs
+ * (sources clustered far below the root cube's scale), its later builds sort
+ * all bits in passes instead.  Either way the order, and every result, is the
+ * same. */
 bh_status bh_build(bh_ctx *ctx, const float *src_pos_mass, int64_t n, void *stream);
 
 /* Accelerations and potentials by the tree walk of [GASPHiA] 计算自引力 /
