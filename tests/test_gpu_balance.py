@@ -158,15 +158,17 @@ def test_uneven_runs_walk_every_group_once():
     t.close()
 
 
-def test_heavy_groups_split_walk_every_target_once():
+@pytest.mark.parametrize("m_queries", [1_000_000, 999_983])
+def test_heavy_groups_split_walk_every_target_once(m_queries):
     """Separate queries around dense surfaces: a few groups of 64 queries take
     far longer than the mean (queries on a surface open many leaves), so after
     the first recorded walk the heaviest are walked as four waves of 16
-    queries each.  Every call gives the first call's bits (outputs filled
-    with NaN before each), and so does the caller-order walk."""
+    queries each (also with a ragged last group).  Every call gives the first
+    call's bits (outputs filled with NaN before each), and so does the
+    caller-order walk."""
     import barnes_hut_tree_amd as bh
     src = torch.from_numpy(W.surface_sources(1 << 20, seed=10)).cuda()
-    q = torch.from_numpy(W.grid_queries()).cuda()
+    q = torch.from_numpy(np.ascontiguousarray(W.grid_queries()[:m_queries])).cuda()
     m = q.shape[0]
     t = bh.BarnesHut(src.shape[0], m, 63, 16, curve="hilbert")
     t.build(src)
